@@ -1,0 +1,240 @@
+/*
+ * mqconv.h -- C ABI of the MI355X (gfx950) microscaled-convolution library.
+ *
+ * The library implements the training hot path of MicroQonv ("MicroQonv:
+ * Reshaping Convolution Tensors for Efficient Microscaling in Training and
+ * Inference", Facq, Ben-Ali, Sentieys):
+ *   1. MX block quantization of each convolution tensor, performed once
+ *      (§III-A microscaling quantization; §IV-B efficient quantization
+ *      directions: square blocks spanning both GEMM directions);
+ *   2. channel-batch-first (CBF) im2col applied to the already-quantized
+ *      activation (§IV-A, Fig. 3);
+ *   3. block-scaled GEMMs for the forward output Y, the input gradient G_X
+ *      and the weight gradient G_W (§II-C3 matrix formulation, §IV-B,
+ *      Eq. 7 block dot product);
+ *   4. a naive path that expands with im2col first and quantizes each tensor
+ *      twice along 1-D lines (§III-C limitations of related work, Table I),
+ *      kept only to compare bytes moved.
+ *
+ * ---------------------------------------------------------------------------
+ * Conventions shared by every entry point
+ * ---------------------------------------------------------------------------
+ * Pointers.   Every tensor pointer is a DEVICE pointer allocated and owned by
+ *             the caller. The library never allocates, frees or retains
+ *             memory. `mq_conv` descriptors are HOST pointers, read during
+ *             the call only.
+ * Streams.    `stream` is a hipStream_t passed as void*; NULL means the
+ *             default stream. Every call only enqueues work and returns.
+ * Errors.     The return value is an mq_status. All argument validation
+ *             happens before any HIP call; an invalid call returns an error
+ *             and enqueues nothing. A failed launch returns MQ_ERR_HIP.
+ *             No C++ exception crosses this interface.
+ * Threading.  Functions keep no state between calls and may be called from
+ *             several host threads on different streams.
+ * Determinism. Equal inputs give bit-identical outputs (no float atomics).
+ *
+ * ---------------------------------------------------------------------------
+ * Number formats (MicroQonv §II-D / §III-A; OCP MX element encodings)
+ * ---------------------------------------------------------------------------
+ * Element codes are sign-magnitude floats:
+ *   MQ_E4M3  8 bit, bias 7,  max 448 (no Inf; S.1111.111 is NaN)
+ *   MQ_E5M2  8 bit, bias 15, max 57344
+ *   MQ_E2M3  6 bit, bias 1,  max 7.5
+ *   MQ_E3M2  6 bit, bias 3,  max 28
+ *   MQ_E2M1  4 bit, bias 1,  max 6
+ * Block scales are E8M0 bytes: value 2^(S-127); 0xFF means NaN.
+ *
+ * Quantization of one block (the OCP MX rule with a power-of-two scale, the
+ * original microscaling format named in §II-D):
+ *   amax = max |x| over the block's elements;
+ *   e    = floor(log2 amax) - emax_elem, clamped to [-127, 127]
+ *          (emax_elem = 8, 15, 2, 4, 2 for the formats above);
+ *          an all-zero block gets e = -127;
+ *   S    = e + 127;
+ *   code = round-to-nearest-even of x * 2^-e on the element grid
+ *          (subnormals included), saturated to +-max; the sign of zero is
+ *          kept; a block holding a NaN or Inf gets S = 0xFF and all codes 0.
+ *
+ * ---------------------------------------------------------------------------
+ * Block geometry (§IV-B: square blocks, one side along the channel, the
+ * other along the partner dimension of the second GEMM)
+ * ---------------------------------------------------------------------------
+ * A block is 32 consecutive channels x `block_partner` (bp) consecutive
+ * partner indices, inside one pixel (activations, gradients) or one kernel
+ * tap (weights). Channel blocks start at channel 0 and the last one is
+ * truncated at C; partner blocks are truncated at the partner extent.
+ * Partner dimension: N (batch) for ACT and GRAD, Cout for WEIGHT.
+ * bp is 1 (a line along the channel) or 32 (a 32x32 square).
+ *
+ * ---------------------------------------------------------------------------
+ * Packed layouts (channel-batch-first, §IV-A "each spatial location holds a
+ * contiguous block of all channels across all batch elements")
+ * ---------------------------------------------------------------------------
+ * Cpad      = C rounded up to a multiple of 32; ncb = Cpad / 32.
+ * run_bytes = bytes of 32 packed codes: 32 (8-bit), 24 (6-bit), 16 (4-bit).
+ * row_bytes = ncb * run_bytes.
+ * Inside a run, code j (channel 32*cb + j) sits at
+ *   8-bit: byte j;
+ *   6-bit: bits [6j, 6j+6) of the run read as a little-endian 192-bit word;
+ *   4-bit: bits [4j, 4j+4) of the run read as a little-endian 128-bit word
+ *          (code 2i in the low nibble of byte i).
+ * Codes of padding channels (C <= c < Cpad) are 0.
+ *
+ *   role ACT / GRAD, dims (d0,d1,d2,d3) = (H, W, N, C):
+ *     codes  [H][W][N][row_bytes]
+ *     scales [H][W][ceil(N/bp)][ncb]
+ *   role WEIGHT, dims (d0,d1,d2,d3) = (Cout, Kh, Kw, Cin):
+ *     codes  [Cout][Kh][Kw][row_bytes]
+ *     scales [Kh][Kw][ceil(Cout/bp)][ncb]
+ *   CBF im2col output X' of an ACT tensor (mqconv_cbf_im2col):
+ *     codes  [Ho][Wo][N][Kh][Kw][row_bytes]
+ *     scales [Ho][Wo][Kh][Kw][ceil(N/bp)][ncb]
+ *
+ * fp32 tensors use the same orders: activations and gradients [H][W][N][C]
+ * (C fastest), weights [Cout][Kh][Kw][Cin].
+ *
+ * Convolution (§II-A, Eqs. 1-3, with stride s and zero padding p; the kernel
+ * is not flipped, as in the im2col patch definition of §II-C1):
+ *   Ho = floor((H + 2p - Kh) / s) + 1  (same for Wo)
+ *   Y[ho,wo,n,co]    = sum_{kh,kw,ci} W[co,kh,kw,ci] * X[ho*s+kh-p, wo*s+kw-p, n, ci]
+ *   G_X[h,w,n,ci]    = sum over (co,kh,kw,ho,wo) with ho*s+kh-p = h, wo*s+kw-p = w
+ *                      of W[co,kh,kw,ci] * G_Y[ho,wo,n,co]
+ *   G_W[co,kh,kw,ci] = sum_{ho,wo,n} G_Y[ho,wo,n,co] * X[ho*s+kh-p, wo*s+kw-p, n, ci]
+ * with out-of-image X taken as 0. The GEMMs use the dequantized operands
+ * (code value * block scale, the fake-quantization view of §III-A) and
+ * accumulate in fp32.
+ */
+#ifndef MQCONV_H
+#define MQCONV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MQCONV_ABI_VERSION 1
+
+typedef enum {
+  MQ_OK = 0,
+  MQ_ERR_NULL = -1,        /* a required pointer is NULL */
+  MQ_ERR_SHAPE = -2,       /* a dimension is < 1, inconsistent, or too large */
+  MQ_ERR_FORMAT = -3,      /* unknown element format or role mismatch */
+  MQ_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned */
+  MQ_ERR_WORKSPACE = -5,   /* workspace smaller than the *_workspace_bytes query */
+  MQ_ERR_UNSUPPORTED = -6, /* valid but unsupported combination (see each call) */
+  MQ_ERR_HIP = -7          /* a HIP launch or runtime call failed */
+} mq_status;
+
+typedef enum { MQ_E4M3 = 0, MQ_E5M2 = 1, MQ_E2M3 = 2, MQ_E3M2 = 3, MQ_E2M1 = 4 } mq_elem;
+
+typedef enum { MQ_ROLE_ACT = 0, MQ_ROLE_WEIGHT = 1, MQ_ROLE_GRAD = 2 } mq_role;
+
+/* Convolution geometry (host struct). All fields >= 1 except pads (>= 0).
+ * Supported: kh, kw <= 7; pad < kernel size; Ho, Wo >= 1. */
+typedef struct {
+  int32_t n, cin, h, w, cout, kh, kw, stride_h, stride_w, pad_h, pad_w;
+} mq_conv;
+
+/* Packed MX tensor view (layouts above). Caller owns both buffers. */
+typedef struct {
+  void* codes;           /* device, 16-byte aligned */
+  uint8_t* scales;       /* device, 16-byte aligned, one E8M0 byte per block */
+  mq_elem fmt;
+  int32_t block_partner; /* bp: 1 or 32 */
+  mq_role role;
+  int32_t d0, d1, d2, d3; /* ACT/GRAD: (H, W, N, C); WEIGHT: (Cout, Kh, Kw, Cin) */
+} mq_mx;
+
+/* Returns MQCONV_ABI_VERSION. */
+int mqconv_abi_version(void);
+
+/* Static English text for a status code; never NULL. */
+const char* mqconv_status_string(int status);
+
+/* Bytes of the packed code / scale buffers of a tensor with the given role
+ * and dims (layouts above). 0 for invalid arguments. Host-only, no HIP call. */
+size_t mqconv_codes_bytes(mq_role role, mq_elem fmt, int32_t d0, int32_t d1, int32_t d2,
+                          int32_t d3);
+size_t mqconv_scales_bytes(mq_role role, int32_t bp, int32_t d0, int32_t d1, int32_t d2,
+                           int32_t d3);
+/* Bytes of the CBF im2col output of an ACT tensor for conv `cv`. */
+size_t mqconv_im2col_codes_bytes(const mq_conv* cv, mq_elem fmt);
+size_t mqconv_im2col_scales_bytes(const mq_conv* cv, int32_t bp);
+
+/* MX-quantize an fp32 tensor once (§III-A, §IV-B).
+ * src: fp32 in the role's order ([H][W][N][C] or [Cout][Kh][Kw][Cin]).
+ * dst: role, fmt, bp and dims select the block geometry; its code and scale
+ *      buffers must hold mqconv_codes_bytes / mqconv_scales_bytes bytes and
+ *      are fully overwritten (padding codes included). */
+int mqconv_quantize(const float* src, mq_mx dst, void* stream);
+
+/* Channel-batch-first im2col of an already-quantized activation (§IV-A):
+ *   X'[ho,wo,n,kh,kw,c] = X[ho*s+kh-p, wo*s+kw-p, n, c]
+ * Codes and scales are moved unchanged (no requantization): every
+ * (ho,wo,kh,kw, n-block, c-block) block of X' takes the scale of its source
+ * block; positions outside the image get code 0 and scale byte 0.
+ * xq must be an ACT tensor of dims (H, W, N, Cin) matching cv. */
+int mqconv_cbf_im2col(const mq_conv* cv, mq_mx xq, void* col_codes, uint8_t* col_scales,
+                      void* stream);
+
+/* Workspace (device bytes) needed by the GEMM entry points.
+ * op: 0 forward, 1 backward-data, 2 backward-weight. fa/fb: the formats of
+ * the two operands in the order of the call's arguments. */
+size_t mqconv_workspace_bytes(const mq_conv* cv, int op, mq_elem fa, mq_elem fb);
+
+/* Forward GEMM Y_f = W_f . X'  (§IV-B), with X' generated on the fly from
+ * the packed CBF activation (implicit CBF im2col).
+ *   xq: ACT (H, W, N, Cin), bp 1 or 32;  wq: WEIGHT (Cout, Kh, Kw, Cin), bp 1 or 32.
+ *   y:  fp32 [Ho][Wo][N][Cout], fully overwritten. */
+int mqconv_forward(const mq_conv* cv, mq_mx xq, mq_mx wq, float* y, void* ws, size_t ws_bytes,
+                   void* stream);
+
+/* Input-gradient GEMM G_X' = W_f^T . G_Yf (§IV-B) folded back to G_X
+ * (Eq. 2: convolution of G_Y with the channel-transposed kernel).
+ *   dyq: GRAD (Ho, Wo, N, Cout), any bp;  wq: WEIGHT, bp must be 32
+ *        (the contraction runs along Cout, the weight's partner dimension;
+ *        bp 1 returns MQ_ERR_UNSUPPORTED).
+ *   dx: fp32 [H][W][N][Cin], fully overwritten. */
+int mqconv_backward_data(const mq_conv* cv, mq_mx dyq, mq_mx wq, float* dx, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/* Weight-gradient GEMM G_Wf = G_Yf . X'^T (§IV-B; Eq. 3).
+ *   dyq: GRAD (Ho, Wo, N, Cout) and xq: ACT (H, W, N, Cin), both bp 32
+ *        (the contraction runs along N, the partner dimension; bp 1 returns
+ *        MQ_ERR_UNSUPPORTED).
+ *   dw: fp32 [Cout][Kh][Kw][Cin], fully overwritten. */
+int mqconv_backward_weight(const mq_conv* cv, mq_mx dyq, mq_mx xq, float* dw, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Naive comparison path (kept only to measure bytes moved; §III-C, Table I
+ * "Dacapo" column). Every tensor stays fp32 in memory; im2col is explicit
+ * and runs before quantization; 1-D blocks of 32 follow the GEMM direction,
+ * so X' and W and G_Y are each quantized twice:
+ *   X'  = classic im2col of X: rows m = (ho, wo, n), columns k = (ci, kh, kw)
+ *         (channel-major patch flattening, §II-C1/§II-C2), zero outside.
+ *   W_f = W flattened to [Cout][k] with the same k order.
+ *   forward:  X' and W_f quantized along k;          Y  = X'q . W_fq^T
+ *   backward-data: G_Y [m][Cout] and W_f quantized along Cout;
+ *             G_X' = G_Yq . W_fq (fp32 [m][k]), then col2im into G_X
+ *   backward-weight: G_Y and X' quantized along m;   G_W = G_Yq^T . X'q
+ * Inputs and outputs are fp32 in the layouts above (x, dy, dx CBF; w, dw
+ * [Cout][Kh][Kw][Cin]). The workspace holds the expanded and quantized
+ * intermediates.
+ * --------------------------------------------------------------------------- */
+size_t mqconv_naive_workspace_bytes(const mq_conv* cv, int op, mq_elem fa, mq_elem fb);
+int mqconv_naive_forward(const mq_conv* cv, const float* x, const float* w, mq_elem fx,
+                         mq_elem fw, float* y, void* ws, size_t ws_bytes, void* stream);
+int mqconv_naive_backward_data(const mq_conv* cv, const float* dy, const float* w, mq_elem fdy,
+                               mq_elem fw, float* dx, void* ws, size_t ws_bytes, void* stream);
+int mqconv_naive_backward_weight(const mq_conv* cv, const float* dy, const float* x,
+                                 mq_elem fdy, mq_elem fx, float* dw, void* ws, size_t ws_bytes,
+                                 void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MQCONV_H */

@@ -1,0 +1,192 @@
+"""Pins of the oracle's im2col, convolution and naive-path composition against
+torch (float64, CPU), closed identities and the paper's invariants."""
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from microscaling_quantized_convolution_mxq_amd.workloads import ConvShape
+
+SMALL = [
+    ConvShape(2, 3, 6, 5, 4, 3, 3, 1, 1),
+    ConvShape(2, 4, 6, 6, 3, 3, 3, 2, 1),
+    ConvShape(1, 2, 5, 6, 2, 3, 3, 1, 0),
+    ConvShape(2, 3, 5, 5, 2, 1, 1, 1, 0),
+    ConvShape(2, 2, 6, 6, 3, 3, 3, 2, 0),
+    ConvShape(1, 4, 4, 4, 2, 1, 1, 2, 0),
+]
+
+
+def _nchw(t):
+    return torch.from_numpy(np.ascontiguousarray(np.transpose(t, (2, 3, 0, 1)))).double()
+
+
+def _oihw(w):
+    return torch.from_numpy(np.ascontiguousarray(np.transpose(w, (0, 3, 1, 2)))).double()
+
+
+def _rand(shape, seed):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((shape.h, shape.w, shape.n, shape.cin))
+    w = rng.standard_normal((shape.cout, shape.kh, shape.kw, shape.cin))
+    dy = rng.standard_normal((shape.ho, shape.wo, shape.n, shape.cout))
+    return x, w, dy
+
+
+@pytest.mark.parametrize("shape", SMALL)
+def test_conv_matches_torch_conv2d_and_autograd(shape):
+    x, w, dy = _rand(shape, 1)
+    xt = _nchw(x).requires_grad_(True)
+    wt = _oihw(w).requires_grad_(True)
+    yt = F.conv2d(xt, wt, stride=shape.stride, padding=shape.pad)
+    gx, gw = torch.autograd.grad(yt, (xt, wt), _nchw(dy))
+    y = oracle.conv_fwd(shape, x, w)
+    np.testing.assert_allclose(y, yt.detach().numpy().transpose(2, 3, 0, 1), rtol=1e-12, atol=1e-12)
+    dx = oracle.conv_dgrad(shape, dy, w)
+    np.testing.assert_allclose(dx, gx.numpy().transpose(2, 3, 0, 1), rtol=1e-12, atol=1e-12)
+    dw = oracle.conv_wgrad(shape, dy, x)
+    np.testing.assert_allclose(dw, gw.numpy().transpose(0, 2, 3, 1), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("shape", SMALL)
+def test_adjoint_identity(shape):
+    """<conv(X, W), G> = <X, dgrad(G, W)> = <W, wgrad(G, X)>."""
+    x, w, g = _rand(shape, 2)
+    a = np.sum(oracle.conv_fwd(shape, x, w) * g)
+    b = np.sum(x * oracle.conv_dgrad(shape, g, w))
+    c = np.sum(w * oracle.conv_wgrad(shape, g, x))
+    assert b == pytest.approx(a, rel=1e-12)
+    assert c == pytest.approx(a, rel=1e-12)
+
+
+@pytest.mark.parametrize("shape", SMALL)
+def test_classic_im2col_gemm_equals_direct_conv(shape):
+    """§II-C3: Y_f = W_f . X' (explicit im2col GEMM) equals the direct loops;
+    classic im2col equals torch's unfold and col2im equals torch's fold."""
+    x, w, dy = _rand(shape, 3)
+    xc = oracle.classic_im2col(shape, x.astype(np.float32))
+    u = F.unfold(_nchw(x.astype(np.float32)), (shape.kh, shape.kw), padding=shape.pad,
+                 stride=shape.stride).numpy()  # [N][K][L]
+    np.testing.assert_array_equal(xc, np.transpose(u, (2, 0, 1)).reshape(-1, u.shape[1]))
+    y = (xc.astype(np.float64) @ oracle.flatten_kernel(w).T).reshape(shape.ho, shape.wo, shape.n, shape.cout)
+    np.testing.assert_allclose(y, oracle.conv_fwd(shape, x.astype(np.float32).astype(np.float64), w),
+                               rtol=1e-10, atol=1e-10)
+    gcol = np.random.default_rng(4).standard_normal(xc.shape)
+    gx = oracle.col2im(shape, gcol)
+    folded = F.fold(torch.from_numpy(np.transpose(gcol.reshape(shape.ho * shape.wo, shape.n, -1), (1, 2, 0)).copy()),
+                    (shape.h, shape.w), (shape.kh, shape.kw), padding=shape.pad, stride=shape.stride)
+    np.testing.assert_allclose(gx, folded.numpy().transpose(2, 3, 0, 1), rtol=1e-12, atol=1e-12)
+
+
+def test_points_match_full():
+    shape = ConvShape(3, 5, 7, 6, 4, 3, 3, 2, 1)
+    x, w, dy = _rand(shape, 5)
+    ev = oracle.PointEvaluator(shape, x, w, dy)
+    y, dx, dw = oracle.conv_fwd(shape, x, w), oracle.conv_dgrad(shape, dy, w), oracle.conv_wgrad(shape, dy, x)
+    pts = np.array(np.unravel_index(np.arange(y.size), y.shape)).T
+    np.testing.assert_allclose(ev.fwd(pts), y.reshape(-1), rtol=1e-13, atol=1e-13)
+    pts = np.array(np.unravel_index(np.arange(dx.size), dx.shape)).T
+    np.testing.assert_allclose(ev.dgrad(pts), dx.reshape(-1), rtol=1e-13, atol=1e-13)
+    pts = np.array(np.unravel_index(np.arange(dw.size), dw.shape)).T
+    np.testing.assert_allclose(ev.wgrad(pts), dw.reshape(-1), rtol=1e-13, atol=1e-13)
+
+
+I1_CASES = [
+    (ConvShape(16, 64, 9, 9, 8, 3, 3, 1, 1), 0, 32),
+    (ConvShape(16, 64, 9, 9, 8, 3, 3, 1, 1), 1, 1),
+    (ConvShape(40, 45, 7, 6, 8, 3, 3, 2, 1), 3, 32),
+    (ConvShape(33, 3, 8, 8, 8, 3, 3, 2, 0), 4, 32),
+    (ConvShape(5, 70, 6, 7, 8, 1, 1, 1, 0), 2, 32),
+    (ConvShape(2, 32, 16, 16, 32, 3, 3, 1, 1), 0, 1),
+]
+
+
+@pytest.mark.parametrize("shape,fmt,bp", I1_CASES)
+def test_invariant_quantize_then_cbf_im2col(shape, fmt, bp):
+    """§IV-A/§IV-B: with blocks inside one pixel, quantizing the CBF tensor and
+    then applying CBF im2col gives exactly the codes and scales of quantizing
+    the expanded tensor (zero blocks at padding included)."""
+    rng = np.random.default_rng(6)
+    x = (rng.standard_normal((shape.h, shape.w, shape.n, shape.cin)) * np.exp(rng.uniform(-3, 3, (shape.h, shape.w, 1, 1)))).astype(np.float32)
+    xc, xs, _ = oracle.quantize(oracle.ROLE_ACT, fmt, bp, x)
+    c1, s1 = oracle.cbf_im2col_codes(shape, bp, xc, xs)
+    c2, s2, n = oracle.quantize_im2col_expanded(shape, fmt, bp, oracle.cbf_im2col_f32(shape, x))
+    np.testing.assert_array_equal(c1, c2)
+    np.testing.assert_array_equal(s1, s2)
+    assert n == shape.ho * shape.wo * shape.n * shape.kh * shape.kw * shape.cin
+
+
+@pytest.mark.parametrize("fmt,min_fraction", [(0, 0.0), (4, 0.15)])
+def test_counter_witness_classic_im2col_requantizes(fmt, min_fraction):
+    """§I and §II-C4: after classic im2col, line blocks along k mix different
+    pixels, so one input element gets several quantized values (always at
+    least one element; with 4-bit elements a large share of them)."""
+    shape = ConvShape(16, 64, 10, 10, 8, 3, 3, 1, 1)
+    rng = np.random.default_rng(8)
+    z = rng.standard_normal((shape.h, shape.w, shape.n, shape.cin))
+    x = (z / (1 + np.exp(-z))).astype(np.float32)
+    deq, _ = oracle.quantize_lines(fmt, oracle.classic_im2col(shape, x))
+    # source element of every X' entry, found by expanding an index tensor
+    ids = np.arange(x.size, dtype=np.float32).reshape(x.shape) + 1
+    src = oracle.classic_im2col(shape, ids).astype(np.int64) - 1
+    inside = src >= 0
+    order = np.argsort(src[inside], kind="stable")
+    s_sorted = src[inside][order]
+    v_sorted = deq[inside][order]
+    starts = np.flatnonzero(np.r_[True, s_sorted[1:] != s_sorted[:-1]])
+    vmin = np.minimum.reduceat(v_sorted, starts)
+    vmax = np.maximum.reduceat(v_sorted, starts)
+    multi = np.count_nonzero(vmin != vmax)
+    assert multi >= 1
+    assert multi >= min_fraction * x.size
+
+
+def _lossless(shape, seed):
+    """Inputs whose E4M3 / E5M2 quantization is exact: powers of two within
+    a factor 2^6 of each block's maximum, and zeros."""
+    rng = np.random.default_rng(seed)
+
+    def draw(sh):
+        v = 2.0 ** rng.integers(-6, 1, size=sh) * rng.choice([-1.0, 1.0], size=sh)
+        v[rng.random(sh) < 0.2] = 0.0
+        return v.astype(np.float32)
+    return (draw((shape.h, shape.w, shape.n, shape.cin)), draw((shape.cout, shape.kh, shape.kw, shape.cin)),
+            draw((shape.ho, shape.wo, shape.n, shape.cout)))
+
+
+@pytest.mark.parametrize("shape", SMALL)
+def test_paths_on_lossless_inputs_equal_exact_conv(shape):
+    """When quantization is exact, the MicroQonv composition and the naive
+    quantize-twice composition both reduce to the plain convolution."""
+    x, w, dy = _lossless(shape, 9)
+    ref_y = oracle.conv_fwd(shape, x.astype(np.float64), w.astype(np.float64))
+    ref_dx = oracle.conv_dgrad(shape, dy.astype(np.float64), w.astype(np.float64))
+    ref_dw = oracle.conv_wgrad(shape, dy.astype(np.float64), x.astype(np.float64))
+    for bp in (1, 32):
+        out = oracle.microqonv_step(shape, x, w, dy, 0, 0, 1, bp)
+        np.testing.assert_allclose(out["y"], ref_y, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(out["dx"], ref_dx, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(out["dw"], ref_dw, rtol=1e-12, atol=1e-12)
+    y, _ = oracle.naive_fwd(shape, x, w, 0, 0)
+    np.testing.assert_allclose(y, ref_y, rtol=1e-12, atol=1e-12)
+    dx, _ = oracle.naive_dgrad(shape, dy, w, 1, 0)
+    np.testing.assert_allclose(dx, ref_dx, rtol=1e-12, atol=1e-12)
+    dw, _ = oracle.naive_wgrad(shape, dy, x, 1, 0)
+    np.testing.assert_allclose(dw, ref_dw, rtol=1e-12, atol=1e-12)
+
+
+def test_paths_on_random_inputs_are_close_to_exact_conv():
+    """On random data both compositions stay within the FP8 quantization
+    error of the exact convolution (relative to the output's scale)."""
+    shape = ConvShape(4, 40, 6, 6, 36, 3, 3, 1, 1)
+    rng = np.random.default_rng(10)
+    x = rng.standard_normal((shape.h, shape.w, shape.n, shape.cin)).astype(np.float32)
+    w = rng.standard_normal((shape.cout, shape.kh, shape.kw, shape.cin)).astype(np.float32)
+    dy = rng.standard_normal((shape.ho, shape.wo, shape.n, shape.cout)).astype(np.float32)
+    exact = oracle.conv_fwd(shape, x.astype(np.float64), w.astype(np.float64))
+    out = oracle.microqonv_step(shape, x, w, dy, 0, 0, 1, 32)
+    naive, _ = oracle.naive_fwd(shape, x, w, 0, 0)
+    for got in (out["y"], naive):
+        err = np.abs(got - exact).max() / np.abs(exact).max()
+        assert 1e-4 < err < 0.05
