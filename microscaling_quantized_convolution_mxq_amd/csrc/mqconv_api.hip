@@ -1,0 +1,242 @@
+// mqconv_api.hip -- the C ABI declared in include/mqconv.h.
+// Validates every argument on the host before any HIP call (an invalid call
+// enqueues nothing), converts descriptors and hands off to the launchers.
+#include "mqconv.h"
+#include "mqconv_internal.h"
+
+#include <limits.h>
+
+using namespace mq;
+
+namespace {
+
+const long long kMaxElems = (1LL << 31) - 1;  // index arithmetic inside kernels is 32-bit per dimension
+
+bool fmt_ok(int f) { return f >= MQ_E4M3 && f <= MQ_E2M1; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool dims_ok(int32_t d0, int32_t d1, int32_t d2, int32_t d3) {
+  if (d0 < 1 || d1 < 1 || d2 < 1 || d3 < 1) return false;
+  long long n = (long long)d0 * d1 * d2;
+  if (n > kMaxElems) return false;
+  long long cpad = ((long long)d3 + 31) / 32 * 32;
+  return n * cpad <= kMaxElems;
+}
+
+// Element counts of the conv's tensors (0 if the geometry is invalid).
+bool conv_ok(const mq_conv* c) {
+  if (!c) return false;
+  if (c->n < 1 || c->cin < 1 || c->h < 1 || c->w < 1 || c->cout < 1) return false;
+  if (c->kh < 1 || c->kw < 1 || c->kh > 15 || c->kw > 15) return false;
+  if (c->stride_h < 1 || c->stride_w < 1 || c->stride_h > 8 || c->stride_w > 8) return false;
+  if (c->pad_h < 0 || c->pad_w < 0 || c->pad_h >= c->kh || c->pad_w >= c->kw) return false;
+  long long ho = ((long long)c->h + 2LL * c->pad_h - c->kh) / c->stride_h + 1;
+  long long wo = ((long long)c->w + 2LL * c->pad_w - c->kw) / c->stride_w + 1;
+  if (c->h + 2LL * c->pad_h < c->kh || c->w + 2LL * c->pad_w < c->kw) return false;
+  if (ho < 1 || wo < 1) return false;
+  long long cpi = ((long long)c->cin + 31) / 32 * 32, cpo = ((long long)c->cout + 31) / 32 * 32;
+  long long npad = ((long long)c->n + 31) / 32 * 32;
+  if ((long long)c->h * c->w * npad * cpi > kMaxElems) return false;
+  if (ho * wo * npad * cpo > kMaxElems) return false;
+  if (ho * wo * c->n * (long long)c->kh * c->kw * cpi > kMaxElems * 4) return false;
+  if ((long long)c->cout * c->kh * c->kw * cpi > kMaxElems) return false;
+  return true;
+}
+
+Conv to_conv(const mq_conv* c) {
+  Conv v;
+  v.n = c->n; v.cin = c->cin; v.h = c->h; v.w = c->w; v.cout = c->cout; v.kh = c->kh; v.kw = c->kw;
+  v.sh = c->stride_h; v.sw = c->stride_w; v.ph = c->pad_h; v.pw = c->pad_w;
+  return v;
+}
+
+// Checks a packed tensor view against a role and expected dims.
+int check_mx(const mq_mx& t, mq_role role, int32_t d0, int32_t d1, int32_t d2, int32_t d3) {
+  if (!t.codes || !t.scales) return MQ_ERR_NULL;
+  if (!fmt_ok(t.fmt)) return MQ_ERR_FORMAT;
+  if (t.role != role) return MQ_ERR_FORMAT;
+  if (t.block_partner != 1 && t.block_partner != 32) return MQ_ERR_UNSUPPORTED;
+  if (t.d0 != d0 || t.d1 != d1 || t.d2 != d2 || t.d3 != d3) return MQ_ERR_SHAPE;
+  if (!aligned16(t.codes) || !aligned16(t.scales)) return MQ_ERR_ALIGN;
+  return MQ_OK;
+}
+
+MxView view(const mq_mx& t) {
+  MxView v;
+  v.codes = static_cast<const uint8_t*>(t.codes);
+  v.scales = t.scales;
+  v.fmt = t.fmt;
+  v.bp = t.block_partner;
+  return v;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MQ_OK : MQ_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int mqconv_abi_version(void) { return MQCONV_ABI_VERSION; }
+
+const char* mqconv_status_string(int status) {
+  switch (status) {
+    case MQ_OK: return "ok";
+    case MQ_ERR_NULL: return "a required pointer is NULL";
+    case MQ_ERR_SHAPE: return "invalid or inconsistent shape";
+    case MQ_ERR_FORMAT: return "unknown element format or role mismatch";
+    case MQ_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case MQ_ERR_WORKSPACE: return "workspace too small";
+    case MQ_ERR_UNSUPPORTED: return "unsupported combination";
+    case MQ_ERR_HIP: return "HIP runtime or launch failure";
+    default: return "unknown status";
+  }
+}
+
+size_t mqconv_codes_bytes(mq_role role, mq_elem fmt, int32_t d0, int32_t d1, int32_t d2, int32_t d3) {
+  if (!fmt_ok(fmt) || !dims_ok(d0, d1, d2, d3)) return 0;
+  if (role != MQ_ROLE_ACT && role != MQ_ROLE_GRAD && role != MQ_ROLE_WEIGHT) return 0;
+  return (size_t)((long long)d0 * d1 * d2 * row_bytes(fmt, d3));
+}
+
+size_t mqconv_scales_bytes(mq_role role, int32_t bp, int32_t d0, int32_t d1, int32_t d2, int32_t d3) {
+  if ((bp != 1 && bp != 32) || !dims_ok(d0, d1, d2, d3)) return 0;
+  const long long ncb = (d3 + 31) / 32;
+  if (role == MQ_ROLE_ACT || role == MQ_ROLE_GRAD)
+    return (size_t)((long long)d0 * d1 * ceil_div(d2, bp) * ncb);
+  if (role == MQ_ROLE_WEIGHT) return (size_t)((long long)d1 * d2 * ceil_div(d0, bp) * ncb);
+  return 0;
+}
+
+size_t mqconv_im2col_codes_bytes(const mq_conv* cv, mq_elem fmt) {
+  if (!conv_ok(cv) || !fmt_ok(fmt)) return 0;
+  Conv c = to_conv(cv);
+  return (size_t)((long long)c.ho() * c.wo() * c.n * c.kh * c.kw * row_bytes(fmt, c.cin));
+}
+
+size_t mqconv_im2col_scales_bytes(const mq_conv* cv, int32_t bp) {
+  if (!conv_ok(cv) || (bp != 1 && bp != 32)) return 0;
+  Conv c = to_conv(cv);
+  return (size_t)((long long)c.ho() * c.wo() * c.kh * c.kw * ceil_div(c.n, bp) * ceil_div(c.cin, 32));
+}
+
+int mqconv_quantize(const float* src, mq_mx dst, void* stream) {
+  if (!src || !dst.codes || !dst.scales) return MQ_ERR_NULL;
+  if (!fmt_ok(dst.fmt)) return MQ_ERR_FORMAT;
+  if (dst.role != MQ_ROLE_ACT && dst.role != MQ_ROLE_GRAD && dst.role != MQ_ROLE_WEIGHT) return MQ_ERR_FORMAT;
+  if (dst.block_partner != 1 && dst.block_partner != 32) return MQ_ERR_UNSUPPORTED;
+  if (!dims_ok(dst.d0, dst.d1, dst.d2, dst.d3)) return MQ_ERR_SHAPE;
+  if (!aligned16(dst.codes) || !aligned16(dst.scales) || ((uintptr_t)src & 3u)) return MQ_ERR_ALIGN;
+  int A, P, B;
+  if (dst.role == MQ_ROLE_WEIGHT) { A = 1; P = dst.d0; B = dst.d1 * dst.d2; }
+  else if (dst.block_partner == 1) { A = 1; P = dst.d0 * dst.d1 * dst.d2; B = 1; }  // rows independent
+  else { A = dst.d0 * dst.d1; P = dst.d2; B = 1; }
+  return hip_status(launch_quantize(src, static_cast<uint8_t*>(dst.codes), dst.scales, dst.fmt,
+                                    dst.block_partner, A, P, B, dst.d3, (hipStream_t)stream));
+}
+
+int mqconv_cbf_im2col(const mq_conv* cv, mq_mx xq, void* col_codes, uint8_t* col_scales, void* stream) {
+  if (!cv) return MQ_ERR_NULL;
+  if (!conv_ok(cv)) return MQ_ERR_SHAPE;
+  int s = check_mx(xq, MQ_ROLE_ACT, cv->h, cv->w, cv->n, cv->cin);
+  if (s != MQ_OK) return s;
+  if (!col_codes || !col_scales) return MQ_ERR_NULL;
+  if (!aligned16(col_codes) || !aligned16(col_scales)) return MQ_ERR_ALIGN;
+  return hip_status(launch_cbf_im2col(to_conv(cv), view(xq), static_cast<uint8_t*>(col_codes),
+                                      col_scales, (hipStream_t)stream));
+}
+
+size_t mqconv_workspace_bytes(const mq_conv* cv, int op, mq_elem fa, mq_elem fb) {
+  if (!conv_ok(cv) || !fmt_ok(fa) || !fmt_ok(fb) || op < 0 || op > 2) return 0;
+  return gemm_workspace_bytes(to_conv(cv), op, fa, fb);
+}
+
+int mqconv_forward(const mq_conv* cv, mq_mx xq, mq_mx wq, float* y, void* ws, size_t ws_bytes, void* stream) {
+  if (!cv) return MQ_ERR_NULL;
+  if (!conv_ok(cv)) return MQ_ERR_SHAPE;
+  int s = check_mx(xq, MQ_ROLE_ACT, cv->h, cv->w, cv->n, cv->cin);
+  if (s != MQ_OK) return s;
+  s = check_mx(wq, MQ_ROLE_WEIGHT, cv->cout, cv->kh, cv->kw, cv->cin);
+  if (s != MQ_OK) return s;
+  if (!y) return MQ_ERR_NULL;
+  if ((uintptr_t)y & 3u) return MQ_ERR_ALIGN;
+  const size_t need = gemm_workspace_bytes(to_conv(cv), 0, xq.fmt, wq.fmt);
+  if (need > 0 && (!ws || ws_bytes < need)) return MQ_ERR_WORKSPACE;
+  return hip_status(launch_forward(to_conv(cv), view(xq), view(wq), y, ws, ws_bytes, (hipStream_t)stream));
+}
+
+int mqconv_backward_data(const mq_conv* cv, mq_mx dyq, mq_mx wq, float* dx, void* ws, size_t ws_bytes,
+                         void* stream) {
+  if (!cv) return MQ_ERR_NULL;
+  if (!conv_ok(cv)) return MQ_ERR_SHAPE;
+  Conv c = to_conv(cv);
+  int s = check_mx(dyq, MQ_ROLE_GRAD, c.ho(), c.wo(), cv->n, cv->cout);
+  if (s != MQ_OK) return s;
+  s = check_mx(wq, MQ_ROLE_WEIGHT, cv->cout, cv->kh, cv->kw, cv->cin);
+  if (s != MQ_OK) return s;
+  if (wq.block_partner != 32) return MQ_ERR_UNSUPPORTED;
+  if (!dx) return MQ_ERR_NULL;
+  if ((uintptr_t)dx & 3u) return MQ_ERR_ALIGN;
+  const size_t need = gemm_workspace_bytes(c, 1, dyq.fmt, wq.fmt);
+  if (need > 0 && (!ws || ws_bytes < need)) return MQ_ERR_WORKSPACE;
+  if (ws && !aligned16(ws)) return MQ_ERR_ALIGN;
+  return hip_status(launch_backward_data(c, view(dyq), view(wq), dx, ws, ws_bytes, (hipStream_t)stream));
+}
+
+int mqconv_backward_weight(const mq_conv* cv, mq_mx dyq, mq_mx xq, float* dw, void* ws, size_t ws_bytes,
+                           void* stream) {
+  if (!cv) return MQ_ERR_NULL;
+  if (!conv_ok(cv)) return MQ_ERR_SHAPE;
+  Conv c = to_conv(cv);
+  int s = check_mx(dyq, MQ_ROLE_GRAD, c.ho(), c.wo(), cv->n, cv->cout);
+  if (s != MQ_OK) return s;
+  s = check_mx(xq, MQ_ROLE_ACT, cv->h, cv->w, cv->n, cv->cin);
+  if (s != MQ_OK) return s;
+  if (dyq.block_partner != 32 || xq.block_partner != 32) return MQ_ERR_UNSUPPORTED;
+  if (!dw) return MQ_ERR_NULL;
+  if ((uintptr_t)dw & 3u) return MQ_ERR_ALIGN;
+  const size_t need = gemm_workspace_bytes(c, 2, dyq.fmt, xq.fmt);
+  if (need > 0 && (!ws || ws_bytes < need)) return MQ_ERR_WORKSPACE;
+  if (ws && !aligned16(ws)) return MQ_ERR_ALIGN;
+  return hip_status(launch_backward_weight(c, view(dyq), view(xq), dw, ws, ws_bytes, (hipStream_t)stream));
+}
+
+size_t mqconv_naive_workspace_bytes(const mq_conv* cv, int op, mq_elem fa, mq_elem fb) {
+  if (!conv_ok(cv) || !fmt_ok(fa) || !fmt_ok(fb) || op < 0 || op > 2) return 0;
+  return naive_workspace_bytes(to_conv(cv), op, fa, fb);
+}
+
+static int naive_common(const mq_conv* cv, const void* a, const void* b, int fa, int fb, const void* out,
+                        void* ws, size_t ws_bytes, int op) {
+  if (!cv) return MQ_ERR_NULL;
+  if (!conv_ok(cv)) return MQ_ERR_SHAPE;
+  if (!a || !b || !out) return MQ_ERR_NULL;
+  if (!fmt_ok(fa) || !fmt_ok(fb)) return MQ_ERR_FORMAT;
+  if (((uintptr_t)a & 3u) || ((uintptr_t)b & 3u) || ((uintptr_t)out & 3u)) return MQ_ERR_ALIGN;
+  const size_t need = naive_workspace_bytes(to_conv(cv), op, fa, fb);
+  if (!ws || ws_bytes < need) return MQ_ERR_WORKSPACE;
+  if (!aligned16(ws)) return MQ_ERR_ALIGN;
+  return MQ_OK;
+}
+
+int mqconv_naive_forward(const mq_conv* cv, const float* x, const float* w, mq_elem fx, mq_elem fw, float* y,
+                         void* ws, size_t ws_bytes, void* stream) {
+  int s = naive_common(cv, x, w, fx, fw, y, ws, ws_bytes, 0);
+  if (s != MQ_OK) return s;
+  return hip_status(launch_naive_forward(to_conv(cv), x, w, fx, fw, y, ws, (hipStream_t)stream));
+}
+
+int mqconv_naive_backward_data(const mq_conv* cv, const float* dy, const float* w, mq_elem fdy, mq_elem fw,
+                               float* dx, void* ws, size_t ws_bytes, void* stream) {
+  int s = naive_common(cv, dy, w, fdy, fw, dx, ws, ws_bytes, 1);
+  if (s != MQ_OK) return s;
+  return hip_status(launch_naive_backward_data(to_conv(cv), dy, w, fdy, fw, dx, ws, (hipStream_t)stream));
+}
+
+int mqconv_naive_backward_weight(const mq_conv* cv, const float* dy, const float* x, mq_elem fdy, mq_elem fx,
+                                 float* dw, void* ws, size_t ws_bytes, void* stream) {
+  int s = naive_common(cv, dy, x, fdy, fx, dw, ws, ws_bytes, 2);
+  if (s != MQ_OK) return s;
+  return hip_status(launch_naive_backward_weight(to_conv(cv), dy, x, fdy, fx, dw, ws, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,66 @@
+// mqconv_internal.h -- launchers shared between the C ABI layer and the
+// kernel translation units. Host-side only; arguments are already validated.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace mq {
+
+// Geometry of one convolution (copied from the ABI descriptor).
+struct Conv {
+  int n, cin, h, w, cout, kh, kw, sh, sw, ph, pw;
+  int ho() const { return (h + 2 * ph - kh) / sh + 1; }
+  int wo() const { return (w + 2 * pw - kw) / sw + 1; }
+};
+
+// A packed MX operand as the kernels see it.
+struct MxView {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  int fmt;
+  int bp;
+};
+
+inline int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
+inline long long run_bytes(int fmt) { return fmt <= 1 ? 32 : (fmt <= 3 ? 24 : 16); }
+inline long long row_bytes(int fmt, long long C) { return ((C + 31) / 32) * run_bytes(fmt); }
+
+hipError_t launch_quantize(const float* src, uint8_t* codes, uint8_t* scales, int fmt, int bp, int A,
+                           int P, int B, int C, hipStream_t st);
+
+hipError_t launch_cbf_im2col(const Conv& cv, MxView x, uint8_t* col_codes, uint8_t* col_scales,
+                             hipStream_t st);
+
+// Codes of a [A][P][B] x C tensor re-laid out so that runs of 32 codes run
+// along P: out[((a*B + b)*C + c)*nPB*RB + pb*RB ...] (zeros for p >= P).
+hipError_t launch_transpose_codes(const uint8_t* in, uint8_t* out, int fmt, int A, int P, int B,
+                                  int C, hipStream_t st);
+inline size_t transposed_bytes(int fmt, long long A, long long P, long long B, long long C) {
+  return (size_t)(A * B * C * ((P + 31) / 32) * run_bytes(fmt));
+}
+
+size_t gemm_workspace_bytes(const Conv& cv, int op, int fa, int fb);
+hipError_t launch_forward(const Conv& cv, MxView x, MxView w, float* y, void* ws, size_t ws_bytes,
+                          hipStream_t st);
+hipError_t launch_backward_data(const Conv& cv, MxView dy, MxView w, float* dx, void* ws,
+                                size_t ws_bytes, hipStream_t st);
+hipError_t launch_backward_weight(const Conv& cv, MxView dy, MxView x, float* dw, void* ws,
+                                  size_t ws_bytes, hipStream_t st);
+
+// Plain packed GEMM (runs already along the contraction); splits > 1 writes
+// partial products [splits][Ma][Nb] to `out`.
+int plain_gemm_splits(long long Ma, long long Nb, long long nkb);
+hipError_t launch_plain_gemm(int fa, int fb, const uint8_t* ac, const uint8_t* as, const uint8_t* bc,
+                             const uint8_t* bs, int Ma, int Nb, int nkb, float* out, int splits,
+                             hipStream_t st);
+
+size_t naive_workspace_bytes(const Conv& cv, int op, int fa, int fb);
+hipError_t launch_naive_forward(const Conv& cv, const float* x, const float* w, int fx, int fw,
+                                float* y, void* ws, hipStream_t st);
+hipError_t launch_naive_backward_data(const Conv& cv, const float* dy, const float* w, int fdy,
+                                      int fw, float* dx, void* ws, hipStream_t st);
+hipError_t launch_naive_backward_weight(const Conv& cv, const float* dy, const float* x, int fdy,
+                                        int fx, float* dw, void* ws, hipStream_t st);
+
+}  // namespace mq

@@ -1,0 +1,84 @@
+// mx_common.h -- device-side building blocks shared by the gfx950 kernels:
+// MX element-format traits, the block-scaled MFMA wrapper and operand
+// register images.
+//
+// Element formats are the OCP MX ones the MicroQonv paper names (FP8 E4M3 /
+// E5M2, FP6 E2M3 / E3M2, FP4 E2M1; §II-D, §III-A, §IV-D) with one E8M0 scale
+// per block (§II-D "power of two encoded in E8M0"). The enumeration values
+// equal the gfx950 MFMA format selectors (cbsz/blgp): 0 fp8 E4M3,
+// 1 bf8 E5M2, 2 fp6 E2M3, 3 bf6 E3M2, 4 fp4 E2M1.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mq {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+template <int F> struct Fmt;
+// bits: code width; M: mantissa bits; E: exponent bits; bias; emax: exponent of
+// the largest binade; emin: exponent of the smallest normal; maxbits: fp32 bit
+// pattern of the largest finite value.
+template <> struct Fmt<0> { static constexpr int bits = 8, E = 4, M = 3, bias = 7,  emax = 8,  emin = -6;  static constexpr float maxv = 448.0f; };
+template <> struct Fmt<1> { static constexpr int bits = 8, E = 5, M = 2, bias = 15, emax = 15, emin = -14; static constexpr float maxv = 57344.0f; };
+template <> struct Fmt<2> { static constexpr int bits = 6, E = 2, M = 3, bias = 1,  emax = 2,  emin = 0;   static constexpr float maxv = 7.5f; };
+template <> struct Fmt<3> { static constexpr int bits = 6, E = 3, M = 2, bias = 3,  emax = 4,  emin = -2;  static constexpr float maxv = 28.0f; };
+template <> struct Fmt<4> { static constexpr int bits = 4, E = 2, M = 1, bias = 1,  emax = 2,  emin = 0;   static constexpr float maxv = 6.0f; };
+
+__host__ __device__ constexpr int run_bytes_of(int fmt) { return fmt <= 1 ? 32 : (fmt <= 3 ? 24 : 16); }
+__host__ __device__ constexpr int bits_of(int fmt) { return fmt <= 1 ? 8 : (fmt <= 3 ? 6 : 4); }
+
+// Round an fp32 value that has already been multiplied by 2^-e onto the
+// element grid: nearest, ties to even mantissa, saturating at the largest
+// finite value, sign of zero kept. Returns the sign-magnitude code.
+template <int F>
+__device__ __forceinline__ uint32_t encode_scaled(float v) {
+  using T = Fmt<F>;
+  const uint32_t ub = __float_as_uint(v);
+  const uint32_t sign = ub >> 31;
+  float a = fminf(__uint_as_float(ub & 0x7fffffffu), T::maxv);
+  const uint32_t ab = __float_as_uint(a);
+  // normal range of the element format: round the fp32 mantissa to M bits
+  constexpr int sh = 23 - T::M;
+  uint32_t r = ab + ((1u << (sh - 1)) - 1u) + ((ab >> sh) & 1u);
+  uint32_t mag_norm = (r >> sh) - (uint32_t)((127 - T::bias) << T::M);
+  // subnormal range: adding 2^(emin - M + 23) makes the fp32 adder round
+  // |v| to a multiple of the element's subnormal spacing 2^(emin - M)
+  constexpr uint32_t Kbits = (uint32_t)(T::emin - T::M + 23 + 127) << 23;
+  uint32_t mag_sub = __float_as_uint(a + __uint_as_float(Kbits)) - Kbits;
+  constexpr uint32_t min_normal_bits = (uint32_t)(T::emin + 127) << 23;
+  uint32_t mag = (ab < min_normal_bits) ? mag_sub : mag_norm;
+  return mag | (sign << (T::bits - 1));
+}
+
+// E8M0 scale byte of a block from the fp32 bit pattern of its |max|
+// (sign bit cleared): S = max(exponent field - emax, 0); 0xFF if the block
+// holds a NaN or an infinity.
+template <int F>
+__device__ __forceinline__ uint32_t scale_byte_from_amax(uint32_t amax_bits) {
+  if (amax_bits >= 0x7f800000u) return 255u;
+  int ef = (int)(amax_bits >> 23);
+  int s = ef - Fmt<F>::emax;
+  return (uint32_t)(s < 0 ? 0 : s);
+}
+
+// 2^(127 - S) as fp32 for S in [0, 253].
+__device__ __forceinline__ float inv_scale_from_byte(uint32_t S) {
+  return __uint_as_float((254u - S) << 23);
+}
+
+// Block-scaled MFMA 32x32x64 with E8M0 scales (gfx950 v_mfma_scale_f32_32x32x64_f8f6f4).
+// Register images (lane l = row r + 32 q, rows of A and of B^T are "rows"):
+//   8-bit formats: bytes 0..15 = codes [16q, 16q+16) of K-block 0 of the pair,
+//                  bytes 16..31 = codes [16q, 16q+16) of K-block 1;
+//   6/4-bit formats: the whole packed 32-code run of K-block q.
+//   scale operand: the E8M0 byte of K-block q of this lane's row.
+template <int FA, int FB>
+__device__ __forceinline__ v16f mfma_scaled_32x32x64(const v8i& a, const v8i& b, int sa, int sb, v16f c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, sa, 0, sb);
+}
+
+}  // namespace mq
