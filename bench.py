@@ -1,0 +1,248 @@
+"""Benchmark of the MicroQonv training hot path on one MI355X.
+
+One step = one pass of every step of the path over one batch of synthetic
+input: quantize X, W and G_Y once (MX, E8M0 scales), channel-batch-first
+im2col of the quantized activation, then the forward, backward-data and
+backward-weight block-scaled GEMMs. Inputs are resident in HBM before the
+timed region; R copies of every buffer are rotated so the live set exceeds
+the 256 MB Infinity Cache.
+
+Prints one JSON line. `value` is fwd+bwd TFLOP/s of the whole step
+(algorithmic FLOPs of the three GEMMs / step time). `roofline` covers the
+kernel that takes the most time per step, timed with HIP events on the
+stream it runs on. `cpu_baseline` times the CPU oracle on the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "fp6fp4": 10100.0}  # dense, MI355X public spec
+CSRC = os.path.join(ROOT, "microscaling_quantized_convolution_mxq_amd", "csrc")
+
+
+def source_sha() -> str:
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c2")
+    ap.add_argument("--rotate-mb", type=float, default=640.0, help="minimum live set across rotated buffers")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-naive", action="store_true")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the per-GPU kernels are what it measures). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import microscaling_quantized_convolution_mxq_amd as mq
+    from microscaling_quantized_convolution_mxq_amd.workloads import WORKLOADS, FORMAT_NAMES, draw_inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    mq.lib()  # fails loudly if the HIP library is missing
+    wl = WORKLOADS[args.workload]
+    s = wl.shape
+    x, w, dy = draw_inputs(wl)
+    bp = wl.bp
+
+    # ---- per-set buffers ---------------------------------------------------
+    def make_set():
+        d = {}
+        d["x"] = torch.from_numpy(x).cuda()
+        d["w"] = torch.from_numpy(w).cuda()
+        d["dy"] = torch.from_numpy(dy).cuda()
+        d["xq"] = mq.MxTensor.empty(mq.ROLE_ACT, wl.fx, bp, x.shape)
+        d["wq"] = mq.MxTensor.empty(mq.ROLE_WEIGHT, wl.fw, bp, w.shape)
+        d["gq"] = mq.MxTensor.empty(mq.ROLE_GRAD, wl.fdy, bp, dy.shape)
+        d["cc"] = torch.empty(mq.mqconv_im2col_codes_bytes(s, wl.fx), dtype=torch.uint8, device="cuda")
+        d["cs"] = torch.empty(mq.mqconv_im2col_scales_bytes(s, bp), dtype=torch.uint8, device="cuda")
+        d["y"] = torch.empty((s.ho, s.wo, s.n, s.cout), device="cuda")
+        d["dx"] = torch.empty(x.shape, device="cuda")
+        d["dw"] = torch.empty(w.shape, device="cuda")
+        d["ws1"] = torch.empty(max(1, mq.mqconv_workspace_bytes(s, 1, wl.fdy, wl.fw)), dtype=torch.uint8, device="cuda")
+        d["ws2"] = torch.empty(max(1, mq.mqconv_workspace_bytes(s, 2, wl.fdy, wl.fx)), dtype=torch.uint8, device="cuda")
+        return d
+
+    first = make_set()
+    set_bytes = sum((t.codes.numel() + t.scales.numel()) if isinstance(t, mq.MxTensor) else t.numel() * t.element_size()
+                    for t in first.values())
+    R = int(min(8, max(2, np.ceil(args.rotate_mb * 1e6 / set_bytes))))
+    sets = [first] + [make_set() for _ in range(R - 1)]
+
+    calls = ["quantize_x", "quantize_w", "quantize_dy", "cbf_im2col", "forward", "backward_data", "backward_weight"]
+
+    def run(d, name):
+        if name == "quantize_x":
+            mq.mqconv_quantize(d["x"], d["xq"])
+        elif name == "quantize_w":
+            mq.mqconv_quantize(d["w"], d["wq"])
+        elif name == "quantize_dy":
+            mq.mqconv_quantize(d["dy"], d["gq"])
+        elif name == "cbf_im2col":
+            mq.mqconv_cbf_im2col(s, d["xq"], d["cc"], d["cs"])
+        elif name == "forward":
+            mq.mqconv_forward(s, d["xq"], d["wq"], d["y"])
+        elif name == "backward_data":
+            mq.mqconv_backward_data(s, d["gq"], d["wq"], d["dx"], d["ws1"])
+        elif name == "backward_weight":
+            mq.mqconv_backward_weight(s, d["gq"], d["xq"], d["dw"], d["ws2"])
+
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        for c in calls:
+            run(sets[i % R], c)
+    torch.cuda.synchronize()
+
+    # ---- timed region: events around every call, on the kernels' stream ----
+    K = args.steps
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
+          for _ in range(K)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(K):
+        d = sets[i % R]
+        for j, c in enumerate(calls):
+            ev[i][j][0].record(stream)
+            run(d, c)
+            ev[i][j][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_start.elapsed_time(t_end) / K
+    per_call = {c: float(np.mean([ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(K)])) for j, c in enumerate(calls)}
+
+    # ---- algorithmic work -----------------------------------------------------
+    bits = {0: 8, 1: 8, 2: 6, 3: 6, 4: 4}
+    flop = s.flops()
+    nx, nw, ng = x.size, w.size, dy.size
+    xq_b = mq.mqconv_codes_bytes(mq.ROLE_ACT, wl.fx, *x.shape) + mq.mqconv_scales_bytes(mq.ROLE_ACT, bp, *x.shape)
+    wq_b = mq.mqconv_codes_bytes(mq.ROLE_WEIGHT, wl.fw, *w.shape) + mq.mqconv_scales_bytes(mq.ROLE_WEIGHT, bp, *w.shape)
+    gq_b = mq.mqconv_codes_bytes(mq.ROLE_GRAD, wl.fdy, *dy.shape) + mq.mqconv_scales_bytes(mq.ROLE_GRAD, bp, *dy.shape)
+    col_b = mq.mqconv_im2col_codes_bytes(s, wl.fx) + mq.mqconv_im2col_scales_bytes(s, bp)
+    alg_bytes = {
+        "quantize_x": 4 * nx + xq_b, "quantize_w": 4 * nw + wq_b, "quantize_dy": 4 * ng + gq_b,
+        "cbf_im2col": xq_b + col_b,
+        "forward": xq_b + wq_b + 4 * ng, "backward_data": gq_b + wq_b + 4 * nx, "backward_weight": gq_b + xq_b + 4 * nw,
+    }
+    alg_flop = {"forward": flop, "backward_data": flop, "backward_weight": flop}
+    kernels = {}
+    for c in calls:
+        t = per_call[c] * 1e-3
+        k = {"ms": round(per_call[c], 5), "GB/s": round(alg_bytes[c] / t / 1e9, 1),
+             "hbm_frac": round(alg_bytes[c] / t / 1e9 / HBM_PEAK_GBS, 4)}
+        if c in alg_flop:
+            peak = MFMA_PEAK_TFLOPS["fp8"]
+            ai = alg_flop[c] / alg_bytes[c]
+            attainable = min(peak, ai * HBM_PEAK_GBS / 1e3)
+            k.update({"TFLOP/s": round(alg_flop[c] / t / 1e12, 2), "mfma_frac": round(alg_flop[c] / t / 1e12 / peak, 4),
+                      "attainable_TFLOP/s": round(attainable, 1),
+                      "attainable_frac": round(alg_flop[c] / t / 1e12 / attainable, 4)})
+        kernels[c] = k
+
+    dominant = max(calls, key=lambda c: per_call[c])
+    t_dom = per_call[dominant] * 1e-3
+    if dominant in alg_flop and alg_flop[dominant] / alg_bytes[dominant] > 629:
+        roof = {"bound": "mfma", "achieved": round(alg_flop[dominant] / t_dom / 1e12, 2),
+                "peak": MFMA_PEAK_TFLOPS["fp8"], "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(alg_bytes[dominant] / t_dom / 1e9, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["kernel"] = dominant
+    roof["traffic"] = None
+    tf = os.path.join(ROOT, "profiles", f"traffic_{args.workload}_{dominant}.json")
+    if os.path.exists(tf):
+        rec = json.load(open(tf))
+        if rec.get("source_sha") == source_sha():
+            roof["traffic"] = rec.get("traffic_bytes")
+
+    q_im_bytes = sum(alg_bytes[c] for c in ("quantize_x", "quantize_w", "quantize_dy", "cbf_im2col"))
+    q_im_ms = sum(per_call[c] for c in ("quantize_x", "quantize_w", "quantize_dy", "cbf_im2col"))
+    gemm_ms = sum(per_call[c] for c in alg_flop)
+
+    # ---- naive comparison path (not part of the step) ------------------------
+    naive = None
+    if not args.no_naive:
+        d = sets[0]
+        wsn = [torch.empty(max(1, mq.mqconv_naive_workspace_bytes(s, op, a, b)), dtype=torch.uint8, device="cuda")
+               for op, a, b in ((0, wl.fx, wl.fw), (1, wl.fdy, wl.fw), (2, wl.fdy, wl.fx))]
+        def naive_step():
+            mq.mqconv_naive_forward(s, d["x"], d["w"], wl.fx, wl.fw, d["y"], wsn[0])
+            mq.mqconv_naive_backward_data(s, d["dy"], d["w"], wl.fdy, wl.fw, d["dx"], wsn[1])
+            mq.mqconv_naive_backward_weight(s, d["dy"], d["x"], wl.fdy, wl.fx, d["dw"], wsn[2])
+        for _ in range(3):
+            naive_step()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        nrep = 10
+        for _ in range(nrep):
+            naive_step()
+        b.record(stream)
+        torch.cuda.synchronize()
+        naive = {"ms_per_step": round(a.elapsed_time(b) / nrep, 4)}
+        del wsn
+
+    # ---- CPU baseline: the oracle on the same workload ----------------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        t0 = time.perf_counter()
+        ref = oracle.microqonv_step(s, x, w, dy, wl.fx, wl.fw, wl.fdy, bp)
+        oracle.cbf_im2col_codes(s, bp, ref["xcodes"], ref["xscales"])
+        tc = time.perf_counter() - t0
+        cpu = {"value": round(3 * flop / tc / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.threads(),
+               "kind": "oracle", "ms_per_step": round(tc * 1e3, 1),
+               "sample": f"the full {wl.name} step (quantize X, W, dY; CBF im2col of the codes; fp64 direct "
+                         "fwd, dgrad and wgrad on the dequantized operands), once"}
+
+    value = 3 * flop / (ms_step * 1e-3) / 1e12
+    out = {
+        "metric": "MX conv fwd+bwd TFLOP/s and quantize+im2col HBM GB/s (% of roofline), 1 GPU",
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": f"mx{FORMAT_NAMES[wl.fx]}x{FORMAT_NAMES[wl.fw]}/{FORMAT_NAMES[wl.fdy]} fp32-accumulate",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "n": s.n, "cin": s.cin, "cout": s.cout, "h": s.h, "w": s.w,
+                   "kernel": f"{s.kh}x{s.kw}", "stride": s.stride, "pad": s.pad, "block": f"32 ch x {bp} batch",
+                   "rotated_sets": R},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "quantize_im2col_GB/s": round(q_im_bytes / (q_im_ms * 1e-3) / 1e9, 1),
+        "quantize_im2col_hbm_frac": round(q_im_bytes / (q_im_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "gemm_TFLOP/s": round(3 * flop / (gemm_ms * 1e-3) / 1e12, 2),
+        "kernels": kernels,
+        "naive_path": naive,
+        "wall_s": round(wall, 3),
+        "source_sha": source_sha(),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,26 @@
+// gemm_dgrad.hip -- backward-data GEMM launcher (stride parity classes).
+#include "gemm_kernel.h"
+
+namespace mq {
+
+hipError_t launch_backward_data(const Conv& cv, MxView dy, MxView w, float* dx, void* ws, size_t,
+                                hipStream_t st) {
+  uint8_t* wt = static_cast<uint8_t*>(ws);
+  hipError_t e = launch_transpose_codes(w.codes, wt, w.fmt, 1, cv.cout, cv.kh * cv.kw, cv.cin, st);
+  if (e != hipSuccess) return e;
+  DgradProb p;
+  p.dyc = dy.codes; p.dys = dy.scales; p.wtc = wt; p.ws = w.scales; p.dx = dx;
+  p.N = cv.n; p.H = cv.h; p.W = cv.w; p.Cin = cv.cin; p.Cout = cv.cout; p.KH = cv.kh; p.KW = cv.kw;
+  p.sh = cv.sh; p.sw = cv.sw; p.ph = cv.ph; p.pw = cv.pw; p.Ho = cv.ho(); p.Wo = cv.wo();
+  p.ncob = ceil_div(cv.cout, 32);
+  p.dyRB = (int)run_bytes(dy.fmt); p.dyrb = p.ncob * p.dyRB; p.dybp = dy.bp; p.dynPB = ceil_div(cv.n, dy.bp);
+  p.wRB = (int)run_bytes(w.fmt); p.ncbi = ceil_div(cv.cin, 32);
+  const long long T = (long long)cv.kh * cv.kw;
+  p.dyc_bytes = (long long)p.Ho * p.Wo * cv.n * p.dyrb; p.dys_bytes = (long long)p.Ho * p.Wo * p.dynPB * p.ncob;
+  p.wtc_bytes = T * cv.cin * p.ncob * p.wRB; p.ws_bytes = T * p.ncob * p.ncbi;
+  const int maxHc = ceil_div(cv.h, cv.sh), maxWc = ceil_div(cv.w, cv.sw);
+  return launch_tiled(dy.fmt, w.fmt, p, maxHc * maxWc * cv.n, cv.cin, cv.sh * cv.sw, st);
+}
+
+
+}  // namespace mq

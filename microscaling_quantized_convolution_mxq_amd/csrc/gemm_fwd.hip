@@ -1,0 +1,21 @@
+// gemm_fwd.hip -- forward GEMM launcher (implicit CBF im2col).
+#include "gemm_kernel.h"
+
+namespace mq {
+
+hipError_t launch_forward(const Conv& cv, MxView x, MxView w, float* y, void*, size_t, hipStream_t st) {
+  FwdProb p;
+  p.xc = x.codes; p.xs = x.scales; p.wc = w.codes; p.ws = w.scales; p.y = y;
+  p.N = cv.n; p.H = cv.h; p.W = cv.w; p.Cin = cv.cin; p.Cout = cv.cout; p.KW = cv.kw;
+  p.T = cv.kh * cv.kw; p.sh = cv.sh; p.sw = cv.sw; p.ph = cv.ph; p.pw = cv.pw; p.Wo = cv.wo();
+  p.M = cv.ho() * cv.wo() * cv.n;
+  p.ncb = ceil_div(cv.cin, 32);
+  p.xRB = (int)run_bytes(x.fmt); p.xrb = p.ncb * p.xRB; p.xbp = x.bp; p.xnPB = ceil_div(cv.n, x.bp);
+  p.wRB = (int)run_bytes(w.fmt); p.wrb = p.ncb * p.wRB; p.wbp = w.bp; p.wnCoB = ceil_div(cv.cout, w.bp);
+  p.xc_bytes = (long long)cv.h * cv.w * cv.n * p.xrb; p.xs_bytes = (long long)cv.h * cv.w * p.xnPB * p.ncb;
+  p.wc_bytes = (long long)cv.cout * p.T * p.wrb; p.ws_bytes = (long long)p.T * p.wnCoB * p.ncb;
+  return launch_tiled(x.fmt, w.fmt, p, p.M, cv.cout, 1, st);
+}
+
+
+}  // namespace mq

@@ -1,0 +1,104 @@
+// gemm_wgrad.hip -- backward-weight GEMM launcher, split-K reduction and
+// workspace sizes of the GEMM entry points.
+#include "gemm_kernel.h"
+
+namespace mq {
+
+// out[i] = sum_z part[z][i] in fixed order (deterministic). Each thread sums
+// four consecutive outputs with 16-byte loads; the loop over slices is
+// unrolled so several loads are in flight per thread.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part,
+                                                            float* __restrict__ out, long long n,
+                                                            int splits) {
+  const long long i4 = ((long long)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i4 >= n) return;
+  if (i4 + 4 <= n && (n & 3) == 0) {
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    int z = 0;
+    for (; z + 4 <= splits; z += 4) {
+      float4 a = *reinterpret_cast<const float4*>(part + (long long)z * n + i4);
+      float4 b = *reinterpret_cast<const float4*>(part + (long long)(z + 1) * n + i4);
+      float4 c = *reinterpret_cast<const float4*>(part + (long long)(z + 2) * n + i4);
+      float4 d = *reinterpret_cast<const float4*>(part + (long long)(z + 3) * n + i4);
+      s.x += a.x; s.y += a.y; s.z += a.z; s.w += a.w;
+      s.x += b.x; s.y += b.y; s.z += b.z; s.w += b.w;
+      s.x += c.x; s.y += c.y; s.z += c.z; s.w += c.w;
+      s.x += d.x; s.y += d.y; s.z += d.z; s.w += d.w;
+    }
+    for (; z < splits; z++) {
+      float4 a = *reinterpret_cast<const float4*>(part + (long long)z * n + i4);
+      s.x += a.x; s.y += a.y; s.z += a.z; s.w += a.w;
+    }
+    *reinterpret_cast<float4*>(out + i4) = s;
+  } else {
+    for (long long i = i4; i < i4 + 4 && i < n; i++) {
+      float s = 0.0f;
+      for (int z = 0; z < splits; z++) s += part[(long long)z * n + i];
+      out[i] = s;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Format and tile dispatch
+// ---------------------------------------------------------------------------
+
+static int wgrad_splits(const Conv& cv, int fdy, int fx) {
+  const long long npix = (long long)cv.ho() * cv.wo();
+  const long long nNB = ceil_div(cv.n, 32);
+  const long long ops = npix * cv.cout * nNB * run_bytes(fdy) + (long long)cv.h * cv.w * cv.cin * nNB * run_bytes(fx);
+  int s = splitk_slices(cv.cout, (long long)cv.kh * cv.kw * cv.cin, npix * nNB, ops);
+  if (s > npix) s = (int)npix;
+  return s;
+}
+
+size_t gemm_workspace_bytes(const Conv& cv, int op, int fa, int fb) {
+  if (op == 0) return 0;
+  if (op == 1) {  // W re-laid with runs along Cout
+    return align256(transposed_bytes(fb, 1, cv.cout, (long long)cv.kh * cv.kw, cv.cin));
+  }
+  // op 2: fa = gradient format, fb = activation format
+  const size_t dyt = align256(transposed_bytes(fa, (long long)cv.ho() * cv.wo(), cv.n, 1, cv.cout));
+  const size_t xt = align256(transposed_bytes(fb, (long long)cv.h * cv.w, cv.n, 1, cv.cin));
+  const int S = wgrad_splits(cv, fa, fb);
+  const size_t part = S > 1 ? align256((size_t)S * cv.cout * cv.kh * cv.kw * cv.cin * 4) : 0;
+  return dyt + xt + part;
+}
+
+hipError_t launch_backward_weight(const Conv& cv, MxView dy, MxView x, float* dw, void* ws, size_t,
+                                  hipStream_t st) {
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  const long long npix_o = (long long)cv.ho() * cv.wo();
+  uint8_t* dyt = base;
+  const size_t dyt_b = align256(transposed_bytes(dy.fmt, npix_o, cv.n, 1, cv.cout));
+  uint8_t* xt = base + dyt_b;
+  const size_t xt_b = align256(transposed_bytes(x.fmt, (long long)cv.h * cv.w, cv.n, 1, cv.cin));
+  float* part = reinterpret_cast<float*>(base + dyt_b + xt_b);
+  hipError_t e = launch_transpose_codes(dy.codes, dyt, dy.fmt, (int)npix_o, cv.n, 1, cv.cout, st);
+  if (e != hipSuccess) return e;
+  e = launch_transpose_codes(x.codes, xt, x.fmt, cv.h * cv.w, cv.n, 1, cv.cin, st);
+  if (e != hipSuccess) return e;
+  const int S = wgrad_splits(cv, dy.fmt, x.fmt);
+  WgradProb p;
+  p.dytc = dyt; p.dys = dy.scales; p.xtc = xt; p.xs = x.scales; p.part = S > 1 ? part : dw;
+  p.N = cv.n; p.H = cv.h; p.W = cv.w; p.Cin = cv.cin; p.Cout = cv.cout; p.KW = cv.kw;
+  p.T = cv.kh * cv.kw; p.sh = cv.sh; p.sw = cv.sw; p.ph = cv.ph; p.pw = cv.pw; p.Wo = cv.wo();
+  p.nNB = ceil_div(cv.n, 32); p.ncob = ceil_div(cv.cout, 32); p.ncbi = ceil_div(cv.cin, 32);
+  p.dyRB = (int)run_bytes(dy.fmt); p.xRB = (int)run_bytes(x.fmt);
+  p.npix = (int)npix_o; p.pix_per_split = ceil_div(npix_o, S);
+  p.dytc_bytes = npix_o * cv.cout * p.nNB * p.dyRB; p.dys_bytes = npix_o * p.nNB * p.ncob;
+  p.xtc_bytes = (long long)cv.h * cv.w * cv.cin * p.nNB * p.xRB; p.xs_bytes = (long long)cv.h * cv.w * p.nNB * p.ncbi;
+  const long long nj = (long long)p.T * cv.cin;
+  e = launch_tiled(dy.fmt, x.fmt, p, cv.cout, (int)nj, S, st);
+  if (e != hipSuccess) return e;
+  if (S > 1) {
+    const long long n = (long long)cv.cout * nj;
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((n / 4 + 256) / 256)), dim3(256), 0, st,
+                       part, dw, n, S);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+
+}  // namespace mq

@@ -10,7 +10,9 @@ using namespace mq;
 
 namespace {
 
-const long long kMaxElems = (1LL << 31) - 1;  // index arithmetic inside kernels is 32-bit per dimension
+// Kernels address packed tensors with 32-bit byte offsets (buffer loads), so
+// every tensor is limited to 2^30 elements (channel padding included).
+const long long kMaxElems = 1LL << 30;
 
 bool fmt_ok(int f) { return f >= MQ_E4M3 && f <= MQ_E2M1; }
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -38,7 +40,7 @@ bool conv_ok(const mq_conv* c) {
   long long npad = ((long long)c->n + 31) / 32 * 32;
   if ((long long)c->h * c->w * npad * cpi > kMaxElems) return false;
   if (ho * wo * npad * cpo > kMaxElems) return false;
-  if (ho * wo * c->n * (long long)c->kh * c->kw * cpi > kMaxElems * 4) return false;
+  if (ho * wo * c->n * (long long)c->kh * c->kw * cpi > kMaxElems) return false;
   if ((long long)c->cout * c->kh * c->kw * cpi > kMaxElems) return false;
   return true;
 }

@@ -53,6 +53,7 @@ def lib():
         I = ctypes.c_int
         D = ctypes.c_double
         sig = {
+            "mqref_threads": (I, []),
             "mqref_elem_bits": (I, [I]),
             "mqref_elem_emax": (I, [I]),
             "mqref_elem_max": (D, [I]),
@@ -103,6 +104,11 @@ def out_hw(shape):
 # --------------------------------------------------------------------------
 # Element codec
 # --------------------------------------------------------------------------
+def threads() -> int:
+    """OpenMP threads the oracle's loops run on."""
+    return lib().mqref_threads()
+
+
 def decode(fmt: int, code: int) -> float:
     return lib().mqref_decode(fmt, int(code))
 

@@ -44,6 +44,18 @@ static const mqref_fmt FMT[5] = {
     {2, 1, 1, 6.0},      /* E2M1 */
 };
 
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+/* Number of threads the parallel loops use. */
+int mqref_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
 int mqref_elem_bits(int f) { return 1 + FMT[f].ebits + FMT[f].mbits; }
 
 /* Largest binade exponent of the element format: floor(log2(max normal)). */
