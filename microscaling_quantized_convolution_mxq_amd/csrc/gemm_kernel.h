@@ -321,7 +321,9 @@ template <class SA, class SB>
 struct StepRegs {
   typename SA::V ga[SA::PER];
   typename SB::V gb[SB::PER];
-  int sa[SA::PER], sb[SB::PER];
+  // kept as bytes up to the LDS byte store: widening them would put a use
+  // of the loaded value (and so a wait for the load) right after the load
+  uint8_t sa[SA::PER], sb[SB::PER];
 };
 
 // WM x WN waves; each wave owns TM x TN MFMA tiles of 32 x 32.
@@ -345,9 +347,23 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave % WM, wn = wave / WM;
-  const int z = blockIdx.z;
+  // XCD-aware tile order: the hardware hands consecutive workgroups to the 8
+  // XCDs in turn, each with its own L2. Remap so that every XCD works on a
+  // contiguous range of tiles (x fastest): neighbouring row tiles share the
+  // weight tile and the rows of the implicit im2col, and now share an L2.
+  int bx, by, z;
+  {
+    const int nx = gridDim.x, ny = gridDim.y;
+    const int nb = nx * ny * gridDim.z;
+    const int lin = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
+    const int xcd = lin % 8, idx = lin / 8, q8 = nb / 8, r8 = nb % 8;
+    const int logical = xcd < r8 ? xcd * (q8 + 1) + idx : r8 * (q8 + 1) + (xcd - r8) * q8 + idx;
+    bx = logical % nx;
+    by = (logical / nx) % ny;
+    z = logical / (nx * ny);
+  }
   const typename P::Ctx cx = prob.ctx(z);
-  const int m0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
+  const int m0 = bx * BM, n0 = by * BN;
   if (m0 >= prob.rows_a(cx)) return;  // whole tile beyond this class's rows (uniform)
   __amdgpu_buffer_rsrc_t rs[4];
   rsrcs(prob, rs);
@@ -424,14 +440,14 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
     for (int i = 0; i < SA::PER; i++) {
       if (SA::TOTAL % 256 == 0 || tid + 256 * i < SA::TOTAL) {
         *reinterpret_cast<typename SA::V*>(&lds_a[st][rowa[i] * SA::PITCH + kbia[i] * SA::RB + offa[i]]) = R.ga[i];
-        sc_a[st][rowa[i] * 2 + kbia[i]] = (uint8_t)R.sa[i];
+        sc_a[st][rowa[i] * 2 + kbia[i]] = R.sa[i];
       }
     }
 #pragma unroll
     for (int i = 0; i < SB::PER; i++) {
       if (SB::TOTAL % 256 == 0 || tid + 256 * i < SB::TOTAL) {
         *reinterpret_cast<typename SB::V*>(&lds_b[st][rowb[i] * SB::PITCH + kbib[i] * SB::RB + offb[i]]) = R.gb[i];
-        sc_b[st][rowb[i] * 2 + kbib[i]] = (uint8_t)R.sb[i];
+        sc_b[st][rowb[i] * 2 + kbib[i]] = R.sb[i];
       }
     }
   };
