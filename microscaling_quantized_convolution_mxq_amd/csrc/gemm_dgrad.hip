@@ -13,11 +13,16 @@ hipError_t launch_backward_data(const Conv& cv, MxView dy, MxView w, float* dx, 
   p.N = cv.n; p.H = cv.h; p.W = cv.w; p.Cin = cv.cin; p.Cout = cv.cout; p.KH = cv.kh; p.KW = cv.kw;
   p.sh = cv.sh; p.sw = cv.sw; p.ph = cv.ph; p.pw = cv.pw; p.Ho = cv.ho(); p.Wo = cv.wo();
   p.ncob = ceil_div(cv.cout, 32);
+  p.npair = (p.ncob + 1) / 2;
   p.dyRB = (int)run_bytes(dy.fmt); p.dyrb = p.ncob * p.dyRB; p.dybp = dy.bp; p.dynPB = ceil_div(cv.n, dy.bp);
   p.wRB = (int)run_bytes(w.fmt); p.ncbi = ceil_div(cv.cin, 32);
   const long long T = (long long)cv.kh * cv.kw;
   p.dyc_bytes = (long long)p.Ho * p.Wo * cv.n * p.dyrb; p.dys_bytes = (long long)p.Ho * p.Wo * p.dynPB * p.ncob;
   p.wtc_bytes = T * cv.cin * p.ncob * p.wRB; p.ws_bytes = T * p.ncob * p.ncbi;
+  // the taps step backwards from a row's first output pixel by up to dmax pixels
+  const long long dmax = (long long)(ceil_div(cv.kh, cv.sh) - 1) * p.Wo + (ceil_div(cv.kw, cv.sw) - 1);
+  p.dycb = (int)(dmax * cv.n * p.dyrb); p.dysb = (int)(dmax * p.dynPB * p.ncob);
+  if (!offsets_fit(p.dyc_bytes, p.dycb) || !offsets_fit(p.dys_bytes, p.dysb)) return hipErrorInvalidValue;
   const int maxHc = ceil_div(cv.h, cv.sh), maxWc = ceil_div(cv.w, cv.sw);
   return launch_tiled(dy.fmt, w.fmt, p, maxHc * maxWc * cv.n, cv.cin, cv.sh * cv.sw, st);
 }

@@ -10,10 +10,15 @@ hipError_t launch_forward(const Conv& cv, MxView x, MxView w, float* y, void*, s
   p.T = cv.kh * cv.kw; p.sh = cv.sh; p.sw = cv.sw; p.ph = cv.ph; p.pw = cv.pw; p.Wo = cv.wo();
   p.M = cv.ho() * cv.wo() * cv.n;
   p.ncb = ceil_div(cv.cin, 32);
+  p.npair = (p.ncb + 1) / 2;
   p.xRB = (int)run_bytes(x.fmt); p.xrb = p.ncb * p.xRB; p.xbp = x.bp; p.xnPB = ceil_div(cv.n, x.bp);
   p.wRB = (int)run_bytes(w.fmt); p.wrb = p.ncb * p.wRB; p.wbp = w.bp; p.wnCoB = ceil_div(cv.cout, w.bp);
   p.xc_bytes = (long long)cv.h * cv.w * cv.n * p.xrb; p.xs_bytes = (long long)cv.h * cv.w * p.xnPB * p.ncb;
   p.wc_bytes = (long long)cv.cout * p.T * p.wrb; p.ws_bytes = (long long)p.T * p.wnCoB * p.ncb;
+  // padding moves the first tap of border rows before the buffer
+  const long long lead = (long long)cv.ph * cv.w + cv.pw;
+  p.xcb = (int)(lead * cv.n * p.xrb); p.xsb = (int)(lead * p.xnPB * p.ncb);
+  if (!offsets_fit(p.xc_bytes, p.xcb) || !offsets_fit(p.xs_bytes, p.xsb)) return hipErrorInvalidValue;
   return launch_tiled(x.fmt, w.fmt, p, p.M, cv.cout, 1, st);
 }
 

@@ -12,31 +12,39 @@
 // one E8M0 scale, which is the block-scaled dot product of Eq. (7): the MFMA
 // multiplies the codes and applies both block scales per K-block.
 //
-// Kernel: 256 threads = 4 waves in a WM x WN grid; each wave owns a 64 x 64
-// output tile = 2 x 2 MFMA tiles of 32 x 32; a K-step covers two K-blocks.
-// Every K-step the workgroup stages its BM x 2 and BN x 2 runs (and their
-// scale bytes) in LDS with coalesced 16-byte (8-byte for 6-bit codes) loads,
-// double-buffered: the global loads of step s+1 are in flight while the
-// MFMAs of step s read their operands from LDS.
+// Kernel: 256 threads = 4 waves in a WM x WN grid; each wave owns TM x TN
+// MFMA tiles of 32 x 32. A K-step is a pair of K-blocks (64 codes per row).
+// Operands go from HBM straight into LDS with buffer loads that write LDS
+// (no register staging): an NS-deep ring of LDS stages, so the loads of
+// step s+NS-1 are in flight while the MFMAs of step s run, with one
+// workgroup barrier per step.
 #pragma once
 #include "mx_common.h"
 #include "mqconv_internal.h"
 
-#include <type_traits>
-
 namespace mq {
 
 // Byte offsets into a problem's code and scale buffers are the sum of a
-// per-row part (computed once per thread) and a per-K-block part (uniform
-// across the workgroup, advanced incrementally in scalar registers):
+// per-row part (fixed per lane, the buffer load's vector offset) and a
+// per-step part (uniform across the workgroup, advanced incrementally in
+// scalar registers, the load's scalar offset):
 //   code  = row.code + k.code,   scale = row.scale + k.scale
-// valid iff row.ok && k.ok && (row.p0 + k.g0) in [0, lim0) && (row.p1 + k.g1)
-// in [0, lim1); the geometric test covers the image borders of the implicit
-// im2col. Invalid (zero) blocks read from past the end of the buffer, where
-// raw buffer loads return 0.
+// Both parts are kept non-negative: where a row or a step moves backwards
+// (padding, backward taps) the problem adds a bias to one part and the
+// buffer descriptor starts that many bytes before the buffer.
+// A block is valid iff row.ok && (row.p0 + k.g0) in [0, lim0) && (row.p1 +
+// k.g1) in [0, lim1); the geometric test covers the image borders of the
+// implicit im2col. Invalid (zero) blocks read from past the end of the
+// buffer, where raw buffer loads return 0 (the range check covers the sum of
+// both offsets, per dword). The second K-block of a pair is the first one
+// moved by a problem-wide PairDelta; a step whose pair has no second K-block
+// (odd count) says so with tail().
 constexpr int kOOB = 0x7fffff00;
+constexpr int kFar = 0x40000000;  // row coordinate that fails every border test
 struct RowInfo { int code, scale, p0, p1; bool ok; };
-struct KInfo { int code, scale, g0, g1; bool ok; };
+struct KInfo { int code, scale, g0, g1; };
+struct PairDelta { int code, scale, g0, g1; };
+struct GRange { int min0, max0, min1, max1; };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, long long bytes) {
   const int n = bytes < (long long)kOOB ? (int)bytes : kOOB;
@@ -46,62 +54,88 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, long 
 // ---------------------------------------------------------------------------
 // Problem descriptors
 // ---------------------------------------------------------------------------
-// Forward: rows m = (ho, wo, n), K-block (kh, kw, cb).
+// Forward: rows m = (ho, wo, n); a step is channel blocks (v, v+1) of tap (kh, kw).
 struct FwdProb {
   const uint8_t *xc, *xs, *wc, *ws;
   float* y;
   long long xc_bytes, xs_bytes, wc_bytes, ws_bytes;
   int N, H, W, Cin, Cout, KW, T, sh, sw, ph, pw, Wo, M;
-  int xrb, xRB, xbp, xnPB, ncb;  // activation row bytes, run bytes, bp, partner blocks, channel blocks
-  int wrb, wRB, wnCoB, wbp;       // weight row bytes, run bytes, Cout blocks, bp
+  int xrb, xRB, xbp, xnPB, ncb, npair;  // activation row bytes, run bytes, bp, partner blocks, channel blocks, pairs
+  int wrb, wRB, wnCoB, wbp;              // weight row bytes, run bytes, Cout blocks, bp
+  int xcb, xsb;                          // bias of the activation row offsets (padding)
+  static constexpr bool kGeoA = true, kGeoB = false;
   struct Ctx {};
-  struct KS { int kh, kw, v; };
+  struct KS {
+    int kh, kw, v;
+    __device__ void uniform() { kh = __builtin_amdgcn_readfirstlane(kh); kw = __builtin_amdgcn_readfirstlane(kw); v = __builtin_amdgcn_readfirstlane(v); }
+  };
   __device__ Ctx ctx(int) const { return Ctx{}; }
   __device__ int rows_a(const Ctx&) const { return M; }
   __device__ int ncols() const { return Cout; }
-  __device__ void krange(const Ctx&, int, int& lo, int& hi) const { lo = 0; hi = T * ncb; }
-  __device__ KS kstart(const Ctx&, int kb) const {
-    const int u = kb / ncb; KS k; k.v = kb - u * ncb; k.kh = u / KW; k.kw = u - k.kh * KW; return k;
+  __device__ void steps(const Ctx&, int, int& lo, int& hi) const { lo = 0; hi = T * npair; }
+  __device__ KS kstart(const Ctx&, int s) const {
+    const int u = s / npair; KS k; k.v = 2 * (s - u * npair); k.kh = u / KW; k.kw = u - k.kh * KW; return k;
   }
-  __device__ void knext(const Ctx&, KS& k) const {
-    if (++k.v == ncb) { k.v = 0; if (++k.kw == KW) { k.kw = 0; k.kh++; } }
+  // advances k by one step when go (field-wise selects: no branch, no memory)
+  __device__ void knext(const Ctx&, KS& k, bool go) const {
+    const int v = k.v + 2;
+    const bool w1 = v >= ncb;
+    const int kw = k.kw + (w1 ? 1 : 0);
+    const bool w2 = kw == KW;
+    k.v = go ? (w1 ? 0 : v) : k.v; k.kw = go ? (w2 ? 0 : kw) : k.kw; k.kh += (go & w2) ? 1 : 0;
   }
+  __device__ bool tail(const Ctx&, const KS& k) const { return k.v + 1 >= ncb; }
+  __device__ PairDelta pd_a() const { return PairDelta{xRB, 1, 0, 0}; }
+  __device__ PairDelta pd_b() const { return PairDelta{wRB, 1, 0, 0}; }
   __device__ RowInfo row_a(const Ctx&, int m) const {
     RowInfo r; r.ok = m < M; const int mm = r.ok ? m : 0;
     const int pix = mm / N, n = mm - pix * N, ho = pix / Wo, wo = pix - ho * Wo;
     r.p0 = ho * sh - ph; r.p1 = wo * sw - pw;
     const int p = r.p0 * W + r.p1;
-    r.code = (p * N + n) * xrb; r.scale = (p * xnPB + n / xbp) * ncb; return r;
+    r.code = (p * N + n) * xrb + xcb; r.scale = (p * xnPB + n / xbp) * ncb + xsb; return r;
   }
-  __device__ KInfo k_a(const Ctx&, const KS& k, bool ok) const {
+  __device__ KInfo k_a(const Ctx&, const KS& k) const {
     const int d = k.kh * W + k.kw;
-    return KInfo{d * N * xrb + k.v * xRB, d * xnPB * ncb + k.v, k.kh, k.kw, ok};
+    return KInfo{d * N * xrb + k.v * xRB, d * xnPB * ncb + k.v, k.kh, k.kw};
   }
   __device__ RowInfo row_b(const Ctx&, int c) const {
     RowInfo r; r.ok = c < Cout; const int cc = r.ok ? c : 0;
     r.code = cc * T * wrb; r.scale = (cc / wbp) * ncb; r.p0 = 0; r.p1 = 0; return r;
   }
-  __device__ KInfo k_b(const Ctx&, const KS& k, bool ok) const {
+  __device__ KInfo k_b(const Ctx&, const KS& k) const {
     const int tap = k.kh * KW + k.kw;
-    return KInfo{tap * wrb + k.v * wRB, tap * wnCoB * ncb + k.v, 0, 0, ok};
+    return KInfo{tap * wrb + k.v * wRB, tap * wnCoB * ncb + k.v, 0, 0};
   }
   __device__ int lim_a0() const { return H; }
   __device__ int lim_a1() const { return W; }
+  __device__ int lim_b0() const { return 1; }
+  __device__ int lim_b1() const { return 1; }
+  // range of (k.g0, k.g1) over all steps, and steps valid for every row
+  __device__ GRange g_range_a(const Ctx&) const { return GRange{0, T / KW - 1, 0, KW - 1}; }
+  __device__ GRange g_range_b(const Ctx&) const { return GRange{0, 0, 0, 0}; }
+  __device__ bool step_interior_a(const Ctx&, const KS&) const { return false; }
+  __device__ bool step_interior_b(const Ctx&, const KS&) const { return true; }
   __device__ float* out_row(const Ctx&, int, int m) const { return m < M ? y + (long long)m * Cout : nullptr; }
 };
 
 // Backward-data: rows of parity class z are h = hq*sh + ph_c, w = wq*sw + pw_c
 // (and all n); the taps reaching them are kh = kh0 + sh*ih, kw = kw0 + sw*iw,
-// from output pixel (ho0 - ih, wo0 - iw). K-block (ih, iw, cob).
+// from output pixel (ho0 - ih, wo0 - iw). A step is Cout blocks (v, v+1) of
+// tap (ih, iw).
 struct DgradProb {
   const uint8_t *dyc, *dys, *wtc, *ws;
   float* dx;
   long long dyc_bytes, dys_bytes, wtc_bytes, ws_bytes;
   int N, H, W, Cin, Cout, KH, KW, sh, sw, ph, pw, Ho, Wo;
-  int dyrb, dyRB, dybp, dynPB, ncob;  // gradient row bytes, run bytes, bp, partner blocks, Cout blocks
-  int wRB, ncbi;                      // weight run bytes, Cin blocks
+  int dyrb, dyRB, dybp, dynPB, ncob, npair;  // gradient row bytes, run bytes, bp, partner blocks, Cout blocks, pairs
+  int wRB, ncbi;                             // weight run bytes, Cin blocks
+  int dycb, dysb;                            // bias of the step offsets (backward taps)
+  static constexpr bool kGeoA = true, kGeoB = false;
   struct Ctx { int ph_c, pw_c, Hc, Wc, kh0, kw0, nkh, nkw, M; };
-  struct KS { int ih, iw, v; };
+  struct KS {
+    int ih, iw, v;
+    __device__ void uniform() { ih = __builtin_amdgcn_readfirstlane(ih); iw = __builtin_amdgcn_readfirstlane(iw); v = __builtin_amdgcn_readfirstlane(v); }
+  };
   __device__ Ctx ctx(int z) const {
     Ctx c; c.ph_c = z / sw; c.pw_c = z - c.ph_c * sw;
     c.Hc = H > c.ph_c ? (H - c.ph_c + sh - 1) / sh : 0;
@@ -114,14 +148,21 @@ struct DgradProb {
   }
   __device__ int rows_a(const Ctx& c) const { return c.M; }
   __device__ int ncols() const { return Cin; }
-  __device__ void krange(const Ctx& c, int, int& lo, int& hi) const { lo = 0; hi = c.nkh * c.nkw * ncob; }
-  __device__ KS kstart(const Ctx& c, int kb) const {
+  __device__ void steps(const Ctx& c, int, int& lo, int& hi) const { lo = 0; hi = c.nkh * c.nkw * npair; }
+  __device__ KS kstart(const Ctx& c, int s) const {
     const int nkw = c.nkw > 0 ? c.nkw : 1;
-    const int u = kb / ncob; KS k; k.v = kb - u * ncob; k.ih = u / nkw; k.iw = u - k.ih * nkw; return k;
+    const int u = s / npair; KS k; k.v = 2 * (s - u * npair); k.ih = u / nkw; k.iw = u - k.ih * nkw; return k;
   }
-  __device__ void knext(const Ctx& c, KS& k) const {
-    if (++k.v == ncob) { k.v = 0; if (++k.iw == c.nkw) { k.iw = 0; k.ih++; } }
+  __device__ void knext(const Ctx& c, KS& k, bool go) const {
+    const int v = k.v + 2;
+    const bool w1 = v >= ncob;
+    const int iw = k.iw + (w1 ? 1 : 0);
+    const bool w2 = iw == c.nkw;
+    k.v = go ? (w1 ? 0 : v) : k.v; k.iw = go ? (w2 ? 0 : iw) : k.iw; k.ih += (go & w2) ? 1 : 0;
   }
+  __device__ bool tail(const Ctx&, const KS& k) const { return k.v + 1 >= ncob; }
+  __device__ PairDelta pd_a() const { return PairDelta{dyRB, 1, 0, 0}; }
+  __device__ PairDelta pd_b() const { return PairDelta{wRB, ncbi, 0, 0}; }
   __device__ RowInfo row_a(const Ctx& c, int m) const {
     RowInfo r; r.ok = m < c.M; const int mm = r.ok ? m : 0;
     const int wc = c.Wc > 0 ? c.Wc : 1;
@@ -132,20 +173,26 @@ struct DgradProb {
     const int p = r.p0 * Wo + r.p1;
     r.code = (p * N + n) * dyrb; r.scale = (p * dynPB + n / dybp) * ncob; return r;
   }
-  __device__ KInfo k_a(const Ctx&, const KS& k, bool ok) const {
+  __device__ KInfo k_a(const Ctx&, const KS& k) const {
     const int d = k.ih * Wo + k.iw;
-    return KInfo{-d * N * dyrb + k.v * dyRB, -d * dynPB * ncob + k.v, -k.ih, -k.iw, ok};
+    return KInfo{-d * N * dyrb + k.v * dyRB + dycb, -d * dynPB * ncob + k.v + dysb, -k.ih, -k.iw};
   }
   __device__ RowInfo row_b(const Ctx&, int c) const {
     RowInfo r; r.ok = c < Cin; const int cc = r.ok ? c : 0;
     r.code = cc * ncob * wRB; r.scale = cc / 32; r.p0 = 0; r.p1 = 0; return r;
   }
-  __device__ KInfo k_b(const Ctx& c, const KS& k, bool ok) const {
+  __device__ KInfo k_b(const Ctx& c, const KS& k) const {
     const int tap = (c.kh0 + sh * k.ih) * KW + (c.kw0 + sw * k.iw);
-    return KInfo{(tap * Cin * ncob + k.v) * wRB, (tap * ncob + k.v) * ncbi, 0, 0, ok};
+    return KInfo{(tap * Cin * ncob + k.v) * wRB, (tap * ncob + k.v) * ncbi, 0, 0};
   }
   __device__ int lim_a0() const { return Ho; }
   __device__ int lim_a1() const { return Wo; }
+  __device__ int lim_b0() const { return 1; }
+  __device__ int lim_b1() const { return 1; }
+  __device__ GRange g_range_a(const Ctx& c) const { return GRange{1 - c.nkh, 0, 1 - c.nkw, 0}; }
+  __device__ GRange g_range_b(const Ctx&) const { return GRange{0, 0, 0, 0}; }
+  __device__ bool step_interior_a(const Ctx&, const KS&) const { return false; }
+  __device__ bool step_interior_b(const Ctx&, const KS&) const { return true; }
   __device__ float* out_row(const Ctx& c, int, int m) const {
     if (m >= c.M) return nullptr;
     const int pix = m / N, n = m - pix * N, hq = pix / c.Wc, wq = pix - hq * c.Wc;
@@ -155,53 +202,82 @@ struct DgradProb {
 };
 
 // Backward-weight on codes re-laid with runs along N: rows co (A) and
-// j = (kh, kw, ci) (B); K-block (ho, wo, nb) over the slice's output pixels.
+// j = (kh, kw, ci) (B); K-block (ho, wo, nb). A step pairs N blocks (nb,
+// nb+1) of one output pixel, or, when N fits one block, the output pixels
+// (ho, wo) and (ho, wo+1). Slice z covers steps [z*steps_per_split, ...).
 struct WgradProb {
   const uint8_t *dytc, *dys, *xtc, *xs;
   float* part;
   long long dytc_bytes, dys_bytes, xtc_bytes, xs_bytes;
-  int N, H, W, Cin, Cout, KW, T, sh, sw, ph, pw, Wo, nNB, ncob, ncbi;
+  int N, H, W, Cin, Cout, KW, T, sh, sw, ph, pw, Ho, Wo, nNB, ncob, ncbi;
   int dyRB, xRB;
-  int npix;  // Ho*Wo
-  int pix_per_split;
+  int pair_w;          // 1: pairs along wo (nNB == 1), 0: pairs along nb
+  int nsub;            // pairs per pixel (pair_w 0) or per output row (pair_w 1)
+  int total_steps, steps_per_split;
+  int xtcb, xsb;       // bias of the activation row offsets (padding)
+  static constexpr bool kGeoA = false, kGeoB = true;
   struct Ctx {};
-  struct KS { int ho, wo, v; };
+  struct KS {
+    int ho, wo, v;
+    __device__ void uniform() { ho = __builtin_amdgcn_readfirstlane(ho); wo = __builtin_amdgcn_readfirstlane(wo); v = __builtin_amdgcn_readfirstlane(v); }
+  };
   __device__ Ctx ctx(int) const { return Ctx{}; }
   __device__ int rows_a(const Ctx&) const { return Cout; }
   __device__ int ncols() const { return T * Cin; }
-  __device__ void krange(const Ctx&, int z, int& lo, int& hi) const {
-    int p0 = z * pix_per_split, p1 = min(npix, p0 + pix_per_split);
-    lo = p0 * nNB; hi = max(p0, p1) * nNB;
+  __device__ void steps(const Ctx&, int z, int& lo, int& hi) const {
+    lo = min(total_steps, z * steps_per_split); hi = min(total_steps, lo + steps_per_split);
   }
-  __device__ KS kstart(const Ctx&, int kb) const {
-    const int u = kb / nNB; KS k; k.v = kb - u * nNB; k.ho = u / Wo; k.wo = u - k.ho * Wo; return k;
+  __device__ KS kstart(const Ctx&, int s) const {
+    KS k;
+    if (pair_w) { k.ho = s / nsub; k.wo = 2 * (s - k.ho * nsub); k.v = 0; }
+    else { const int pix = s / nsub; k.v = 2 * (s - pix * nsub); k.ho = pix / Wo; k.wo = pix - k.ho * Wo; }
+    return k;
   }
-  __device__ void knext(const Ctx&, KS& k) const {
-    if (++k.v == nNB) { k.v = 0; if (++k.wo == Wo) { k.wo = 0; k.ho++; } }
+  __device__ void knext(const Ctx&, KS& k, bool go) const {
+    const int v = k.v + (pair_w ? 0 : 2);
+    const bool wv = !pair_w & (v >= nNB);
+    const int wo = k.wo + (pair_w ? 2 : (wv ? 1 : 0));
+    const bool ww = pair_w ? (wo >= Wo) : (wo == Wo);
+    k.v = go ? (wv ? 0 : v) : k.v; k.wo = go ? (ww ? 0 : wo) : k.wo; k.ho += (go & ww) ? 1 : 0;
+  }
+  __device__ bool tail(const Ctx&, const KS& k) const { return pair_w ? k.wo + 1 >= Wo : k.v + 1 >= nNB; }
+  __device__ PairDelta pd_a() const {
+    return pair_w ? PairDelta{Cout * nNB * dyRB, nNB * ncob, 0, 0} : PairDelta{dyRB, ncob, 0, 0};
+  }
+  __device__ PairDelta pd_b() const {
+    return pair_w ? PairDelta{sw * Cin * nNB * xRB, sw * nNB * ncbi, 0, sw} : PairDelta{xRB, ncbi, 0, 0};
   }
   __device__ RowInfo row_a(const Ctx&, int m) const {
     RowInfo r; r.ok = m < Cout; const int co = r.ok ? m : 0;
     r.code = co * nNB * dyRB; r.scale = co / 32; r.p0 = 0; r.p1 = 0; return r;
   }
-  __device__ KInfo k_a(const Ctx&, const KS& k, bool ok) const {
+  __device__ KInfo k_a(const Ctx&, const KS& k) const {
     const int pix = k.ho * Wo + k.wo;
-    return KInfo{(pix * Cout * nNB + k.v) * dyRB, (pix * nNB + k.v) * ncob, 0, 0, ok};
+    return KInfo{(pix * Cout * nNB + k.v) * dyRB, (pix * nNB + k.v) * ncob, 0, 0};
   }
   __device__ RowInfo row_b(const Ctx&, int j) const {
     RowInfo r; r.ok = j < T * Cin; const int jj = r.ok ? j : 0;
     const int tap = jj / Cin, ci = jj - tap * Cin, kh = tap / KW, kw = tap - kh * KW;
     r.p0 = kh - ph; r.p1 = kw - pw;
     const int p = r.p0 * W + r.p1;
-    r.code = (p * Cin + ci) * nNB * xRB; r.scale = p * nNB * ncbi + ci / 32; return r;
+    r.code = (p * Cin + ci) * nNB * xRB + xtcb; r.scale = p * nNB * ncbi + ci / 32 + xsb; return r;
   }
-  __device__ KInfo k_b(const Ctx&, const KS& k, bool ok) const {
+  __device__ KInfo k_b(const Ctx&, const KS& k) const {
     const int g0 = k.ho * sh, g1 = k.wo * sw, d = g0 * W + g1;
-    return KInfo{(d * Cin * nNB + k.v) * xRB, (d * nNB + k.v) * ncbi, g0, g1, ok};
+    return KInfo{(d * Cin * nNB + k.v) * xRB, (d * nNB + k.v) * ncbi, g0, g1};
   }
   __device__ int lim_a0() const { return 1; }
   __device__ int lim_a1() const { return 1; }
   __device__ int lim_b0() const { return H; }
   __device__ int lim_b1() const { return W; }
+  __device__ GRange g_range_a(const Ctx&) const { return GRange{0, 0, 0, 0}; }
+  __device__ GRange g_range_b(const Ctx&) const { return GRange{0, (Ho - 1) * sh, 0, (Wo - 1) * sw}; }
+  __device__ bool step_interior_a(const Ctx&, const KS&) const { return true; }
+  // every tap of every row in range for this step (both pixels of a pair)
+  __device__ bool step_interior_b(const Ctx&, const KS& k) const {
+    const int h0 = k.ho * sh - ph, w0 = k.wo * sw - pw, w1 = w0 + (pair_w ? sw : 0);
+    return (h0 >= 0) & (h0 + T / KW - 1 < H) & (w0 >= 0) & (w1 + KW - 1 < W);
+  }
   __device__ float* out_row(const Ctx&, int z, int m) const {
     return m < Cout ? part + ((long long)z * Cout + m) * ((long long)T * Cin) : nullptr;
   }
@@ -209,58 +285,66 @@ struct WgradProb {
 
 // Plain GEMM out[m][c] = sum_kb A[m][kb] . B[c][kb] over packed rows whose
 // runs already follow the contraction (used by the naive comparison path).
-// Slice z covers K-blocks [z*kb_per_split, (z+1)*kb_per_split) and writes its
-// partial product to out + z*Ma*Nb.
+// Slice z covers K-block pairs [z*pairs_per_split, (z+1)*pairs_per_split)
+// and writes its partial product to out + z*Ma*Nb.
 struct PlainProb {
   const uint8_t *ac, *as, *bc, *bs;
   float* out;
   long long ac_bytes, as_bytes, bc_bytes, bs_bytes;
-  int Ma, Nb, nkb, aRB, bRB, kb_per_split, arb, brb;
+  int Ma, Nb, nkb, aRB, bRB, pairs_per_split, arb, brb;
+  static constexpr bool kGeoA = false, kGeoB = false;
   struct Ctx {};
-  struct KS { int u; };
+  struct KS {
+    int u;
+    __device__ void uniform() { u = __builtin_amdgcn_readfirstlane(u); }
+  };
   __device__ Ctx ctx(int) const { return Ctx{}; }
   __device__ int rows_a(const Ctx&) const { return Ma; }
   __device__ int ncols() const { return Nb; }
-  __device__ void krange(const Ctx&, int z, int& lo, int& hi) const {
-    lo = z * kb_per_split; hi = min(nkb, lo + kb_per_split); if (hi < lo) hi = lo;
+  __device__ void steps(const Ctx&, int z, int& lo, int& hi) const {
+    const int np = (nkb + 1) / 2;
+    lo = min(np, z * pairs_per_split); hi = min(np, lo + pairs_per_split);
   }
-  __device__ KS kstart(const Ctx&, int kb) const { return KS{kb}; }
-  __device__ void knext(const Ctx&, KS& k) const { k.u++; }
+  __device__ KS kstart(const Ctx&, int s) const { return KS{2 * s}; }
+  __device__ void knext(const Ctx&, KS& k, bool go) const { k.u += go ? 2 : 0; }
+  __device__ bool tail(const Ctx&, const KS& k) const { return k.u + 1 >= nkb; }
+  __device__ PairDelta pd_a() const { return PairDelta{aRB, 1, 0, 0}; }
+  __device__ PairDelta pd_b() const { return PairDelta{bRB, 1, 0, 0}; }
   __device__ RowInfo row_a(const Ctx&, int m) const {
     RowInfo r; r.ok = m < Ma; const int mm = r.ok ? m : 0;
     r.code = mm * arb; r.scale = mm * nkb; r.p0 = 0; r.p1 = 0; return r;
   }
-  __device__ KInfo k_a(const Ctx&, const KS& k, bool ok) const { return KInfo{k.u * aRB, k.u, 0, 0, ok}; }
+  __device__ KInfo k_a(const Ctx&, const KS& k) const { return KInfo{k.u * aRB, k.u, 0, 0}; }
   __device__ RowInfo row_b(const Ctx&, int c) const {
     RowInfo r; r.ok = c < Nb; const int cc = r.ok ? c : 0;
     r.code = cc * brb; r.scale = cc * nkb; r.p0 = 0; r.p1 = 0; return r;
   }
-  __device__ KInfo k_b(const Ctx&, const KS& k, bool ok) const { return KInfo{k.u * bRB, k.u, 0, 0, ok}; }
+  __device__ KInfo k_b(const Ctx&, const KS& k) const { return KInfo{k.u * bRB, k.u, 0, 0}; }
   __device__ int lim_a0() const { return 1; }
   __device__ int lim_a1() const { return 1; }
+  __device__ int lim_b0() const { return 1; }
+  __device__ int lim_b1() const { return 1; }
+  __device__ GRange g_range_a(const Ctx&) const { return GRange{0, 0, 0, 0}; }
+  __device__ GRange g_range_b(const Ctx&) const { return GRange{0, 0, 0, 0}; }
+  __device__ bool step_interior_a(const Ctx&, const KS&) const { return true; }
+  __device__ bool step_interior_b(const Ctx&, const KS&) const { return true; }
   __device__ float* out_row(const Ctx&, int z, int m) const {
     return m < Ma ? out + ((long long)z * Ma + m) * Nb : nullptr;
   }
 };
 
-// Default limits for the B side (weights and plain rows have no borders).
-template <class P> __device__ __forceinline__ int lim_b0(const P&) { return 1; }
-template <class P> __device__ __forceinline__ int lim_b1(const P&) { return 1; }
-template <> __device__ __forceinline__ int lim_b0<WgradProb>(const WgradProb& p) { return p.lim_b0(); }
-template <> __device__ __forceinline__ int lim_b1<WgradProb>(const WgradProb& p) { return p.lim_b1(); }
-
 // Buffers of each problem: (A codes, A scales, B codes, B scales).
 __device__ inline void rsrcs(const FwdProb& p, __amdgpu_buffer_rsrc_t (&r)[4]) {
-  r[0] = make_rsrc(p.xc, p.xc_bytes); r[1] = make_rsrc(p.xs, p.xs_bytes);
+  r[0] = make_rsrc(p.xc - p.xcb, p.xc_bytes + p.xcb); r[1] = make_rsrc(p.xs - p.xsb, p.xs_bytes + p.xsb);
   r[2] = make_rsrc(p.wc, p.wc_bytes); r[3] = make_rsrc(p.ws, p.ws_bytes);
 }
 __device__ inline void rsrcs(const DgradProb& p, __amdgpu_buffer_rsrc_t (&r)[4]) {
-  r[0] = make_rsrc(p.dyc, p.dyc_bytes); r[1] = make_rsrc(p.dys, p.dys_bytes);
+  r[0] = make_rsrc(p.dyc - p.dycb, p.dyc_bytes + p.dycb); r[1] = make_rsrc(p.dys - p.dysb, p.dys_bytes + p.dysb);
   r[2] = make_rsrc(p.wtc, p.wtc_bytes); r[3] = make_rsrc(p.ws, p.ws_bytes);
 }
 __device__ inline void rsrcs(const WgradProb& p, __amdgpu_buffer_rsrc_t (&r)[4]) {
   r[0] = make_rsrc(p.dytc, p.dytc_bytes); r[1] = make_rsrc(p.dys, p.dys_bytes);
-  r[2] = make_rsrc(p.xtc, p.xtc_bytes); r[3] = make_rsrc(p.xs, p.xs_bytes);
+  r[2] = make_rsrc(p.xtc - p.xtcb, p.xtc_bytes + p.xtcb); r[3] = make_rsrc(p.xs - p.xsb, p.xs_bytes + p.xsb);
 }
 __device__ inline void rsrcs(const PlainProb& p, __amdgpu_buffer_rsrc_t (&r)[4]) {
   r[0] = make_rsrc(p.ac, p.ac_bytes); r[1] = make_rsrc(p.as, p.as_bytes);
@@ -268,84 +352,104 @@ __device__ inline void rsrcs(const PlainProb& p, __amdgpu_buffer_rsrc_t (&r)[4])
 }
 
 // ---------------------------------------------------------------------------
-// Staging of one operand (BR rows x 2 runs) into LDS
+// LDS image of one operand stage
 // ---------------------------------------------------------------------------
-template <int F, int BR>
-struct Stage {
-  static constexpr int RB = run_bytes_of(F);
-  static constexpr int CH = (RB == 24) ? 8 : 16;       // bytes per load
-  static constexpr int NC = 2 * RB / CH;               // loads per row
-  // LDS row pitch: 2 runs plus a skew that keeps the 32 rows one MFMA tile
-  // reads (16-byte reads for 8/4-bit codes, 8-byte reads for 6-bit) on
-  // distinct banks
-  static constexpr int PITCH = (RB == 24) ? 2 * RB + 8 : 2 * RB + 16;
-  static constexpr int TOTAL = BR * NC;
-  static constexpr int PER = (TOTAL + 255) / 256;      // loads per thread
-  static constexpr int BYTES = BR * PITCH;
-  typedef typename std::conditional<CH == 16, v4i, v2i>::type V;
-};
-
-template <class V>
-__device__ __forceinline__ V buffer_load(__amdgpu_buffer_rsrc_t r, int off);
-template <>
-__device__ __forceinline__ v4i buffer_load<v4i>(__amdgpu_buffer_rsrc_t r, int off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-}
-template <>
-__device__ __forceinline__ v2i buffer_load<v2i>(__amdgpu_buffer_rsrc_t r, int off) {
-  return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
-}
-
-// Reads one 32x32x64 operand register image (see mx_common.h) of LDS row `base`.
+// Stage layout of an operand with BR rows: [kb][row][NPK] 16-byte slots, kb
+// the K-block of the pair. A run is NPK slots (8-bit and 6-bit codes: 2, the
+// 6-bit ones carrying 12 code bytes each; 4-bit codes: 1). With NPK = 2 the
+// two slots of a row are swapped for rows with swz(row) = 1, so that the
+// 16-byte operand reads of 8 (or 16) consecutive rows hit distinct LDS
+// banks. Scales: one dword per (kb, row), [kb][row]. A 64-lane load that
+// writes LDS fills 64 consecutive slots (or scale dwords), so each load
+// belongs to one K-block.
 template <int F>
-__device__ __forceinline__ v8i lds_operand(const uint8_t* base, int q) {
+struct Op {
+  static constexpr int RB = run_bytes_of(F);
+  static constexpr int NPK = RB == 16 ? 1 : 2;   // slots per run
+  static constexpr int CH = RB == 24 ? 12 : 16;  // code bytes per slot
+};
+__device__ __forceinline__ int slot_swz(int row) { return ((row >> 2) ^ (row >> 3)) & 1; }
+// LDS code reads per 32x32x64 operand image
+template <int F>
+constexpr int F_READS() { return F <= 3 ? 2 : 1; }
+
+// Reads one 32x32x64 operand register image (see mx_common.h) of row `row`
+// from an operand stage with BR rows.
+template <int F, int BR>
+__device__ __forceinline__ v8i lds_operand(const uint8_t* stage, int row, int swz, int q) {
   v8i r = {0, 0, 0, 0, 0, 0, 0, 0};
   if constexpr (F <= 1) {
-    v4i lo = *reinterpret_cast<const v4i*>(base + 16 * q);
-    v4i hi = *reinterpret_cast<const v4i*>(base + 32 + 16 * q);
+    // bytes 0..15: K-block 0, piece q; bytes 16..31: K-block 1, piece q
+    const v4i lo = *reinterpret_cast<const v4i*>(stage + row * 32 + 16 * (q ^ swz));
+    const v4i hi = *reinterpret_cast<const v4i*>(stage + BR * 32 + row * 32 + 16 * (q ^ swz));
     r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3]; r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
   } else if constexpr (F <= 3) {
-    const v2i* p = reinterpret_cast<const v2i*>(base + 24 * q);
-    v2i x0 = p[0], x1 = p[1], x2 = p[2];
-    r[0] = x0[0]; r[1] = x0[1]; r[2] = x1[0]; r[3] = x1[1]; r[4] = x2[0]; r[5] = x2[1];
+    // the 24-byte run of K-block q: 12 bytes from each of its two slots
+    const uint8_t* base = stage + q * BR * 32 + row * 32;
+    const v4i lo = *reinterpret_cast<const v4i*>(base + 16 * swz);
+    const v4i hi = *reinterpret_cast<const v4i*>(base + 16 * (1 ^ swz));
+    r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = hi[0]; r[4] = hi[1]; r[5] = hi[2];
   } else {
-    v4i x = *reinterpret_cast<const v4i*>(base + 16 * q);
+    // the 16-byte run of K-block q
+    const v4i x = *reinterpret_cast<const v4i*>(stage + q * BR * 16 + row * 16);
     r[0] = x[0]; r[1] = x[1]; r[2] = x[2]; r[3] = x[3];
   }
   return r;
 }
 
-// One K-step's staged loads of a thread, held in registers between the
-// global load and the LDS write.
-template <class SA, class SB>
-struct StepRegs {
-  typename SA::V ga[SA::PER];
-  typename SB::V gb[SB::PER];
-  // kept as bytes up to the LDS byte store: widening them would put a use
-  // of the loaded value (and so a wait for the load) right after the load
-  uint8_t sa[SA::PER], sb[SB::PER];
-};
+// Per-lane part of one LDS-writing load: byte offset of the lane's piece
+// relative to the step's uniform offset (kOOB when the row is outside the
+// problem or the load only keeps the count uniform) and the row's border
+// coordinates for the pair's K-block.
+struct LaneLd { int off, p0, p1; };
 
-// WM x WN waves; each wave owns TM x TN MFMA tiles of 32 x 32.
-template <int FA, int FB, class P, int WM, int WN, int TM, int TN>
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+// 16 bytes per lane into LDS at lds + 16*lane, from voff + soff
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, soff, 0, 0);
+}
+// one byte per lane, zero-extended into the dword at lds + 4*lane
+__device__ __forceinline__ void dma1(__amdgpu_buffer_rsrc_t r, uint8_t* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 1, voff, soff, 0, 0);
+}
+// s_waitcnt with vmcnt(N) and lgkmcnt(0) (expcnt not waited)
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+// Workgroup barrier without a memory fence: the waits that complete an LDS
+// stage are explicit (wait_vm_lgkm0), and the empty asm statements keep the
+// compiler from moving LDS accesses across the barrier.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// WM x WN waves; each wave owns TM x TN MFMA tiles of 32 x 32; NS LDS stages.
+template <int FA, int FB, class P, int WM, int WN, int TM, int TN, int NS>
 __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
-  using SA = Stage<FA, BM>;
-  using SB = Stage<FB, BN>;
-  // One LDS arena: the two staging stages (A runs, B runs, A scales, B
-  // scales) during the K loop, the epilogue strips afterwards.
-  constexpr int OFF_B = 2 * SA::BYTES, OFF_SA = OFF_B + 2 * SB::BYTES, OFF_SB = OFF_SA + 2 * BM * 2;
-  constexpr int STAGING = OFF_SB + 2 * BN * 2;
+  using OA = Op<FA>;
+  using OB = Op<FB>;
+  constexpr int A_BYTES = 2 * BM * OA::NPK * 16, B_BYTES = 2 * BN * OB::NPK * 16;
+  constexpr int OFF_B = A_BYTES, OFF_SA = OFF_B + B_BYTES, OFF_SB = OFF_SA + 8 * BM;
+  constexpr int STAGE = OFF_SB + 8 * BN;
+  // LDS-writing loads (64 lanes each) per stage and per wave; load g of a
+  // kind belongs to K-block g / (loads per K-block)
+  constexpr int NCA = 2 * BM * OA::NPK / 64, NCB = 2 * BN * OB::NPK / 64, NSA = 2 * BM / 64, NSB = 2 * BN / 64;
+  constexpr int WCA = (NCA + 3) / 4, WCB = (NCB + 3) / 4, WSA = (NSA + 3) / 4, WSB = (NSB + 3) / 4;
+  constexpr int WPS = WCA + WCB + WSA + WSB;
+  // 1 KB sink for the loads a wave issues only to keep its count uniform
+  constexpr int DUMMY = NS * STAGE;
   constexpr int STRIP = 32 * (TN * 32 + 8) * 4;  // one wave's epilogue strip (bytes)
-  constexpr int ARENA = STAGING > 4 * STRIP ? STAGING : 4 * STRIP;
+  constexpr int ARENA = (DUMMY + 1024) > 4 * STRIP ? (DUMMY + 1024) : 4 * STRIP;
   __shared__ __attribute__((aligned(16))) uint8_t arena[ARENA];
-  auto lds_a = reinterpret_cast<uint8_t(*)[SA::BYTES]>(arena);
-  auto lds_b = reinterpret_cast<uint8_t(*)[SB::BYTES]>(arena + OFF_B);
-  auto sc_a = reinterpret_cast<uint8_t(*)[BM * 2]>(arena + OFF_SA);
-  auto sc_b = reinterpret_cast<uint8_t(*)[BN * 2]>(arena + OFF_SB);
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave % WM, wn = wave / WM;
   // XCD-aware tile order: the hardware hands consecutive workgroups to the 8
   // XCDs in turn, each with its own L2. Remap so that every XCD works on a
@@ -367,89 +471,98 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
   if (m0 >= prob.rows_a(cx)) return;  // whole tile beyond this class's rows (uniform)
   __amdgpu_buffer_rsrc_t rs[4];
   rsrcs(prob, rs);
+  const PairDelta dA = prob.pd_a(), dB = prob.pd_b();
+  const int la0 = prob.lim_a0(), la1 = prob.lim_a1(), lb0 = prob.lim_b0(), lb1 = prob.lim_b1();
+  const GRange gA = prob.g_range_a(cx), gB = prob.g_range_b(cx);
 
-  // Load c = tid + 256*i of a stage covers row c / NC and piece c % NC of
-  // the row's two runs: K-block kbi of the pair, byte offset `off` in the run.
-  RowInfo ra[SA::PER], rb[SB::PER];
-  int rowa[SA::PER], kbia[SA::PER], offa[SA::PER];
-  int rowb[SB::PER], kbib[SB::PER], offb[SB::PER];
-#pragma unroll
-  for (int i = 0; i < SA::PER; i++) {
-    const int c = tid + 256 * i, part = c % SA::NC;
-    rowa[i] = min(c / SA::NC, BM - 1);
-    kbia[i] = part / (SA::NC / 2);
-    offa[i] = (part % (SA::NC / 2)) * SA::CH;
-    ra[i] = prob.row_a(cx, m0 + rowa[i]);
-  }
-#pragma unroll
-  for (int i = 0; i < SB::PER; i++) {
-    const int c = tid + 256 * i, part = c % SB::NC;
-    rowb[i] = min(c / SB::NC, BN - 1);
-    kbib[i] = part / (SB::NC / 2);
-    offb[i] = (part % (SB::NC / 2)) * SB::CH;
-    rb[i] = prob.row_b(cx, n0 + rowb[i]);
-  }
-  const int la0 = prob.lim_a0(), la1 = prob.lim_a1(), lb0 = lim_b0(prob), lb1 = lim_b1(prob);
-
-  int kb_lo, kb_hi;
-  prob.krange(cx, z, kb_lo, kb_hi);
-  // K-block iterator over the fetch sequence (uniform)
-  typename P::KS kit = prob.kstart(cx, kb_lo);
-  int kb_next = kb_lo;
-
-  // (bitwise &, not &&: straight-line selects instead of branches)
-  auto offset = [&](const RowInfo& r, const KInfo& k, int lim0, int lim1, int& code, int& scale) {
-    const bool ok = r.ok & k.ok & ((unsigned)(r.p0 + k.g0) < (unsigned)lim0) &
-                    ((unsigned)(r.p1 + k.g1) < (unsigned)lim1);
-    code = ok ? r.code + k.code : kOOB;
-    scale = ok ? r.scale + k.scale : kOOB;
+  // Per-lane load descriptors. `inner` collects whether all of this wave's
+  // rows stay inside the borders for every step of the problem.
+  LaneLd ca[WCA], cb[WCB], sa[WSA], sb[WSB];
+  bool innerA = true, innerB = true;
+  auto make_lane = [&](LaneLd& l, int g, int ngl, int per_kb, int np, int ch, bool is_code, bool is_a,
+                       bool& inner) {
+    const bool real = g < ngl;
+    const int kb = real ? (64 * g) / per_kb : 0;
+    const int t = real ? 64 * g + lane - kb * per_kb : 0;
+    const int row = t / np, piece = np == 2 ? ((t & 1) ^ slot_swz(row)) : 0;
+    const PairDelta& d = is_a ? dA : dB;
+    const RowInfo r = is_a ? prob.row_a(cx, m0 + row) : prob.row_b(cx, n0 + row);
+    const bool ok = r.ok & real;
+    l.off = ok ? (is_code ? r.code + piece * ch + kb * d.code : r.scale + kb * d.scale) : kOOB;
+    l.p0 = r.p0 + kb * d.g0;
+    l.p1 = r.p1 + kb * d.g1;
+    const GRange& gr = is_a ? gA : gB;
+    const int L0 = is_a ? la0 : lb0, L1 = is_a ? la1 : lb1;
+    inner = inner & (!ok | ((l.p0 + gr.min0 >= 0) & (l.p0 + gr.max0 < L0) & (l.p1 + gr.min1 >= 0) &
+                            (l.p1 + gr.max1 < L1)));
   };
-  // global -> registers for the next K-block pair; no branches: zero blocks
-  // (and pairs past the end) load from past the end of the buffer and read 0
-  auto fetch = [&](StepRegs<SA, SB>& R) {
-    const bool ok0 = kb_next < kb_hi, ok1 = kb_next + 1 < kb_hi;
-    const KInfo a0 = prob.k_a(cx, kit, ok0), b0 = prob.k_b(cx, kit, ok0);
-    if (ok0) prob.knext(cx, kit);
-    const KInfo a1 = prob.k_a(cx, kit, ok1), b1 = prob.k_b(cx, kit, ok1);
-    if (ok1) prob.knext(cx, kit);
-    kb_next += 2;
-    int oca[SA::PER], osa[SA::PER], ocb[SB::PER], osb[SB::PER];
 #pragma unroll
-    for (int i = 0; i < SA::PER; i++) offset(ra[i], kbia[i] ? a1 : a0, la0, la1, oca[i], osa[i]);
+  for (int k = 0; k < WCA; k++) make_lane(ca[k], wave + 4 * k, NCA, BM * OA::NPK, OA::NPK, OA::CH, true, true, innerA);
 #pragma unroll
-    for (int i = 0; i < SB::PER; i++) offset(rb[i], kbib[i] ? b1 : b0, lb0, lb1, ocb[i], osb[i]);
-    // the loads leave together; their consumers (the LDS writes of commit)
-    // stay behind the MFMAs that run meanwhile
-    __builtin_amdgcn_sched_barrier(0);
+  for (int k = 0; k < WCB; k++) make_lane(cb[k], wave + 4 * k, NCB, BN * OB::NPK, OB::NPK, OB::CH, true, false, innerB);
 #pragma unroll
-    for (int i = 0; i < SA::PER; i++) {
-      R.ga[i] = buffer_load<typename SA::V>(rs[0], oca[i] + offa[i]);
-      R.sa[i] = __builtin_amdgcn_raw_buffer_load_b8(rs[1], osa[i], 0, 0);
-    }
+  for (int k = 0; k < WSA; k++) make_lane(sa[k], wave + 4 * k, NSA, BM, 1, 0, false, true, innerA);
 #pragma unroll
-    for (int i = 0; i < SB::PER; i++) {
-      R.gb[i] = buffer_load<typename SB::V>(rs[2], ocb[i] + offb[i]);
-      R.sb[i] = __builtin_amdgcn_raw_buffer_load_b8(rs[3], osb[i], 0, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
+  for (int k = 0; k < WSB; k++) make_lane(sb[k], wave + 4 * k, NSB, BN, 1, 0, false, false, innerB);
+  // wave-uniform: no lane of this wave ever needs the border test
+  const bool waveA = !P::kGeoA || __builtin_amdgcn_ballot_w64(!innerA) == 0;
+  const bool waveB = !P::kGeoB || __builtin_amdgcn_ballot_w64(!innerB) == 0;
+
+  int s_lo, s_hi;
+  prob.steps(cx, z, s_lo, s_hi);
+  // The step state is uniform; readfirstlane keeps it in scalar registers
+  // (integer division by runtime values leaves it in vector ones, and a
+  // vector-held scalar offset would turn each load into a loop).
+  typename P::KS kit = prob.kstart(cx, s_lo);
+  kit.uniform();
+  int s_next = s_lo;
+
+  // lane offset of a load at this step (branch-free): the border test is
+  // void when the wave or the step is known to be inside
+  auto voff = [&](const LaneLd& l, const KInfo& k, bool geo, bool inside, int L0, int L1) {
+    if (!geo) return l.off;
+    const bool ok = inside | (((unsigned)(l.p0 + k.g0) < (unsigned)L0) & ((unsigned)(l.p1 + k.g1) < (unsigned)L1));
+    return ok ? l.off : kOOB;
   };
-  // registers -> LDS stage st. Every load of a run carries the run's scale
-  // byte, so all of them store it (same value, same address).
-  auto commit = [&](const StepRegs<SA, SB>& R, int st) {
+  // uniform offset of a load of K-block kb at this step (kOOB: the load reads zeros)
+  auto soff = [](int kofs, int kb, bool live, bool tl) { return (live & !(kb & tl)) ? kofs : kOOB; };
+
+  // Issue the loads of the next step into stage `st`. Loads past the last
+  // step read zeros, so every wave issues WPS loads per step.
+  auto issue = [&](int st) {
+    const bool live = s_next < s_hi;
+    const KInfo ka = prob.k_a(cx, kit), kb = prob.k_b(cx, kit);
+    const bool tl = prob.tail(cx, kit);
+    const bool inA = waveA || prob.step_interior_a(cx, kit);
+    const bool inB = waveB || prob.step_interior_b(cx, kit);
+    uint8_t* const stage = arena + st * STAGE;
 #pragma unroll
-    for (int i = 0; i < SA::PER; i++) {
-      if (SA::TOTAL % 256 == 0 || tid + 256 * i < SA::TOTAL) {
-        *reinterpret_cast<typename SA::V*>(&lds_a[st][rowa[i] * SA::PITCH + kbia[i] * SA::RB + offa[i]]) = R.ga[i];
-        sc_a[st][rowa[i] * 2 + kbia[i]] = R.sa[i];
-      }
+    for (int k = 0; k < WCA; k++) {
+      const int g = wave + 4 * k, kbi = g * 64 >= BM * OA::NPK;
+      dma16(rs[0], g < NCA ? stage + g * 1024 : arena + DUMMY, voff(ca[k], ka, P::kGeoA, inA, la0, la1),
+            soff(ka.code, kbi, live, tl));
     }
 #pragma unroll
-    for (int i = 0; i < SB::PER; i++) {
-      if (SB::TOTAL % 256 == 0 || tid + 256 * i < SB::TOTAL) {
-        *reinterpret_cast<typename SB::V*>(&lds_b[st][rowb[i] * SB::PITCH + kbib[i] * SB::RB + offb[i]]) = R.gb[i];
-        sc_b[st][rowb[i] * 2 + kbib[i]] = R.sb[i];
-      }
+    for (int k = 0; k < WCB; k++) {
+      const int g = wave + 4 * k, kbi = g * 64 >= BN * OB::NPK;
+      dma16(rs[2], g < NCB ? stage + OFF_B + g * 1024 : arena + DUMMY, voff(cb[k], kb, P::kGeoB, inB, lb0, lb1),
+            soff(kb.code, kbi, live, tl));
     }
+#pragma unroll
+    for (int k = 0; k < WSA; k++) {
+      const int g = wave + 4 * k, kbi = g * 64 >= BM;
+      dma1(rs[1], g < NSA ? stage + OFF_SA + g * 256 : arena + DUMMY, voff(sa[k], ka, P::kGeoA, inA, la0, la1),
+           soff(ka.scale, kbi, live, tl));
+    }
+#pragma unroll
+    for (int k = 0; k < WSB; k++) {
+      const int g = wave + 4 * k, kbi = g * 64 >= BN;
+      dma1(rs[3], g < NSB ? stage + OFF_SB + g * 256 : arena + DUMMY, voff(sb[k], kb, P::kGeoB, inB, lb0, lb1),
+           soff(kb.scale, kbi, live, tl));
+    }
+    prob.knext(cx, kit, live);
+    kit.uniform();
+    s_next++;
   };
 
   v16f acc[TM][TN];
@@ -461,59 +574,69 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
       for (int e = 0; e < 16; e++) acc[i][j][e] = 0.0f;
 
   const int r32 = lane & 31, q = lane >> 5;
-  auto compute = [&](int st) {
-    v8i a[TM], b[TN];
-    int sa[TM], sb[TN];
+  const int swz = slot_swz(r32);  // tile rows start at multiples of 32
+  v8i a[TM], b[TN];
+  int xa[TM], xb[TN];
+  auto read_operands = [&](int st) {
+    const uint8_t* const stage = arena + st * STAGE;
 #pragma unroll
     for (int i = 0; i < TM; i++) {
       const int row = (wm * TM + i) * 32 + r32;
-      a[i] = lds_operand<FA>(&lds_a[st][row * SA::PITCH], q);
-      sa[i] = sc_a[st][row * 2 + q];
+      a[i] = lds_operand<FA, BM>(stage, row, swz, q);
+      xa[i] = *reinterpret_cast<const int*>(stage + OFF_SA + (q * BM + row) * 4);
     }
 #pragma unroll
     for (int j = 0; j < TN; j++) {
       const int row = (wn * TN + j) * 32 + r32;
-      b[j] = lds_operand<FB>(&lds_b[st][row * SB::PITCH], q);
-      sb[j] = sc_b[st][row * 2 + q];
+      b[j] = lds_operand<FB, BN>(stage + OFF_B, row, swz, q);
+      xb[j] = *reinterpret_cast<const int*>(stage + OFF_SB + (q * BN + row) * 4);
     }
+  };
+  auto mfmas = [&]() {
 #pragma unroll
     for (int i = 0; i < TM; i++)
 #pragma unroll
       for (int j = 0; j < TN; j++)
-        acc[i][j] = mfma_scaled_32x32x64<FA, FB>(a[i], b[j], sa[i], sb[j], acc[i][j]);
+        acc[i][j] = mfma_scaled_32x32x64<FA, FB>(a[i], b[j], xa[i], xb[j], acc[i][j]);
   };
 
-  // Pipeline: LDS stages 0/1 and register sets R0/R1; the loads of step s+2
-  // are issued before step s computes, so two steps of MFMAs cover each
-  // load's latency. The step count is rounded up to even (a trailing zero
-  // step adds nothing).
-  const int nsteps = (kb_hi - kb_lo + 1) / 2;
-  if (nsteps > 0) {
-    StepRegs<SA, SB> R0, R1;
-    fetch(R0);
-    fetch(R1);
-    commit(R0, 0);
-    __syncthreads();
-    for (int s = 0; s < nsteps; s += 2) {
-      fetch(R0);
-      compute(0);
-      __builtin_amdgcn_sched_barrier(0);
-      commit(R1, 1);
-      __syncthreads();
-      fetch(R1);
-      compute(1);
-      __builtin_amdgcn_sched_barrier(0);
-      commit(R0, 0);
-      __syncthreads();
+  // Ring of NS stages: at step s the loads of step s+NS-1 go into the stage
+  // that step s-1 computed from. The barrier before them both completes
+  // stage s (every wave has waited for its own loads of step s) and retires
+  // every wave's reads of stage s-1.
+  const int nsteps = s_hi - s_lo;
+#pragma unroll
+  for (int i = 0; i < NS - 1; i++) issue(i);
+  int cs = 0;
+  // LDS reads per step of a wave, for the instruction schedule below
+  constexpr int RDA = F_READS<FA>(), RDB = F_READS<FB>();
+  constexpr int NDS = TM * (RDA + 1) + TN * (RDB + 1);
+  constexpr int NMF = TM * TN;
+  constexpr int VPM = (WPS + NMF - 1) / NMF;  // loads issued after each MFMA
+  for (int s = 0; s < nsteps; s++) {
+    wait_vm_lgkm0<(NS - 2) * WPS>();
+    stage_barrier();
+    read_operands(cs);
+    issue(cs == 0 ? NS - 1 : cs - 1);
+    mfmas();
+    // operand reads first, then the loads of the next stage spread between
+    // the MFMAs so their issue overlaps the matrix pipe
+    __builtin_amdgcn_sched_group_barrier(0x100, NDS, 0);
+#pragma unroll
+    for (int i = 0; i < NMF; i++) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, VPM, 0);
     }
+    cs = cs + 1 == NS ? 0 : cs + 1;
   }
+  wait_vm_lgkm0<0>();
+  stage_barrier();
 
-  // Epilogue through LDS (the staging buffers are free now). For each 32-row
-  // strip i a wave writes its TN accumulator tiles as a 32 x (TN*32) fp32
-  // block (lane = column r32 of rows 8*(e/4) + 4*q + e%4), then reads it back
-  // as 16-byte row pieces and stores them: each output row segment goes out
-  // as whole 16-byte vectors from consecutive lanes.
-  __syncthreads();
+  // Epilogue through LDS (the stages are free now). For each 32-row strip i
+  // a wave writes its TN accumulator tiles as a 32 x (TN*32) fp32 block
+  // (lane = column r32 of rows 8*(e/4) + 4*q + e%4), then reads it back as
+  // 16-byte row pieces and stores them: each output row segment goes out as
+  // whole 16-byte vectors from consecutive lanes.
   constexpr int EW = TN * 32;        // strip width (columns)
   constexpr int EP = EW + 8;         // LDS pitch in floats (rows 4 apart land 32 banks apart)
   float* strip = reinterpret_cast<float*>(arena + wave * STRIP);
@@ -553,12 +676,12 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
   }
 }
 
-template <class P, int WM, int WN, int TM, int TN>
+template <class P, int WM, int WN, int TM, int TN, int NS>
 hipError_t launch_gemm(int fa, int fb, const P& prob, dim3 grid, hipStream_t st) {
-#define MQ_CASE(A, B)                                                                               \
-  if (fa == A && fb == B) {                                                                         \
-    hipLaunchKernelGGL((mx_gemm_kernel<A, B, P, WM, WN, TM, TN>), grid, dim3(256), 0, st, prob);    \
-    return hipGetLastError();                                                                       \
+#define MQ_CASE(A, B)                                                                                 \
+  if (fa == A && fb == B) {                                                                           \
+    hipLaunchKernelGGL((mx_gemm_kernel<A, B, P, WM, WN, TM, TN, NS>), grid, dim3(256), 0, st, prob);  \
+    return hipGetLastError();                                                                         \
   }
   MQ_CASE(0, 0) MQ_CASE(0, 1) MQ_CASE(0, 2) MQ_CASE(0, 3) MQ_CASE(0, 4)
   MQ_CASE(1, 0) MQ_CASE(1, 1) MQ_CASE(1, 2) MQ_CASE(1, 3) MQ_CASE(1, 4)
@@ -598,14 +721,18 @@ hipError_t launch_tiled(int fa, int fb, const P& prob, int M, int Ncols, int Z, 
   const TileChoice t = choose_tile(M, Ncols, Z);
   dim3 grid(ceil_div(M, t.bm), ceil_div(Ncols, t.bn), Z);
   switch (t.id) {
-    case 0: return launch_gemm<P, 4, 1, 2, 2>(fa, fb, prob, grid, st);
-    case 1: return launch_gemm<P, 2, 2, 2, 2>(fa, fb, prob, grid, st);
-    case 2: return launch_gemm<P, 2, 2, 4, 2>(fa, fb, prob, grid, st);
-    default: return launch_gemm<P, 1, 4, 2, 2>(fa, fb, prob, grid, st);
+    case 0: return launch_gemm<P, 4, 1, 2, 2, 3>(fa, fb, prob, grid, st);
+    case 1: return launch_gemm<P, 2, 2, 2, 2, 3>(fa, fb, prob, grid, st);
+    case 2: return launch_gemm<P, 2, 2, 4, 2, 3>(fa, fb, prob, grid, st);
+    default: return launch_gemm<P, 1, 4, 2, 2, 3>(fa, fb, prob, grid, st);
   }
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// A buffer and the bias in front of it must stay below the offset that
+// marks invalid blocks.
+inline bool offsets_fit(long long bytes, long long bias) { return bytes + bias < 0x7f000000LL; }
 
 // Number of K slices for an output of Ma x Nb with nkb K-blocks: enough
 // workgroups to cover the GPU about twice, while the fp32 partial sums that
@@ -620,6 +747,5 @@ inline int splitk_slices(long long Ma, long long Nb, long long nkb, long long op
   if (s < 1) s = 1;
   return (int)s;
 }
-
 
 }  // namespace mq

@@ -17,7 +17,7 @@ hipError_t launch_plain_gemm(int fa, int fb, const uint8_t* ac, const uint8_t* a
   p.arb = nkb * p.aRB; p.brb = nkb * p.bRB;
   p.ac_bytes = (long long)Ma * p.arb; p.as_bytes = (long long)Ma * nkb;
   p.bc_bytes = (long long)Nb * p.brb; p.bs_bytes = (long long)Nb * nkb;
-  p.kb_per_split = ceil_div(nkb, splits);
+  p.pairs_per_split = ceil_div((nkb + 1) / 2, splits);
   return launch_tiled(fa, fb, p, Ma, Nb, splits, st);
 }
 

@@ -43,12 +43,26 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 // Format and tile dispatch
 // ---------------------------------------------------------------------------
 
+// K-steps of the backward-weight GEMM: pairs of N blocks per output pixel,
+// or pairs of output pixels along wo when N fits one block.
+struct WgradSteps { int pair_w, nsub, total; };
+static WgradSteps wgrad_steps(const Conv& cv) {
+  const int nNB = ceil_div(cv.n, 32);
+  WgradSteps s;
+  s.pair_w = nNB == 1;
+  s.nsub = s.pair_w ? (cv.wo() + 1) / 2 : (nNB + 1) / 2;
+  s.total = s.pair_w ? cv.ho() * s.nsub : cv.ho() * cv.wo() * s.nsub;
+  return s;
+}
+
 static int wgrad_splits(const Conv& cv, int fdy, int fx) {
   const long long npix = (long long)cv.ho() * cv.wo();
   const long long nNB = ceil_div(cv.n, 32);
   const long long ops = npix * cv.cout * nNB * run_bytes(fdy) + (long long)cv.h * cv.w * cv.cin * nNB * run_bytes(fx);
-  int s = splitk_slices(cv.cout, (long long)cv.kh * cv.kw * cv.cin, npix * nNB, ops);
-  if (s > npix) s = (int)npix;
+  const WgradSteps ks = wgrad_steps(cv);
+  int s = splitk_slices(cv.cout, (long long)cv.kh * cv.kw * cv.cin, 2LL * ks.total, ops);
+  if (s > ks.total) s = ks.total;
+  if (s < 1) s = 1;
   return s;
 }
 
@@ -82,12 +96,17 @@ hipError_t launch_backward_weight(const Conv& cv, MxView dy, MxView x, float* dw
   WgradProb p;
   p.dytc = dyt; p.dys = dy.scales; p.xtc = xt; p.xs = x.scales; p.part = S > 1 ? part : dw;
   p.N = cv.n; p.H = cv.h; p.W = cv.w; p.Cin = cv.cin; p.Cout = cv.cout; p.KW = cv.kw;
-  p.T = cv.kh * cv.kw; p.sh = cv.sh; p.sw = cv.sw; p.ph = cv.ph; p.pw = cv.pw; p.Wo = cv.wo();
+  p.T = cv.kh * cv.kw; p.sh = cv.sh; p.sw = cv.sw; p.ph = cv.ph; p.pw = cv.pw; p.Ho = cv.ho(); p.Wo = cv.wo();
   p.nNB = ceil_div(cv.n, 32); p.ncob = ceil_div(cv.cout, 32); p.ncbi = ceil_div(cv.cin, 32);
   p.dyRB = (int)run_bytes(dy.fmt); p.xRB = (int)run_bytes(x.fmt);
-  p.npix = (int)npix_o; p.pix_per_split = ceil_div(npix_o, S);
+  const WgradSteps ks = wgrad_steps(cv);
+  p.pair_w = ks.pair_w; p.nsub = ks.nsub; p.total_steps = ks.total; p.steps_per_split = ceil_div(ks.total, S);
   p.dytc_bytes = npix_o * cv.cout * p.nNB * p.dyRB; p.dys_bytes = npix_o * p.nNB * p.ncob;
   p.xtc_bytes = (long long)cv.h * cv.w * cv.cin * p.nNB * p.xRB; p.xs_bytes = (long long)cv.h * cv.w * p.nNB * p.ncbi;
+  // padding moves the taps of the first output pixels before the buffer
+  const long long lead = (long long)cv.ph * cv.w + cv.pw;
+  p.xtcb = (int)(lead * cv.cin * p.nNB * p.xRB); p.xsb = (int)(lead * p.nNB * p.ncbi);
+  if (!offsets_fit(p.xtc_bytes, p.xtcb) || !offsets_fit(p.xs_bytes, p.xsb)) return hipErrorInvalidValue;
   const long long nj = (long long)p.T * cv.cin;
   e = launch_tiled(dy.fmt, x.fmt, p, cv.cout, (int)nj, S, st);
   if (e != hipSuccess) return e;
