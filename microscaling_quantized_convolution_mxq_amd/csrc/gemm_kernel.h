@@ -734,14 +734,15 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // marks invalid blocks.
 inline bool offsets_fit(long long bytes, long long bias) { return bytes + bias < 0x7f000000LL; }
 
-// Number of K slices for an output of Ma x Nb with nkb K-blocks: enough
-// workgroups to cover the GPU about twice, while the fp32 partial sums that
-// the slices write and the reduction reads stay below the operand bytes.
+// Number of K slices for an output of Ma x Nb with nkb K-blocks: up to two
+// workgroups per compute unit (a partial last wave of workgroups would
+// double the time), while the fp32 partial sums that the slices write and
+// the reduction reads stay below twice the operand bytes.
 inline int splitk_slices(long long Ma, long long Nb, long long nkb, long long operand_bytes) {
   const TileChoice t = choose_tile(Ma, Nb, 1);
   const long long tiles = ceil_div(Ma, t.bm) * ceil_div(Nb, t.bn);
-  long long s = (512 + tiles - 1) / tiles;
-  const long long cap_traffic = operand_bytes / (8 * Ma * Nb) + 1;  // 2 x 4 bytes per partial
+  long long s = 512 / tiles;
+  const long long cap_traffic = operand_bytes / (4 * Ma * Nb) + 1;  // 2 x 4 bytes per partial
   if (s > cap_traffic) s = cap_traffic;
   if (s > nkb / 4) s = nkb / 4;  // at least 4 K-blocks per slice
   if (s < 1) s = 1;

@@ -4,37 +4,47 @@
 
 namespace mq {
 
-// out[i] = sum_z part[z][i] in fixed order (deterministic). Each thread sums
-// four consecutive outputs with 16-byte loads; the loop over slices is
-// unrolled so several loads are in flight per thread.
+// out[i] = sum_z part[z][i] in a fixed order (deterministic): the G thread
+// groups of a block sum the slices z = g, g+G, g+2G, ... in turn, then the G
+// group sums are added in order g = 0..G-1. VEC: four consecutive outputs
+// per thread with 16-byte loads (n a multiple of 4).
+constexpr int kRedG = 16;
+template <bool VEC>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part,
                                                             float* __restrict__ out, long long n,
                                                             int splits) {
-  const long long i4 = ((long long)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (i4 >= n) return;
-  if (i4 + 4 <= n && (n & 3) == 0) {
-    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-    int z = 0;
-    for (; z + 4 <= splits; z += 4) {
-      float4 a = *reinterpret_cast<const float4*>(part + (long long)z * n + i4);
-      float4 b = *reinterpret_cast<const float4*>(part + (long long)(z + 1) * n + i4);
-      float4 c = *reinterpret_cast<const float4*>(part + (long long)(z + 2) * n + i4);
-      float4 d = *reinterpret_cast<const float4*>(part + (long long)(z + 3) * n + i4);
-      s.x += a.x; s.y += a.y; s.z += a.z; s.w += a.w;
-      s.x += b.x; s.y += b.y; s.z += b.z; s.w += b.w;
-      s.x += c.x; s.y += c.y; s.z += c.z; s.w += c.w;
-      s.x += d.x; s.y += d.y; s.z += d.z; s.w += d.w;
+  constexpr int C = 256 / kRedG;  // output columns per block
+  constexpr int E = VEC ? 4 : 1;  // outputs per column
+  __shared__ float red[kRedG][C][E];
+  const int tc = threadIdx.x % C, g = threadIdx.x / C;
+  const long long i0 = ((long long)blockIdx.x * C + tc) * E;
+  float s[E];
+#pragma unroll
+  for (int e = 0; e < E; e++) s[e] = 0.0f;
+  if (i0 < n) {
+    if constexpr (VEC) {
+      for (int z = g; z < splits; z += kRedG) {
+        const float4 a = *reinterpret_cast<const float4*>(part + (long long)z * n + i0);
+        s[0] += a.x; s[1] += a.y; s[2] += a.z; s[3] += a.w;
+      }
+    } else {
+      for (int z = g; z < splits; z += kRedG) s[0] += part[(long long)z * n + i0];
     }
-    for (; z < splits; z++) {
-      float4 a = *reinterpret_cast<const float4*>(part + (long long)z * n + i4);
-      s.x += a.x; s.y += a.y; s.z += a.z; s.w += a.w;
+  }
+#pragma unroll
+  for (int e = 0; e < E; e++) red[g][tc][e] = s[e];
+  __syncthreads();
+  if (g == 0 && i0 < n) {
+#pragma unroll
+    for (int e = 0; e < E; e++) {
+      float t = red[0][tc][e];
+      for (int k = 1; k < kRedG; k++) t += red[k][tc][e];
+      s[e] = t;
     }
-    *reinterpret_cast<float4*>(out + i4) = s;
-  } else {
-    for (long long i = i4; i < i4 + 4 && i < n; i++) {
-      float s = 0.0f;
-      for (int z = 0; z < splits; z++) s += part[(long long)z * n + i];
-      out[i] = s;
+    if constexpr (VEC) {
+      *reinterpret_cast<float4*>(out + i0) = make_float4(s[0], s[1], s[2], s[3]);
+    } else {
+      out[i0] = s[0];
     }
   }
 }
@@ -112,8 +122,14 @@ hipError_t launch_backward_weight(const Conv& cv, MxView dy, MxView x, float* dw
   if (e != hipSuccess) return e;
   if (S > 1) {
     const long long n = (long long)cv.cout * nj;
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((n / 4 + 256) / 256)), dim3(256), 0, st,
-                       part, dw, n, S);
+    constexpr int C = 256 / kRedG;
+    if ((n & 3) == 0) {
+      hipLaunchKernelGGL(splitk_reduce_kernel<true>, dim3((unsigned)ceil_div(n / 4, C)), dim3(256), 0, st,
+                         part, dw, n, S);
+    } else {
+      hipLaunchKernelGGL(splitk_reduce_kernel<false>, dim3((unsigned)ceil_div(n, C)), dim3(256), 0, st,
+                         part, dw, n, S);
+    }
     e = hipGetLastError();
   }
   return e;
