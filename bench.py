@@ -7,10 +7,16 @@ backward-weight block-scaled GEMMs. Inputs are resident in HBM before the
 timed region; R copies of every buffer are rotated so the live set exceeds
 the 256 MB Infinity Cache.
 
-Prints one JSON line. `value` is fwd+bwd TFLOP/s of the whole step
-(algorithmic FLOPs of the three GEMMs / step time). `roofline` covers the
-kernel that takes the most time per step, timed with HIP events on the
-stream it runs on. `cpu_baseline` times the CPU oracle on the same workload.
+Each step is one HIP graph (captured once per buffer set) so the timed
+region measures the GPU, not Python launch overhead. `value` is fwd+bwd
+TFLOP/s of the whole step (algorithmic FLOPs of the three GEMMs / step
+time). Every entry point is also timed on its own (a graph of repeated
+calls on rotating buffer sets, HIP events on the stream the kernels run
+on); `roofline` covers the entry point that takes the most time per step,
+with its algorithmic bytes or FLOPs per call. `cpu_baseline` times the CPU
+oracle on a bounded sample of the same workload.
+
+Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -27,8 +33,19 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "fp6fp4": 10100.0}  # dense, MI355X public spec
+# dense MFMA peaks of MI355X (TFLOP/s); mixed 6/4-bit x 8-bit products run at the 8-bit rate
+MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "fp6fp4": 10100.0}
 CSRC = os.path.join(ROOT, "microscaling_quantized_convolution_mxq_amd", "csrc")
+CALLS = ["quantize_x", "quantize_w", "quantize_dy", "cbf_im2col", "forward", "backward_data", "backward_weight"]
+# kernels each entry point launches (see the launchers in csrc/)
+CALL_KERNELS = {
+    "quantize_x": ["mxq_quantize_kernel"], "quantize_w": ["mxq_quantize_kernel"],
+    "quantize_dy": ["mxq_quantize_kernel"], "cbf_im2col": ["cbf_im2col_kernel"],
+    "forward": ["mx_gemm_kernel<FwdProb>"],
+    "backward_data": ["transpose_codes_kernel (W)", "mx_gemm_kernel<DgradProb>"],
+    "backward_weight": ["transpose_codes_kernel (dY)", "transpose_codes_kernel (X)",
+                        "mx_gemm_kernel<WgradProb>", "splitk_reduce_kernel (when split)"],
+}
 
 
 def source_sha() -> str:
@@ -42,12 +59,13 @@ def source_sha() -> str:
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c2")
     ap.add_argument("--rotate-mb", type=float, default=640.0, help="minimum live set across rotated buffers")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-naive", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="launch the step call by call instead of as a graph")
     return ap.parse_args()
 
 
@@ -93,8 +111,6 @@ def main():
     R = int(min(8, max(2, np.ceil(args.rotate_mb * 1e6 / set_bytes))))
     sets = [first] + [make_set() for _ in range(R - 1)]
 
-    calls = ["quantize_x", "quantize_w", "quantize_dy", "cbf_im2col", "forward", "backward_data", "backward_weight"]
-
     def run(d, name):
         if name == "quantize_x":
             mq.mqconv_quantize(d["x"], d["xq"])
@@ -111,53 +127,96 @@ def main():
         elif name == "backward_weight":
             mq.mqconv_backward_weight(s, d["gq"], d["xq"], d["dw"], d["ws2"])
 
-    stream = torch.cuda.current_stream()
-    for i in range(args.warmup):
-        for c in calls:
-            run(sets[i % R], c)
+    def step(d):
+        for c in CALLS:
+            run(d, c)
+
+    stream = torch.cuda.Stream()  # kernels, graphs and events all live on this stream
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for d in sets:  # eager warm-up of every set
+            step(d)
     torch.cuda.synchronize()
 
-    # ---- timed region: events around every call, on the kernels' stream ----
-    K = args.steps
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
-          for _ in range(K)]
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(g, stream=stream):
+                fn()
+        torch.cuda.synchronize()
+        return g
+
+    step_graphs = None if args.eager else [capture(lambda d=d: step(d)) for d in sets]
+
+    def launch_step(i):
+        if step_graphs is None:
+            step(sets[i % R])
+        else:
+            step_graphs[i % R].replay()
+
+    # ---- warm-up, then exactly K timed steps -----------------------------------
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            launch_step(i)
     torch.cuda.synchronize()
+    K = args.steps
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
-    t_start.record(stream)
-    for i in range(K):
-        d = sets[i % R]
-        for j, c in enumerate(calls):
-            ev[i][j][0].record(stream)
-            run(d, c)
-            ev[i][j][1].record(stream)
-    t_end.record(stream)
+    with torch.cuda.stream(stream):
+        t_start.record(stream)
+        for i in range(K):
+            launch_step(i)
+        t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = t_start.elapsed_time(t_end) / K
-    per_call = {c: float(np.mean([ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(K)])) for j, c in enumerate(calls)}
+
+    # ---- every entry point on its own: graph of REP calls over rotating sets ----
+    REP = 4 * R
+    per_call = {}
+    for c in CALLS:
+        g = capture(lambda c=c: [run(sets[i % R], c) for i in range(REP)])
+        with torch.cuda.stream(stream):
+            g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        nrep = 10
+        with torch.cuda.stream(stream):
+            a.record(stream)
+            for _ in range(nrep):
+                g.replay()
+            b.record(stream)
+        torch.cuda.synchronize()
+        per_call[c] = a.elapsed_time(b) / (nrep * REP)
+        del g
 
     # ---- algorithmic work -----------------------------------------------------
-    bits = {0: 8, 1: 8, 2: 6, 3: 6, 4: 4}
     flop = s.flops()
     nx, nw, ng = x.size, w.size, dy.size
     xq_b = mq.mqconv_codes_bytes(mq.ROLE_ACT, wl.fx, *x.shape) + mq.mqconv_scales_bytes(mq.ROLE_ACT, bp, *x.shape)
     wq_b = mq.mqconv_codes_bytes(mq.ROLE_WEIGHT, wl.fw, *w.shape) + mq.mqconv_scales_bytes(mq.ROLE_WEIGHT, bp, *w.shape)
     gq_b = mq.mqconv_codes_bytes(mq.ROLE_GRAD, wl.fdy, *dy.shape) + mq.mqconv_scales_bytes(mq.ROLE_GRAD, bp, *dy.shape)
     col_b = mq.mqconv_im2col_codes_bytes(s, wl.fx) + mq.mqconv_im2col_scales_bytes(s, bp)
+    # bytes each call must move at least once (inputs read, outputs written)
     alg_bytes = {
         "quantize_x": 4 * nx + xq_b, "quantize_w": 4 * nw + wq_b, "quantize_dy": 4 * ng + gq_b,
         "cbf_im2col": xq_b + col_b,
         "forward": xq_b + wq_b + 4 * ng, "backward_data": gq_b + wq_b + 4 * nx, "backward_weight": gq_b + xq_b + 4 * nw,
     }
     alg_flop = {"forward": flop, "backward_data": flop, "backward_weight": flop}
+
+    def mfma_peak(fa, fb):
+        return MFMA_PEAK_TFLOPS["fp6fp4"] if (fa >= 2 and fb >= 2) else MFMA_PEAK_TFLOPS["fp8"]
+
+    call_peak = {"forward": mfma_peak(wl.fx, wl.fw), "backward_data": mfma_peak(wl.fdy, wl.fw),
+                 "backward_weight": mfma_peak(wl.fdy, wl.fx)}
     kernels = {}
-    for c in calls:
+    for c in CALLS:
         t = per_call[c] * 1e-3
         k = {"ms": round(per_call[c], 5), "GB/s": round(alg_bytes[c] / t / 1e9, 1),
-             "hbm_frac": round(alg_bytes[c] / t / 1e9 / HBM_PEAK_GBS, 4)}
+             "hbm_frac": round(alg_bytes[c] / t / 1e9 / HBM_PEAK_GBS, 4), "launches": CALL_KERNELS[c]}
         if c in alg_flop:
-            peak = MFMA_PEAK_TFLOPS["fp8"]
+            peak = call_peak[c]
             ai = alg_flop[c] / alg_bytes[c]
             attainable = min(peak, ai * HBM_PEAK_GBS / 1e3)
             k.update({"TFLOP/s": round(alg_flop[c] / t / 1e12, 2), "mfma_frac": round(alg_flop[c] / t / 1e12 / peak, 4),
@@ -165,18 +224,20 @@ def main():
                       "attainable_frac": round(alg_flop[c] / t / 1e12 / attainable, 4)})
         kernels[c] = k
 
-    dominant = max(calls, key=lambda c: per_call[c])
+    dominant = max(CALLS, key=lambda c: per_call[c])
     t_dom = per_call[dominant] * 1e-3
-    if dominant in alg_flop and alg_flop[dominant] / alg_bytes[dominant] > 629:
+    if dominant in alg_flop and alg_flop[dominant] / alg_bytes[dominant] > call_peak[dominant] * 1e3 / HBM_PEAK_GBS:
         roof = {"bound": "mfma", "achieved": round(alg_flop[dominant] / t_dom / 1e12, 2),
-                "peak": MFMA_PEAK_TFLOPS["fp8"], "unit": "TFLOP/s"}
+                "peak": call_peak[dominant], "unit": "TFLOP/s"}
     else:
         roof = {"bound": "hbm", "achieved": round(alg_bytes[dominant] / t_dom / 1e9, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["kernel"] = dominant
     roof["traffic"] = None
-    tf = os.path.join(ROOT, "profiles", f"traffic_{args.workload}_{dominant}.json")
+    roof["kernel"] = dominant
+    roof["launches"] = CALL_KERNELS[dominant]
+    roof["ms_per_call"] = round(per_call[dominant], 5)
+    tf = os.path.join(ROOT, "profiles", f"traffic_{wl.name}_{dominant}.json")
     if os.path.exists(tf):
         rec = json.load(open(tf))
         if rec.get("source_sha") == source_sha():
@@ -192,23 +253,26 @@ def main():
         d = sets[0]
         wsn = [torch.empty(max(1, mq.mqconv_naive_workspace_bytes(s, op, a, b)), dtype=torch.uint8, device="cuda")
                for op, a, b in ((0, wl.fx, wl.fw), (1, wl.fdy, wl.fw), (2, wl.fdy, wl.fx))]
+
         def naive_step():
             mq.mqconv_naive_forward(s, d["x"], d["w"], wl.fx, wl.fw, d["y"], wsn[0])
             mq.mqconv_naive_backward_data(s, d["dy"], d["w"], wl.fdy, wl.fw, d["dx"], wsn[1])
             mq.mqconv_naive_backward_weight(s, d["dy"], d["x"], wl.fdy, wl.fx, d["dw"], wsn[2])
-        for _ in range(3):
-            naive_step()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        nrep = 10
-        for _ in range(nrep):
-            naive_step()
-        b.record(stream)
+
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                naive_step()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            nrep = 10
+            for _ in range(nrep):
+                naive_step()
+            b.record(stream)
         torch.cuda.synchronize()
-        naive = {"ms_per_step": round(a.elapsed_time(b) / nrep, 4)}
+        naive = {"ms_per_step": round(a.elapsed_time(b) / nrep, 4), "launch": "eager"}
         del wsn
 
-    # ---- CPU baseline: the oracle on the same workload ----------------------
+    # ---- CPU baseline: the oracle on a bounded sample of the same workload ----
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -218,8 +282,8 @@ def main():
         tc = time.perf_counter() - t0
         cpu = {"value": round(3 * flop / tc / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.threads(),
                "kind": "oracle", "ms_per_step": round(tc * 1e3, 1),
-               "sample": f"the full {wl.name} step (quantize X, W, dY; CBF im2col of the codes; fp64 direct "
-                         "fwd, dgrad and wgrad on the dequantized operands), once"}
+               "sample": f"one full {wl.name} step (quantize X, W, dY; CBF im2col of the codes; fp64 direct "
+                         "fwd, dgrad and wgrad on the dequantized operands)"}
 
     value = 3 * flop / (ms_step * 1e-3) / 1e12
     out = {
@@ -230,7 +294,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "n": s.n, "cin": s.cin, "cout": s.cout, "h": s.h, "w": s.w,
                    "kernel": f"{s.kh}x{s.kw}", "stride": s.stride, "pad": s.pad, "block": f"32 ch x {bp} batch",
-                   "rotated_sets": R},
+                   "rotated_sets": R, "launch": "eager" if args.eager else "hip_graph"},
         "roofline": roof,
         "cpu_baseline": cpu,
         "quantize_im2col_GB/s": round(q_im_bytes / (q_im_ms * 1e-3) / 1e9, 1),
