@@ -1,0 +1,175 @@
+"""HBM traffic of the quantize-once path and of the naive path, from rocprofv3
+counters.
+
+Three modes:
+  step       run one training step of a workload (every layer for the YOLOv8n
+             backbone) through one path, so that rocprofv3 --pmc can count it
+  copy       run a plain device-to-device copy of known size (calibration)
+  summarize  read the counter CSVs of those runs and write a summary
+
+Counter passes (one counter group per run, as rocprofv3 requires), e.g. for
+the 3x3 YOLOv8n-style layer:
+  rocprofv3 --pmc FETCH_SIZE -d D -o mq_fetch -- python -m microscaling_quantized_convolution_mxq_amd.traffic step --workload c2 --path microqonv
+  rocprofv3 --pmc WRITE_SIZE -d D -o mq_write -- ... --path microqonv
+  (the same with --path naive -> naive_fetch / naive_write, and copy -> copy_fetch / copy_write)
+  python -m microscaling_quantized_convolution_mxq_amd.traffic summarize --dir D --workload c2
+
+FETCH_SIZE and WRITE_SIZE are KiB per dispatch. Each is divided by what the
+same counter reads per byte of the copy, so the result is in bytes of the
+copy's own accounting.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "microscaling_quantized_convolution_mxq_amd", "csrc")
+COPY_MB = 512
+
+
+def _workloads(name):
+    from microscaling_quantized_convolution_mxq_amd.workloads import WORKLOADS, C3_LAYERS, c3_workload
+    if name == "c3":
+        return [c3_workload(i) for i in range(len(C3_LAYERS))]
+    return [WORKLOADS[name]]
+
+
+def run_step(workload: str, path: str) -> None:
+    import torch
+    import microscaling_quantized_convolution_mxq_amd as mq
+    from microscaling_quantized_convolution_mxq_amd.workloads import draw_inputs
+
+    for wl in _workloads(workload):
+        s = wl.shape
+        x, w, dy = draw_inputs(wl)
+        X, Wt, DY = (torch.from_numpy(a).cuda() for a in (x, w, dy))
+        y = torch.empty((s.ho, s.wo, s.n, s.cout), device="cuda")
+        dx = torch.empty(x.shape, device="cuda")
+        dw = torch.empty(w.shape, device="cuda")
+        if path == "microqonv":
+            xq = mq.MxTensor.empty(mq.ROLE_ACT, wl.fx, wl.bp, x.shape)
+            wq = mq.MxTensor.empty(mq.ROLE_WEIGHT, wl.fw, wl.bp, w.shape)
+            gq = mq.MxTensor.empty(mq.ROLE_GRAD, wl.fdy, wl.bp, dy.shape)
+            ws1 = torch.empty(max(1, mq.mqconv_workspace_bytes(s, 1, wl.fdy, wl.fw)), dtype=torch.uint8, device="cuda")
+            ws2 = torch.empty(max(1, mq.mqconv_workspace_bytes(s, 2, wl.fdy, wl.fx)), dtype=torch.uint8, device="cuda")
+            torch.cuda.synchronize()
+            mq.mqconv_quantize(X, xq)
+            mq.mqconv_quantize(Wt, wq)
+            mq.mqconv_quantize(DY, gq)
+            mq.mqconv_forward(s, xq, wq, y)
+            mq.mqconv_backward_data(s, gq, wq, dx, ws1)
+            mq.mqconv_backward_weight(s, gq, xq, dw, ws2)
+        else:
+            ws = [torch.empty(max(1, mq.mqconv_naive_workspace_bytes(s, op, a, b)), dtype=torch.uint8, device="cuda")
+                  for op, a, b in ((0, wl.fx, wl.fw), (1, wl.fdy, wl.fw), (2, wl.fdy, wl.fx))]
+            torch.cuda.synchronize()
+            mq.mqconv_naive_forward(s, X, Wt, wl.fx, wl.fw, y, ws[0])
+            mq.mqconv_naive_backward_data(s, DY, Wt, wl.fdy, wl.fw, dx, ws[1])
+            mq.mqconv_naive_backward_weight(s, DY, X, wl.fdy, wl.fx, dw, ws[2])
+        torch.cuda.synchronize()
+        print(f"step {path} {wl.name}", flush=True)
+
+
+def run_copy() -> None:
+    import torch
+    n = COPY_MB * (1 << 20) // 4
+    a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    print(f"copy {COPY_MB} MiB", flush=True)
+
+
+def _read(d: str, stem: str, counter: str):
+    """Per-dispatch (kernel name, value in bytes) of one counter run."""
+    files = glob.glob(os.path.join(d, "**", f"{stem}_counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no {stem}_counter_collection.csv under {d}")
+    out = []
+    for r in csv.DictReader(open(files[0])):
+        if r["Counter_Name"] != counter:
+            continue
+        out.append((r["Kernel_Name"], float(r["Counter_Value"]) * 1024.0))
+    return out
+
+
+def _source_sha() -> str:
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def summarize(d: str, workload: str, out_dir: str) -> dict:
+    copy_bytes = COPY_MB * (1 << 20)
+    cf = [v for k, v in _read(d, "copy_fetch", "FETCH_SIZE") if "mq::" not in k]
+    cw = [v for k, v in _read(d, "copy_write", "WRITE_SIZE") if "mq::" not in k]
+    # the copy is the largest dispatch of its run (the fill before it writes only)
+    f_fetch = max(cf) / copy_bytes
+    f_write = max(cw) / copy_bytes
+    res = {"workload": workload, "copy_MiB": COPY_MB, "fetch_factor": round(f_fetch, 4),
+           "write_factor": round(f_write, 4), "source_sha": _source_sha(), "paths": {}}
+    lines = []
+    for path, stem in (("microqonv", "mq"), ("naive", "naive")):
+        fe = [(k, v / f_fetch) for k, v in _read(d, f"{stem}_fetch", "FETCH_SIZE") if "mq::" in k]
+        wr = [(k, v / f_write) for k, v in _read(d, f"{stem}_write", "WRITE_SIZE") if "mq::" in k]
+        per_kernel = {}
+        for k, v in fe:
+            key = k.split("(")[0].replace("void ", "")
+            per_kernel.setdefault(key, [0.0, 0.0, 0])
+            per_kernel[key][0] += v
+            per_kernel[key][2] += 1
+        for k, v in wr:
+            key = k.split("(")[0].replace("void ", "")
+            per_kernel.setdefault(key, [0.0, 0.0, 0])
+            per_kernel[key][1] += v
+        tot_f, tot_w = sum(v for _, v in fe), sum(v for _, v in wr)
+        res["paths"][path] = {"fetch_bytes": tot_f, "write_bytes": tot_w, "total_bytes": tot_f + tot_w,
+                              "dispatches": len(fe),
+                              "kernels": {k: {"fetch": v[0], "write": v[1], "dispatches": v[2]}
+                                          for k, v in per_kernel.items()}}
+        lines.append(f"{path}: {len(fe)} dispatches, read {tot_f / 1e6:.1f} MB, write {tot_w / 1e6:.1f} MB, "
+                     f"total {(tot_f + tot_w) / 1e6:.1f} MB")
+        for k, v in sorted(per_kernel.items(), key=lambda kv: -(kv[1][0] + kv[1][1])):
+            lines.append(f"    {k[:70]:70s} x{v[2]:3d}  read {v[0] / 1e6:9.2f} MB  write {v[1] / 1e6:9.2f} MB")
+    m, n = res["paths"]["microqonv"]["total_bytes"], res["paths"]["naive"]["total_bytes"]
+    res["naive_over_microqonv"] = round(n / m, 3)
+    lines.append(f"naive / quantize-once bytes: x{n / m:.2f}")
+    text = "\n".join(lines)
+    os.makedirs(out_dir, exist_ok=True)
+    with open(os.path.join(out_dir, f"bytes_{workload}.json"), "w") as fh:
+        json.dump(res, fh, indent=1)
+    print(text)
+    return res
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="mode", required=True)
+    a = sub.add_parser("step")
+    a.add_argument("--workload", default="c2")
+    a.add_argument("--path", choices=("microqonv", "naive"), default="microqonv")
+    sub.add_parser("copy")
+    c = sub.add_parser("summarize")
+    c.add_argument("--dir", required=True)
+    c.add_argument("--workload", default="c2")
+    c.add_argument("--out", default=os.path.join(ROOT, "gpurun_out"))
+    args = ap.parse_args(argv)
+    if args.mode == "step":
+        run_step(args.workload, args.path)
+    elif args.mode == "copy":
+        run_copy()
+    else:
+        summarize(args.dir, args.workload, args.out)
+
+
+if __name__ == "__main__":
+    main()
