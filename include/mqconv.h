@@ -132,7 +132,8 @@ typedef enum { MQ_E4M3 = 0, MQ_E5M2 = 1, MQ_E2M3 = 2, MQ_E3M2 = 3, MQ_E2M1 = 4 }
 typedef enum { MQ_ROLE_ACT = 0, MQ_ROLE_WEIGHT = 1, MQ_ROLE_GRAD = 2 } mq_role;
 
 /* Convolution geometry (host struct). All fields >= 1 except pads (>= 0).
- * Supported: kh, kw <= 7; pad < kernel size; Ho, Wo >= 1. */
+ * Supported: kh, kw <= 15; stride <= 8; pad < kernel size; Ho, Wo >= 1;
+ * every packed tensor and im2col output below 2^30 elements. */
 typedef struct {
   int32_t n, cin, h, w, cout, kh, kw, stride_h, stride_w, pad_h, pad_w;
 } mq_conv;
