@@ -13,51 +13,75 @@
 #include "mx_common.h"
 #include "mqconv_internal.h"
 
+#include <algorithm>
+
 namespace mq {
 
 // ----------------------------------------------------------------------------
-// CBF im2col. Codes: one thread per CH-byte chunk of output (CH = 16 when rows
-// are 16-byte multiples, else 8). Scales: one thread per output scale byte,
-// in the trailing blocks of the same grid.
+// CBF im2col. One workgroup per output pixel o = (ho, wo): its output is one
+// contiguous stretch of N * T * row_bytes code bytes ([n][kh][kw][row]) and
+// T * nsb scale bytes ([kh][kw][nsb]), written with consecutive 16-byte
+// (8-byte when rows are not 16-byte multiples) stores; every chunk copies the
+// matching chunk of the source row (n at pixel (ho*s+kh-p, wo*s+kw-p)) or
+// zeros outside the image. Divisions by the launch's runtime extents use
+// precomputed multiply-shift reciprocals.
 // ----------------------------------------------------------------------------
+// x / d for 0 <= x < 2^31 as (x * m) >> (32 + s), m = ceil(2^(31+l) / d),
+// l = ceil(log2 d), s = l - 1: m * d exceeds 2^(31+l) by less than d <= 2^l,
+// so the error stays below 1/d and the floor is exact; m < 2^32.
+struct FastDiv {
+  unsigned m, s, d;
+};
+inline FastDiv make_fastdiv(unsigned d) {
+  FastDiv f; f.d = d;
+  if (d == 1) { f.m = 0; f.s = 0; return f; }
+  unsigned l = 0;
+  while ((1ull << l) < d) l++;
+  f.m = (unsigned)(((1ull << (31 + l)) + d - 1) / d);
+  f.s = l - 1;
+  return f;
+}
+__device__ __forceinline__ unsigned fdiv(unsigned x, const FastDiv& f) {
+  return f.d == 1 ? x : (__umulhi(x, f.m) >> f.s);
+}
+
 template <int CH>
 __global__ __launch_bounds__(256) void cbf_im2col_kernel(
     const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xs, uint8_t* __restrict__ oc,
-    uint8_t* __restrict__ os, int N, int H, int W, int KH, int KW, int sh, int sw, int ph, int pw,
-    int Wo, int cpr /*chunks per row*/, long long nchunks, int nsb /*scale bytes per pixel*/,
-    long long nscales, long long code_blocks) {
-  if ((long long)blockIdx.x < code_blocks) {
-    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= nchunks) return;
-    const int T = KH * KW;
-    const int ch = (int)(idx % cpr);
-    const long long row = idx / cpr;  // ((o*N + n)*T + t)
-    const int t = (int)(row % T);
-    const long long on = row / T;
-    const int n = (int)(on % N);
-    const int o = (int)(on / N);
-    const int ho = o / Wo, wo = o - ho * Wo;
-    const int kh = t / KW, kw = t - kh * KW;
-    const int hi = ho * sh + kh - ph, wi = wo * sw + kw - pw;
-    typedef typename std::conditional<CH == 16, uint4, uint2>::type V;
+    uint8_t* __restrict__ os, int N, int H, int W, int sh, int sw, int ph, int pw, int T, int cpr,
+    int nsb, FastDiv div_tc /* T*cpr */, FastDiv div_c /* cpr */, FastDiv div_kw /* KW */,
+    FastDiv div_nsb /* nsb */, FastDiv div_wo /* Wo */) {
+  typedef typename std::conditional<CH == 16, uint4, uint2>::type V;
+  const unsigned o = blockIdx.x;
+  const unsigned ho = fdiv(o, div_wo), wo = o - ho * div_wo.d;
+  const int hb = (int)ho * sh - ph, wb = (int)wo * sw - pw;
+  const unsigned per_n = T * cpr;
+  const unsigned nch = N * per_n;
+  const V* src = reinterpret_cast<const V*>(xc);
+  V* dst = reinterpret_cast<V*>(oc) + (unsigned long long)o * nch;
+  // blockIdx.y splits a pixel's chunks when there are few pixels
+  const unsigned per = (nch + gridDim.y - 1) / gridDim.y;
+  const unsigned c_lo = blockIdx.y * per, c_hi = min(nch, c_lo + per);
+  for (unsigned c = c_lo + threadIdx.x; c < c_hi; c += 256) {
+    const unsigned n = fdiv(c, div_tc);
+    const unsigned r = c - n * per_n;
+    const unsigned t = fdiv(r, div_c);
+    const unsigned ch = r - t * cpr;
+    const unsigned kh = fdiv(t, div_kw), kw = t - kh * div_kw.d;
+    const int hi = hb + (int)kh, wi = wb + (int)kw;
     V v = {};
-    if (hi >= 0 && hi < H && wi >= 0 && wi < W)
-      v = reinterpret_cast<const V*>(xc)[((long long)(hi * W + wi) * N + n) * cpr + ch];
-    reinterpret_cast<V*>(oc)[idx] = v;
-  } else {
-    const long long idx = ((long long)blockIdx.x - code_blocks) * 256 + threadIdx.x;
-    if (idx >= nscales) return;
-    const int T = KH * KW;
-    const int k = (int)(idx % nsb);
-    const long long ot = idx / nsb;  // o*T + t
-    const int t = (int)(ot % T);
-    const int o = (int)(ot / T);
-    const int ho = o / Wo, wo = o - ho * Wo;
-    const int kh = t / KW, kw = t - kh * KW;
-    const int hi = ho * sh + kh - ph, wi = wo * sw + kw - pw;
-    uint8_t s = 0;
-    if (hi >= 0 && hi < H && wi >= 0 && wi < W) s = xs[(long long)(hi * W + wi) * nsb + k];
-    os[idx] = s;
+    if ((unsigned)hi < (unsigned)H && (unsigned)wi < (unsigned)W)
+      v = src[((unsigned long long)(hi * W + wi) * N + n) * cpr + ch];
+    dst[c] = v;
+  }
+  const unsigned ns = T * nsb;
+  for (unsigned c = threadIdx.x; blockIdx.y == 0 && c < ns; c += 256) {
+    const unsigned t = fdiv(c, div_nsb), k = c - t * nsb;
+    const unsigned kh = fdiv(t, div_kw), kw = t - kh * div_kw.d;
+    const int hi = hb + (int)kh, wi = wb + (int)kw;
+    uint8_t v = 0;
+    if ((unsigned)hi < (unsigned)H && (unsigned)wi < (unsigned)W) v = xs[(unsigned long long)(hi * W + wi) * nsb + k];
+    os[(unsigned long long)o * ns + c] = v;
   }
 }
 
@@ -66,19 +90,26 @@ hipError_t launch_cbf_im2col(const Conv& cv, MxView x, uint8_t* col_codes, uint8
   const long long rb = row_bytes(x.fmt, cv.cin);
   const int CH = (rb % 16 == 0) ? 16 : 8;
   const int cpr = (int)(rb / CH);
-  const long long Ho = cv.ho(), Wo = cv.wo(), T = (long long)cv.kh * cv.kw;
-  const long long nchunks = Ho * Wo * cv.n * T * cpr;
+  const int Ho = cv.ho(), Wo = cv.wo(), T = cv.kh * cv.kw;
   const int nsb = ceil_div(cv.n, x.bp) * ceil_div(cv.cin, 32);
-  const long long nscales = Ho * Wo * T * nsb;
-  const long long cblocks = (nchunks + 255) / 256, sblocks = (nscales + 255) / 256;
+  // per-pixel chunk indices stay below 2^31 (tensor sizes are capped at 2^30 elements)
+  const FastDiv dtc = make_fastdiv((unsigned)(T * cpr)), dc = make_fastdiv((unsigned)cpr),
+                dkw = make_fastdiv((unsigned)cv.kw), dnsb = make_fastdiv((unsigned)nsb),
+                dwo = make_fastdiv((unsigned)Wo);
+  const unsigned blocks = (unsigned)Ho * (unsigned)Wo;
+  // at least ~2048 workgroups, but no split below 1024 chunks per workgroup
+  const unsigned nch = (unsigned)cv.n * T * cpr;
+  unsigned split = blocks >= 2048 ? 1u : (2048u + blocks - 1) / blocks;
+  split = std::max(1u, std::min(split, nch / 1024u));
+  const dim3 grid(blocks, split);
   if (CH == 16)
-    hipLaunchKernelGGL(cbf_im2col_kernel<16>, dim3((unsigned)(cblocks + sblocks)), dim3(256), 0, st,
-                       x.codes, x.scales, col_codes, col_scales, cv.n, cv.h, cv.w, cv.kh, cv.kw,
-                       cv.sh, cv.sw, cv.ph, cv.pw, (int)Wo, cpr, nchunks, nsb, nscales, cblocks);
+    hipLaunchKernelGGL(cbf_im2col_kernel<16>, grid, dim3(256), 0, st, x.codes, x.scales, col_codes,
+                       col_scales, cv.n, cv.h, cv.w, cv.sh, cv.sw, cv.ph, cv.pw, T, cpr, nsb, dtc, dc, dkw,
+                       dnsb, dwo);
   else
-    hipLaunchKernelGGL(cbf_im2col_kernel<8>, dim3((unsigned)(cblocks + sblocks)), dim3(256), 0, st,
-                       x.codes, x.scales, col_codes, col_scales, cv.n, cv.h, cv.w, cv.kh, cv.kw,
-                       cv.sh, cv.sw, cv.ph, cv.pw, (int)Wo, cpr, nchunks, nsb, nscales, cblocks);
+    hipLaunchKernelGGL(cbf_im2col_kernel<8>, grid, dim3(256), 0, st, x.codes, x.scales, col_codes,
+                       col_scales, cv.n, cv.h, cv.w, cv.sh, cv.sw, cv.ph, cv.pw, T, cpr, nsb, dtc, dc, dkw,
+                       dnsb, dwo);
   return hipGetLastError();
 }
 
@@ -164,8 +195,72 @@ __global__ __launch_bounds__(256) void transpose_codes_kernel(const uint8_t* __r
   }
 }
 
+// 8-bit codes: one wave per tile of 32 partner rows x 64 channels. The wave
+// stages the tile in LDS (row pitch 72 bytes: the transposing reads of 8 rows
+// then hit distinct banks) and reads it back with ds_read_b64_tr_b8: in each
+// group of 16 lanes, lanes 2i and 2i+1 address the two 8-byte halves of row
+// r0+i, and lane t receives rows r0..r0+7 of column t of the group. Four such
+// reads give every lane the 32 partner codes of one channel: one output run,
+// stored as 32 contiguous bytes (consecutive lanes, consecutive channels).
+__global__ __launch_bounds__(256) void transpose_codes8_kernel(const uint8_t* __restrict__ in,
+                                                              uint8_t* __restrict__ out, int P, int B,
+                                                              int C, int nPB, int nCC, long long ntiles) {
+  constexpr int PITCH = 72;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[4][32 * PITCH];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const long long tile = (long long)blockIdx.x * 4 + wave;
+  if (tile >= ntiles) return;  // whole wave (no workgroup barrier below)
+  const int cc = (int)(tile % nCC);
+  const long long rest = tile / nCC;
+  const int pb = (int)(rest % nPB);
+  const long long ab = rest / nPB;
+  const long long a = ab / B;
+  const int b = (int)(ab % B);
+  const int nCB = (C + 31) / 32;
+  const long long rb = (long long)nCB * 32;
+  const int c0 = cc * 64;
+  uint8_t* t = lds[wave];
+  {  // load: lane -> row lane/2, 32 bytes at column c0 + 32*(lane%2)
+    const int r = lane >> 1, hc = (lane & 1) * 32;
+    const int p = pb * 32 + r;
+    uint4 v0 = make_uint4(0, 0, 0, 0), v1 = v0;
+    if (p < P && c0 + hc < rb) {
+      const uint4* src = reinterpret_cast<const uint4*>(in + ((a * P + p) * B + b) * rb + c0 + hc);
+      v0 = src[0];
+      v1 = src[1];
+    }
+    uint2* d = reinterpret_cast<uint2*>(t + r * PITCH + hc);
+    d[0] = make_uint2(v0.x, v0.y); d[1] = make_uint2(v0.z, v0.w);
+    d[2] = make_uint2(v1.x, v1.y); d[3] = make_uint2(v1.z, v1.w);
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's tile is in LDS
+  __builtin_amdgcn_wave_barrier();
+  typedef v2i __attribute__((address_space(3)))* lds_v2i_ptr;
+  const int g = lane >> 4, j = lane & 15;
+  uint32_t run[8];
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    const int row = 8 * q + (j >> 1), col = 16 * g + 8 * (j & 1);
+    const v2i r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_ptr)(t + row * PITCH + col));
+    run[2 * q] = r.x; run[2 * q + 1] = r.y;
+  }
+  const int c = c0 + lane;
+  if (c < C) {
+    uint4* dst = reinterpret_cast<uint4*>(out + ((ab * C + c) * nPB + pb) * 32);
+    dst[0] = make_uint4(run[0], run[1], run[2], run[3]);
+    dst[1] = make_uint4(run[4], run[5], run[6], run[7]);
+  }
+}
+
 hipError_t launch_transpose_codes(const uint8_t* in, uint8_t* out, int fmt, int A, int P, int B,
                                   int C, hipStream_t st) {
+  if (fmt <= 1) {  // 8-bit codes
+    const int nPB = ceil_div(P, 32), nCC = ceil_div(ceil_div(C, 32) * 32, 64);
+    const long long ntiles = (long long)A * B * nPB * nCC;
+    hipLaunchKernelGGL(transpose_codes8_kernel, dim3((unsigned)((ntiles + 3) / 4)), dim3(256), 0, st, in, out,
+                       P, B, C, nPB, nCC, ntiles);
+    return hipGetLastError();
+  }
   const int nPB = ceil_div(P, 32);
   const long long blocks = (long long)A * B * nPB;
   switch (fmt) {
