@@ -23,6 +23,9 @@ hipError_t launch_backward_data(const Conv& cv, MxView dy, MxView w, float* dx, 
   const long long dmax = (long long)(ceil_div(cv.kh, cv.sh) - 1) * p.Wo + (ceil_div(cv.kw, cv.sw) - 1);
   p.dycb = (int)(dmax * cv.n * p.dyrb); p.dysb = (int)(dmax * p.dynPB * p.ncob);
   if (!offsets_fit(p.dyc_bytes, p.dycb) || !offsets_fit(p.dys_bytes, p.dysb)) return hipErrorInvalidValue;
+  // rows of A are (pixel, n); rows of B are Cin, 32 to a block
+  p.ga = scale_group_rows(dy.bp, cv.n);
+  p.gb = 32;
   const int maxHc = ceil_div(cv.h, cv.sh), maxWc = ceil_div(cv.w, cv.sw);
   return launch_tiled(dy.fmt, w.fmt, p, maxHc * maxWc * cv.n, cv.cin, cv.sh * cv.sw, st);
 }

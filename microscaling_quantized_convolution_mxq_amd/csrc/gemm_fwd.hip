@@ -19,6 +19,9 @@ hipError_t launch_forward(const Conv& cv, MxView x, MxView w, float* y, void*, s
   const long long lead = (long long)cv.ph * cv.w + cv.pw;
   p.xcb = (int)(lead * cv.n * p.xrb); p.xsb = (int)(lead * p.xnPB * p.ncb);
   if (!offsets_fit(p.xc_bytes, p.xcb) || !offsets_fit(p.xs_bytes, p.xsb)) return hipErrorInvalidValue;
+  // rows of A are (pixel, n): a block is 32 (or all N < 32) of them; rows of B are Cout
+  p.ga = scale_group_rows(x.bp, cv.n);
+  p.gb = w.bp == 32 ? 32 : 0;
   return launch_tiled(x.fmt, w.fmt, p, p.M, cv.cout, 1, st);
 }
 

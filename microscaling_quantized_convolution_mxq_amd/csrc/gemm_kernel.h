@@ -63,7 +63,8 @@ struct FwdProb {
   int xrb, xRB, xbp, xnPB, ncb, npair;  // activation row bytes, run bytes, bp, partner blocks, channel blocks, pairs
   int wrb, wRB, wnCoB, wbp;              // weight row bytes, run bytes, Cout blocks, bp
   int xcb, xsb;                          // bias of the activation row offsets (padding)
-  static constexpr bool kGeoA = true, kGeoB = false;
+  int ga, gb;                            // rows sharing one scale (A, B); 0: per-row scales
+  static constexpr bool kGeoA = true, kGeoB = false, kCanGroup = true;
   struct Ctx {};
   struct KS {
     int kh, kw, v;
@@ -130,7 +131,8 @@ struct DgradProb {
   int dyrb, dyRB, dybp, dynPB, ncob, npair;  // gradient row bytes, run bytes, bp, partner blocks, Cout blocks, pairs
   int wRB, ncbi;                             // weight run bytes, Cin blocks
   int dycb, dysb;                            // bias of the step offsets (backward taps)
-  static constexpr bool kGeoA = true, kGeoB = false;
+  int ga, gb;                                // rows sharing one scale (A, B); 0: per-row scales
+  static constexpr bool kGeoA = true, kGeoB = false, kCanGroup = true;
   struct Ctx { int ph_c, pw_c, Hc, Wc, kh0, kw0, nkh, nkw, M; };
   struct KS {
     int ih, iw, v;
@@ -215,7 +217,8 @@ struct WgradProb {
   int nsub;            // pairs per pixel (pair_w 0) or per output row (pair_w 1)
   int total_steps, steps_per_split;
   int xtcb, xsb;       // bias of the activation row offsets (padding)
-  static constexpr bool kGeoA = false, kGeoB = true;
+  int ga, gb;          // rows sharing one scale (A, B); 0: per-row scales
+  static constexpr bool kGeoA = false, kGeoB = true, kCanGroup = true;
   struct Ctx {};
   struct KS {
     int ho, wo, v;
@@ -292,7 +295,8 @@ struct PlainProb {
   float* out;
   long long ac_bytes, as_bytes, bc_bytes, bs_bytes;
   int Ma, Nb, nkb, aRB, bRB, pairs_per_split, arb, brb;
-  static constexpr bool kGeoA = false, kGeoB = false;
+  int ga = 0, gb = 0;
+  static constexpr bool kGeoA = false, kGeoB = false, kCanGroup = false;
   struct Ctx {};
   struct KS {
     int u;
@@ -428,18 +432,27 @@ __device__ __forceinline__ void stage_barrier() {
 }
 
 // WM x WN waves; each wave owns TM x TN MFMA tiles of 32 x 32; NS LDS stages.
-template <int FA, int FB, class P, int WM, int WN, int TM, int TN, int NS>
+// GS: grouped scales. When every run of prob.ga rows of A (prob.gb of B)
+// shares one scale (a 32 x 32 block, or a whole pixel's N < 32 rows), a stage
+// holds one scale per (K-block, group) instead of per (K-block, row), and
+// one 64-lane load per operand fetches them: wave 0 the A scales, wave 1 the
+// B scales; waves 2 and 3 issue a zero-reading load to keep every wave's
+// load count equal.
+template <int FA, int FB, class P, int WM, int WN, int TM, int TN, int NS, bool GS>
 __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
   using OA = Op<FA>;
   using OB = Op<FB>;
   constexpr int A_BYTES = 2 * BM * OA::NPK * 16, B_BYTES = 2 * BN * OB::NPK * 16;
-  constexpr int OFF_B = A_BYTES, OFF_SA = OFF_B + B_BYTES, OFF_SB = OFF_SA + 8 * BM;
-  constexpr int STAGE = OFF_SB + 8 * BN;
+  constexpr int SA_BYTES = GS ? 256 : 8 * BM, SB_BYTES = GS ? 256 : 8 * BN;
+  constexpr int OFF_B = A_BYTES, OFF_SA = OFF_B + B_BYTES, OFF_SB = OFF_SA + SA_BYTES;
+  constexpr int STAGE = OFF_SB + SB_BYTES;
   // LDS-writing loads (64 lanes each) per stage and per wave; load g of a
   // kind belongs to K-block g / (loads per K-block)
-  constexpr int NCA = 2 * BM * OA::NPK / 64, NCB = 2 * BN * OB::NPK / 64, NSA = 2 * BM / 64, NSB = 2 * BN / 64;
-  constexpr int WCA = (NCA + 3) / 4, WCB = (NCB + 3) / 4, WSA = (NSA + 3) / 4, WSB = (NSB + 3) / 4;
+  constexpr int NCA = 2 * BM * OA::NPK / 64, NCB = 2 * BN * OB::NPK / 64;
+  constexpr int NSA = GS ? 1 : 2 * BM / 64, NSB = GS ? 1 : 2 * BN / 64;
+  constexpr int WCA = (NCA + 3) / 4, WCB = (NCB + 3) / 4;
+  constexpr int WSA = GS ? 1 : (NSA + 3) / 4, WSB = GS ? 0 : (NSB + 3) / 4;
   constexpr int WPS = WCA + WCB + WSA + WSB;
   // 1 KB sink for the loads a wave issues only to keep its count uniform
   constexpr int DUMMY = NS * STAGE;
@@ -477,7 +490,7 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
 
   // Per-lane load descriptors. `inner` collects whether all of this wave's
   // rows stay inside the borders for every step of the problem.
-  LaneLd ca[WCA], cb[WCB], sa[WSA], sb[WSB];
+  LaneLd ca[WCA], cb[WCB], sa[WSA], sb[WSB > 0 ? WSB : 1];
   bool innerA = true, innerB = true;
   auto make_lane = [&](LaneLd& l, int g, int ngl, int per_kb, int np, int ch, bool is_code, bool is_a,
                        bool& inner) {
@@ -500,10 +513,35 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
   for (int k = 0; k < WCA; k++) make_lane(ca[k], wave + 4 * k, NCA, BM * OA::NPK, OA::NPK, OA::CH, true, true, innerA);
 #pragma unroll
   for (int k = 0; k < WCB; k++) make_lane(cb[k], wave + 4 * k, NCB, BN * OB::NPK, OB::NPK, OB::CH, true, false, innerB);
+  // grouped scales: lane e of wave 0 (A) or wave 1 (B) loads the scale of
+  // group e % ngroups of K-block e / ngroups (e < 2 * ngroups)
+  const int gsa = GS ? prob.ga : 1, gsb = GS ? prob.gb : 1;
+  bool second_s = false;
+  if constexpr (GS) {
+    const bool isA = wave == 0, isB = wave == 1;
+    const int rows = isA ? BM : BN, grp = isA ? gsa : gsb;
+    const int ng = rows / grp;
+    const bool real = (isA | isB) & (lane < 2 * ng);
+    const int kb = real ? lane / ng : 0, row = real ? (lane - kb * ng) * grp : 0;
+    const PairDelta& d = isA ? dA : dB;
+    const RowInfo r = isA ? prob.row_a(cx, m0 + row) : prob.row_b(cx, n0 + row);
+    const bool ok = r.ok & real;
+    sa[0].off = ok ? r.scale + kb * d.scale : kOOB;
+    sa[0].p0 = r.p0 + kb * d.g0;
+    sa[0].p1 = r.p1 + kb * d.g1;
+    second_s = kb != 0;
+    const GRange& gr = isA ? gA : gB;
+    const int L0 = isA ? la0 : lb0, L1 = isA ? la1 : lb1;
+    const bool inner = !ok | ((sa[0].p0 + gr.min0 >= 0) & (sa[0].p0 + gr.max0 < L0) & (sa[0].p1 + gr.min1 >= 0) &
+                              (sa[0].p1 + gr.max1 < L1));
+    if (isA) innerA = innerA & inner;
+    if (isB) innerB = innerB & inner;
+  } else {
 #pragma unroll
-  for (int k = 0; k < WSA; k++) make_lane(sa[k], wave + 4 * k, NSA, BM, 1, 0, false, true, innerA);
+    for (int k = 0; k < WSA; k++) make_lane(sa[k], wave + 4 * k, NSA, BM, 1, 0, false, true, innerA);
 #pragma unroll
-  for (int k = 0; k < WSB; k++) make_lane(sb[k], wave + 4 * k, NSB, BN, 1, 0, false, false, innerB);
+    for (int k = 0; k < WSB; k++) make_lane(sb[k], wave + 4 * k, NSB, BN, 1, 0, false, false, innerB);
+  }
   // wave-uniform: no lane of this wave ever needs the border test
   const bool waveA = !P::kGeoA || __builtin_amdgcn_ballot_w64(!innerA) == 0;
   const bool waveB = !P::kGeoB || __builtin_amdgcn_ballot_w64(!innerB) == 0;
@@ -548,17 +586,26 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
       dma16(rs[2], g < NCB ? stage + OFF_B + g * 1024 : arena + DUMMY, voff(cb[k], kb, P::kGeoB, inB, lb0, lb1),
             soff(kb.code, kbi, live, tl));
     }
+    if constexpr (GS) {
+      // wave 0: A scales, wave 1: B scales, waves 2-3: zero-reading filler
+      const bool isA = wave == 0;
+      const int v = isA ? voff(sa[0], ka, P::kGeoA, inA, la0, la1) : voff(sa[0], kb, P::kGeoB, inB, lb0, lb1);
+      const int vt = (second_s & tl) ? kOOB : v;
+      dma1(isA ? rs[1] : rs[3], wave == 0 ? stage + OFF_SA : (wave == 1 ? stage + OFF_SB : arena + DUMMY), vt,
+           live ? (isA ? ka.scale : kb.scale) : kOOB);
+    } else {
 #pragma unroll
-    for (int k = 0; k < WSA; k++) {
-      const int g = wave + 4 * k, kbi = g * 64 >= BM;
-      dma1(rs[1], g < NSA ? stage + OFF_SA + g * 256 : arena + DUMMY, voff(sa[k], ka, P::kGeoA, inA, la0, la1),
-           soff(ka.scale, kbi, live, tl));
-    }
+      for (int k = 0; k < WSA; k++) {
+        const int g = wave + 4 * k, kbi = g * 64 >= BM;
+        dma1(rs[1], g < NSA ? stage + OFF_SA + g * 256 : arena + DUMMY, voff(sa[k], ka, P::kGeoA, inA, la0, la1),
+             soff(ka.scale, kbi, live, tl));
+      }
 #pragma unroll
-    for (int k = 0; k < WSB; k++) {
-      const int g = wave + 4 * k, kbi = g * 64 >= BN;
-      dma1(rs[3], g < NSB ? stage + OFF_SB + g * 256 : arena + DUMMY, voff(sb[k], kb, P::kGeoB, inB, lb0, lb1),
-           soff(kb.scale, kbi, live, tl));
+      for (int k = 0; k < WSB; k++) {
+        const int g = wave + 4 * k, kbi = g * 64 >= BN;
+        dma1(rs[3], g < NSB ? stage + OFF_SB + g * 256 : arena + DUMMY, voff(sb[k], kb, P::kGeoB, inB, lb0, lb1),
+             soff(kb.scale, kbi, live, tl));
+      }
     }
     prob.knext(cx, kit, live);
     kit.uniform();
@@ -583,13 +630,13 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
     for (int i = 0; i < TM; i++) {
       const int row = (wm * TM + i) * 32 + r32;
       a[i] = lds_operand<FA, BM>(stage, row, swz, q);
-      xa[i] = *reinterpret_cast<const int*>(stage + OFF_SA + (q * BM + row) * 4);
+      xa[i] = *reinterpret_cast<const int*>(stage + OFF_SA + (GS ? q * (BM / gsa) + row / gsa : q * BM + row) * 4);
     }
 #pragma unroll
     for (int j = 0; j < TN; j++) {
       const int row = (wn * TN + j) * 32 + r32;
       b[j] = lds_operand<FB, BN>(stage + OFF_B, row, swz, q);
-      xb[j] = *reinterpret_cast<const int*>(stage + OFF_SB + (q * BN + row) * 4);
+      xb[j] = *reinterpret_cast<const int*>(stage + OFF_SB + (GS ? q * (BN / gsb) + row / gsb : q * BN + row) * 4);
     }
   };
   auto mfmas = [&]() {
@@ -676,12 +723,12 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
   }
 }
 
-template <class P, int WM, int WN, int TM, int TN, int NS>
+template <class P, int WM, int WN, int TM, int TN, int NS, bool GS>
 hipError_t launch_gemm(int fa, int fb, const P& prob, dim3 grid, hipStream_t st) {
-#define MQ_CASE(A, B)                                                                                 \
-  if (fa == A && fb == B) {                                                                           \
-    hipLaunchKernelGGL((mx_gemm_kernel<A, B, P, WM, WN, TM, TN, NS>), grid, dim3(256), 0, st, prob);  \
-    return hipGetLastError();                                                                         \
+#define MQ_CASE(A, B)                                                                                     \
+  if (fa == A && fb == B) {                                                                               \
+    hipLaunchKernelGGL((mx_gemm_kernel<A, B, P, WM, WN, TM, TN, NS, GS>), grid, dim3(256), 0, st, prob);  \
+    return hipGetLastError();                                                                             \
   }
   MQ_CASE(0, 0) MQ_CASE(0, 1) MQ_CASE(0, 2) MQ_CASE(0, 3) MQ_CASE(0, 4)
   MQ_CASE(1, 0) MQ_CASE(1, 1) MQ_CASE(1, 2) MQ_CASE(1, 3) MQ_CASE(1, 4)
@@ -716,16 +763,36 @@ inline TileChoice choose_tile(long long M, long long Ncols, long long Z) {
   return tile_shape(1);
 }
 
+template <class P, bool GS>
+hipError_t launch_tile_id(int id, int fa, int fb, const P& prob, dim3 grid, hipStream_t st) {
+  switch (id) {
+    case 0: return launch_gemm<P, 4, 1, 2, 2, 3, GS>(fa, fb, prob, grid, st);
+    case 1: return launch_gemm<P, 2, 2, 2, 2, 3, GS>(fa, fb, prob, grid, st);
+    case 2: return launch_gemm<P, 2, 2, 4, 2, 3, GS>(fa, fb, prob, grid, st);
+    default: return launch_gemm<P, 1, 4, 2, 2, 3, GS>(fa, fb, prob, grid, st);
+  }
+}
+
+// Rows sharing one scale in a tile of `rows` rows starting at a multiple of
+// it: the block partner extent (32) when the partner size is a multiple of
+// it, the whole partner extent when it divides 32, else 0 (per-row scales).
+inline int scale_group_rows(int bp, int partner) {
+  if (bp != 32) return 0;
+  if (partner % 32 == 0) return 32;
+  if (partner < 32 && 32 % partner == 0) return partner;
+  return 0;
+}
+
 template <class P>
 hipError_t launch_tiled(int fa, int fb, const P& prob, int M, int Ncols, int Z, hipStream_t st) {
   const TileChoice t = choose_tile(M, Ncols, Z);
   dim3 grid(ceil_div(M, t.bm), ceil_div(Ncols, t.bn), Z);
-  switch (t.id) {
-    case 0: return launch_gemm<P, 4, 1, 2, 2, 3>(fa, fb, prob, grid, st);
-    case 1: return launch_gemm<P, 2, 2, 2, 2, 3>(fa, fb, prob, grid, st);
-    case 2: return launch_gemm<P, 2, 2, 4, 2, 3>(fa, fb, prob, grid, st);
-    default: return launch_gemm<P, 1, 4, 2, 2, 3>(fa, fb, prob, grid, st);
+  if constexpr (P::kCanGroup) {
+    // one 64-lane load holds both K-blocks' group scales of a 256-row tile
+    // when groups have at least 8 rows
+    if (prob.ga >= 8 && prob.gb >= 8) return launch_tile_id<P, true>(t.id, fa, fb, prob, grid, st);
   }
+  return launch_tile_id<P, false>(t.id, fa, fb, prob, grid, st);
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }

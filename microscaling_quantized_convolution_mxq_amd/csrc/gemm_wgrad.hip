@@ -117,6 +117,10 @@ hipError_t launch_backward_weight(const Conv& cv, MxView dy, MxView x, float* dw
   const long long lead = (long long)cv.ph * cv.w + cv.pw;
   p.xtcb = (int)(lead * cv.cin * p.nNB * p.xRB); p.xsb = (int)(lead * p.nNB * p.ncbi);
   if (!offsets_fit(p.xtc_bytes, p.xtcb) || !offsets_fit(p.xs_bytes, p.xsb)) return hipErrorInvalidValue;
+  // rows of A are Cout (32 to a block); rows of B are (tap, Cin), whose
+  // 32-channel blocks line up with 32-row groups when Cin is a multiple of 32
+  p.ga = 32;
+  p.gb = cv.cin % 32 == 0 ? 32 : 0;
   const long long nj = (long long)p.T * cv.cin;
   e = launch_tiled(dy.fmt, x.fmt, p, cv.cout, (int)nj, S, st);
   if (e != hipSuccess) return e;
