@@ -24,6 +24,12 @@ hipError_t launch_backward_data(const Conv& cv, MxView dy, MxView w, float* dx, 
   p.dycb = (int)(dmax * cv.n * p.dyrb); p.dysb = (int)(dmax * p.dynPB * p.ncob);
   if (!offsets_fit(p.dyc_bytes, p.dycb) || !offsets_fit(p.dys_bytes, p.dysb)) return hipErrorInvalidValue;
   // rows of A are (pixel, n); rows of B are Cin, 32 to a block
+  p.dybps = dy.bp == 32 ? 5 : 0;
+  p.dN = make_fastdiv(cv.n);
+  for (int c = 0; c < 8; c++) {  // width of the parity class with column offset c (c < sw)
+    const int wc = c < cv.sw && cv.w > c ? (cv.w - c + cv.sw - 1) / cv.sw : 1;
+    p.dWc[c] = make_fastdiv((unsigned)(wc > 0 ? wc : 1));
+  }
   p.ga = scale_group_rows(dy.bp, cv.n);
   p.gb = 32;
   const int maxHc = ceil_div(cv.h, cv.sh), maxWc = ceil_div(cv.w, cv.sw);

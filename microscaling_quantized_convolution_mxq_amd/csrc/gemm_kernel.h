@@ -45,6 +45,8 @@ struct RowInfo { int code, scale, p0, p1; bool ok; };
 struct KInfo { int code, scale, g0, g1; };
 struct PairDelta { int code, scale, g0, g1; };
 struct GRange { int min0, max0, min1, max1; };
+// Reciprocals of the grid's x extent and x*y extent (workgroup re-ordering).
+struct GridDivs { FastDiv nx, nxy; };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, long long bytes) {
   const int n = bytes < (long long)kOOB ? (int)bytes : kOOB;
@@ -64,6 +66,9 @@ struct FwdProb {
   int wrb, wRB, wnCoB, wbp;              // weight row bytes, run bytes, Cout blocks, bp
   int xcb, xsb;                          // bias of the activation row offsets (padding)
   int ga, gb;                            // rows sharing one scale (A, B); 0: per-row scales
+  int xbps, wbps;                        // log2 of the activation and weight bp
+  FastDiv dN, dWo, dKW, dnp;             // reciprocals of N, Wo, KW, npair
+  GridDivs grid;
   static constexpr bool kGeoA = true, kGeoB = false, kCanGroup = true;
   struct Ctx {};
   struct KS {
@@ -75,7 +80,8 @@ struct FwdProb {
   __device__ int ncols() const { return Cout; }
   __device__ void steps(const Ctx&, int, int& lo, int& hi) const { lo = 0; hi = T * npair; }
   __device__ KS kstart(const Ctx&, int s) const {
-    const int u = s / npair; KS k; k.v = 2 * (s - u * npair); k.kh = u / KW; k.kw = u - k.kh * KW; return k;
+    const int u = (int)fdiv((unsigned)s, dnp); KS k; k.v = 2 * (s - u * npair);
+    k.kh = (int)fdiv((unsigned)u, dKW); k.kw = u - k.kh * KW; return k;
   }
   // advances k by one step when go (field-wise selects: no branch, no memory)
   __device__ void knext(const Ctx&, KS& k, bool go) const {
@@ -90,10 +96,11 @@ struct FwdProb {
   __device__ PairDelta pd_b() const { return PairDelta{wRB, 1, 0, 0}; }
   __device__ RowInfo row_a(const Ctx&, int m) const {
     RowInfo r; r.ok = m < M; const int mm = r.ok ? m : 0;
-    const int pix = mm / N, n = mm - pix * N, ho = pix / Wo, wo = pix - ho * Wo;
+    const int pix = (int)fdiv((unsigned)mm, dN), n = mm - pix * N;
+    const int ho = (int)fdiv((unsigned)pix, dWo), wo = pix - ho * Wo;
     r.p0 = ho * sh - ph; r.p1 = wo * sw - pw;
     const int p = r.p0 * W + r.p1;
-    r.code = (p * N + n) * xrb + xcb; r.scale = (p * xnPB + n / xbp) * ncb + xsb; return r;
+    r.code = (p * N + n) * xrb + xcb; r.scale = (p * xnPB + (n >> xbps)) * ncb + xsb; return r;
   }
   __device__ KInfo k_a(const Ctx&, const KS& k) const {
     const int d = k.kh * W + k.kw;
@@ -101,7 +108,7 @@ struct FwdProb {
   }
   __device__ RowInfo row_b(const Ctx&, int c) const {
     RowInfo r; r.ok = c < Cout; const int cc = r.ok ? c : 0;
-    r.code = cc * T * wrb; r.scale = (cc / wbp) * ncb; r.p0 = 0; r.p1 = 0; return r;
+    r.code = cc * T * wrb; r.scale = (cc >> wbps) * ncb; r.p0 = 0; r.p1 = 0; return r;
   }
   __device__ KInfo k_b(const Ctx&, const KS& k) const {
     const int tap = k.kh * KW + k.kw;
@@ -132,6 +139,9 @@ struct DgradProb {
   int wRB, ncbi;                             // weight run bytes, Cin blocks
   int dycb, dysb;                            // bias of the step offsets (backward taps)
   int ga, gb;                                // rows sharing one scale (A, B); 0: per-row scales
+  int dybps;                                 // log2 of the gradient bp
+  FastDiv dN, dWc[8];                        // reciprocals of N and of each class's width (by pw_c)
+  GridDivs grid;
   static constexpr bool kGeoA = true, kGeoB = false, kCanGroup = true;
   struct Ctx { int ph_c, pw_c, Hc, Wc, kh0, kw0, nkh, nkw, M; };
   struct KS {
@@ -168,12 +178,13 @@ struct DgradProb {
   __device__ RowInfo row_a(const Ctx& c, int m) const {
     RowInfo r; r.ok = m < c.M; const int mm = r.ok ? m : 0;
     const int wc = c.Wc > 0 ? c.Wc : 1;
-    const int pix = mm / N, n = mm - pix * N, hq = pix / wc, wq = pix - hq * wc;
+    const int pix = (int)fdiv((unsigned)mm, dN), n = mm - pix * N;
+    const int hq = (int)fdiv((unsigned)pix, dWc[c.pw_c]), wq = pix - hq * wc;
     // output pixel of tap (kh0, kw0); exact division by the class choice
     r.p0 = hq + (c.ph_c + ph - c.kh0) / sh;
     r.p1 = wq + (c.pw_c + pw - c.kw0) / sw;
     const int p = r.p0 * Wo + r.p1;
-    r.code = (p * N + n) * dyrb; r.scale = (p * dynPB + n / dybp) * ncob; return r;
+    r.code = (p * N + n) * dyrb; r.scale = (p * dynPB + (n >> dybps)) * ncob; return r;
   }
   __device__ KInfo k_a(const Ctx&, const KS& k) const {
     const int d = k.ih * Wo + k.iw;
@@ -197,7 +208,8 @@ struct DgradProb {
   __device__ bool step_interior_b(const Ctx&, const KS&) const { return true; }
   __device__ float* out_row(const Ctx& c, int, int m) const {
     if (m >= c.M) return nullptr;
-    const int pix = m / N, n = m - pix * N, hq = pix / c.Wc, wq = pix - hq * c.Wc;
+    const int pix = (int)fdiv((unsigned)m, dN), n = m - pix * N;
+    const int hq = (int)fdiv((unsigned)pix, dWc[c.pw_c]), wq = pix - hq * c.Wc;
     const int h = hq * sh + c.ph_c, w = wq * sw + c.pw_c;
     return dx + (((long long)h * W + w) * N + n) * Cin;
   }
@@ -218,6 +230,8 @@ struct WgradProb {
   int total_steps, steps_per_split;
   int xtcb, xsb;       // bias of the activation row offsets (padding)
   int ga, gb;          // rows sharing one scale (A, B); 0: per-row scales
+  FastDiv dCin, dKW;   // reciprocals of Cin and KW
+  GridDivs grid;
   static constexpr bool kGeoA = false, kGeoB = true, kCanGroup = true;
   struct Ctx {};
   struct KS {
@@ -260,7 +274,8 @@ struct WgradProb {
   }
   __device__ RowInfo row_b(const Ctx&, int j) const {
     RowInfo r; r.ok = j < T * Cin; const int jj = r.ok ? j : 0;
-    const int tap = jj / Cin, ci = jj - tap * Cin, kh = tap / KW, kw = tap - kh * KW;
+    const int tap = (int)fdiv((unsigned)jj, dCin), ci = jj - tap * Cin;
+    const int kh = (int)fdiv((unsigned)tap, dKW), kw = tap - kh * KW;
     r.p0 = kh - ph; r.p1 = kw - pw;
     const int p = r.p0 * W + r.p1;
     r.code = (p * Cin + ci) * nNB * xRB + xtcb; r.scale = p * nNB * ncbi + ci / 32 + xsb; return r;
@@ -296,6 +311,7 @@ struct PlainProb {
   long long ac_bytes, as_bytes, bc_bytes, bs_bytes;
   int Ma, Nb, nkb, aRB, bRB, pairs_per_split, arb, brb;
   int ga = 0, gb = 0;
+  GridDivs grid;
   static constexpr bool kGeoA = false, kGeoB = false, kCanGroup = false;
   struct Ctx {};
   struct KS {
@@ -475,9 +491,10 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
     const int lin = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
     const int xcd = lin % 8, idx = lin / 8, q8 = nb / 8, r8 = nb % 8;
     const int logical = xcd < r8 ? xcd * (q8 + 1) + idx : r8 * (q8 + 1) + (xcd - r8) * q8 + idx;
-    bx = logical % nx;
-    by = (logical / nx) % ny;
-    z = logical / (nx * ny);
+    z = (int)fdiv((unsigned)logical, prob.grid.nxy);
+    const int rem = logical - z * nx * ny;
+    by = (int)fdiv((unsigned)rem, prob.grid.nx);
+    bx = rem - by * nx;
   }
   const typename P::Ctx cx = prob.ctx(z);
   const int m0 = bx * BM, n0 = by * BN;
@@ -784,9 +801,12 @@ inline int scale_group_rows(int bp, int partner) {
 }
 
 template <class P>
-hipError_t launch_tiled(int fa, int fb, const P& prob, int M, int Ncols, int Z, hipStream_t st) {
+hipError_t launch_tiled(int fa, int fb, const P& prob_in, int M, int Ncols, int Z, hipStream_t st) {
   const TileChoice t = choose_tile(M, Ncols, Z);
   dim3 grid(ceil_div(M, t.bm), ceil_div(Ncols, t.bn), Z);
+  P prob = prob_in;
+  prob.grid.nx = make_fastdiv(grid.x);
+  prob.grid.nxy = make_fastdiv(grid.x * grid.y);
   if constexpr (P::kCanGroup) {
     // one 64-lane load holds both K-blocks' group scales of a 256-row tile
     // when groups have at least 8 rows

@@ -119,6 +119,7 @@ hipError_t launch_backward_weight(const Conv& cv, MxView dy, MxView x, float* dw
   if (!offsets_fit(p.xtc_bytes, p.xtcb) || !offsets_fit(p.xs_bytes, p.xsb)) return hipErrorInvalidValue;
   // rows of A are Cout (32 to a block); rows of B are (tap, Cin), whose
   // 32-channel blocks line up with 32-row groups when Cin is a multiple of 32
+  p.dCin = make_fastdiv(cv.cin); p.dKW = make_fastdiv(cv.kw);
   p.ga = 32;
   p.gb = cv.cin % 32 == 0 ? 32 : 0;
   const long long nj = (long long)p.T * cv.cin;

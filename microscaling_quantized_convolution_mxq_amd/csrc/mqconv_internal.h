@@ -23,6 +23,26 @@ struct MxView {
 };
 
 inline int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+// x / d for 0 <= x < 2^31 as (x * m) >> (32 + s), m = ceil(2^(31+l) / d),
+// l = ceil(log2 d), s = l - 1: m * d exceeds 2^(31+l) by less than d <= 2^l,
+// so the error stays below 1/d and the floor is exact; m < 2^32.
+struct FastDiv {
+  unsigned m, s, d;
+};
+inline FastDiv make_fastdiv(unsigned d) {
+  FastDiv f; f.d = d;
+  if (d == 1) { f.m = 0; f.s = 0; return f; }
+  unsigned l = 0;
+  while ((1ull << l) < d) l++;
+  f.m = (unsigned)(((1ull << (31 + l)) + d - 1) / d);
+  f.s = l - 1;
+  return f;
+}
+__device__ __forceinline__ unsigned fdiv(unsigned x, const FastDiv& f) {
+  return f.d == 1 ? x : (__umulhi(x, f.m) >> f.s);
+}
+
 inline long long run_bytes(int fmt) { return fmt <= 1 ? 32 : (fmt <= 3 ? 24 : 16); }
 inline long long row_bytes(int fmt, long long C) { return ((C + 31) / 32) * run_bytes(fmt); }
 
