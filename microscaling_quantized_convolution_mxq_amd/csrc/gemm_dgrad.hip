@@ -30,6 +30,7 @@ hipError_t launch_backward_data(const Conv& cv, MxView dy, MxView w, float* dx, 
     const int wc = c < cv.sw && cv.w > c ? (cv.w - c + cv.sw - 1) / cv.sw : 1;
     p.dWc[c] = make_fastdiv((unsigned)(wc > 0 ? wc : 1));
   }
+  p.khalf = cv.cout <= 16;
   p.ga = scale_group_rows(dy.bp, cv.n);
   p.gb = 32;
   const int maxHc = ceil_div(cv.h, cv.sh), maxWc = ceil_div(cv.w, cv.sw);

@@ -22,6 +22,7 @@ hipError_t launch_forward(const Conv& cv, MxView x, MxView w, float* y, void*, s
   // rows of A are (pixel, n): a block is 32 (or all N < 32) of them; rows of B are Cout
   p.xbps = x.bp == 32 ? 5 : 0; p.wbps = w.bp == 32 ? 5 : 0;
   p.dN = make_fastdiv(cv.n); p.dWo = make_fastdiv(p.Wo); p.dKW = make_fastdiv(cv.kw); p.dnp = make_fastdiv(p.npair);
+  p.khalf = cv.cin <= 16;
   p.ga = scale_group_rows(x.bp, cv.n);
   p.gb = w.bp == 32 ? 32 : 0;
   return launch_tiled(x.fmt, w.fmt, p, p.M, cv.cout, 1, st);

@@ -67,6 +67,7 @@ struct FwdProb {
   int xcb, xsb;                          // bias of the activation row offsets (padding)
   int ga, gb;                            // rows sharing one scale (A, B); 0: per-row scales
   int xbps, wbps;                        // log2 of the activation and weight bp
+  int khalf;                             // every K-block holds at most 16 valid codes
   FastDiv dN, dWo, dKW, dnp;             // reciprocals of N, Wo, KW, npair
   GridDivs grid;
   static constexpr bool kGeoA = true, kGeoB = false, kCanGroup = true;
@@ -140,6 +141,7 @@ struct DgradProb {
   int dycb, dysb;                            // bias of the step offsets (backward taps)
   int ga, gb;                                // rows sharing one scale (A, B); 0: per-row scales
   int dybps;                                 // log2 of the gradient bp
+  int khalf;                                 // every K-block holds at most 16 valid codes
   FastDiv dN, dWc[8];                        // reciprocals of N and of each class's width (by pw_c)
   GridDivs grid;
   static constexpr bool kGeoA = true, kGeoB = false, kCanGroup = true;
@@ -231,6 +233,7 @@ struct WgradProb {
   int xtcb, xsb;       // bias of the activation row offsets (padding)
   int ga, gb;          // rows sharing one scale (A, B); 0: per-row scales
   FastDiv dCin, dKW;   // reciprocals of Cin and KW
+  int khalf;           // every K-block holds at most 16 valid codes (N <= 16)
   GridDivs grid;
   static constexpr bool kGeoA = false, kGeoB = true, kCanGroup = true;
   struct Ctx {};
@@ -417,6 +420,17 @@ __device__ __forceinline__ v8i lds_operand(const uint8_t* stage, int row, int sw
   return r;
 }
 
+// Operand image of an 8-bit row from a piece-major stage ([kb][piece][row]
+// 16-byte slots), used when only piece 0 of each run is loaded (K-blocks
+// with at most 16 valid codes; piece 1 holds zeros).
+template <int BR>
+__device__ __forceinline__ v8i lds_operand_pm(const uint8_t* stage, int row, int q) {
+  const v4i lo = *reinterpret_cast<const v4i*>(stage + (q * BR + row) * 16);
+  const v4i hi = *reinterpret_cast<const v4i*>(stage + ((2 + q) * BR + row) * 16);
+  v8i r = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return r;
+}
+
 // Per-lane part of one LDS-writing load: byte offset of the lane's piece
 // relative to the step's uniform offset (kOOB when the row is outside the
 // problem or the load only keeps the count uniform) and the row's border
@@ -454,8 +468,12 @@ __device__ __forceinline__ void stage_barrier() {
 // one 64-lane load per operand fetches them: wave 0 the A scales, wave 1 the
 // B scales; waves 2 and 3 issue a zero-reading load to keep every wave's
 // load count equal.
-template <int FA, int FB, class P, int WM, int WN, int TM, int TN, int NS, bool GS>
+// KH: every K-block has at most 16 valid codes (8-bit formats only): the
+// stages are piece-major and only piece 0 of each run is loaded; piece 1 is
+// zeroed once.
+template <int FA, int FB, class P, int WM, int WN, int TM, int TN, int NS, bool GS, bool KH>
 __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
+  static_assert(!KH || (FA <= 1 && FB <= 1), "half K-blocks only for 8-bit codes");
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
   using OA = Op<FA>;
   using OB = Op<FB>;
@@ -465,7 +483,7 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
   constexpr int STAGE = OFF_SB + SB_BYTES;
   // LDS-writing loads (64 lanes each) per stage and per wave; load g of a
   // kind belongs to K-block g / (loads per K-block)
-  constexpr int NCA = 2 * BM * OA::NPK / 64, NCB = 2 * BN * OB::NPK / 64;
+  constexpr int NCA = 2 * BM * (KH ? 1 : OA::NPK) / 64, NCB = 2 * BN * (KH ? 1 : OB::NPK) / 64;
   constexpr int NSA = GS ? 1 : 2 * BM / 64, NSB = GS ? 1 : 2 * BN / 64;
   constexpr int WCA = (NCA + 3) / 4, WCB = (NCB + 3) / 4;
   constexpr int WSA = GS ? 1 : (NSA + 3) / 4, WSB = GS ? 0 : (NSB + 3) / 4;
@@ -527,9 +545,11 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
                             (l.p1 + gr.max1 < L1)));
   };
 #pragma unroll
-  for (int k = 0; k < WCA; k++) make_lane(ca[k], wave + 4 * k, NCA, BM * OA::NPK, OA::NPK, OA::CH, true, true, innerA);
+  for (int k = 0; k < WCA; k++)
+    make_lane(ca[k], wave + 4 * k, NCA, BM * (KH ? 1 : OA::NPK), KH ? 1 : OA::NPK, OA::CH, true, true, innerA);
 #pragma unroll
-  for (int k = 0; k < WCB; k++) make_lane(cb[k], wave + 4 * k, NCB, BN * OB::NPK, OB::NPK, OB::CH, true, false, innerB);
+  for (int k = 0; k < WCB; k++)
+    make_lane(cb[k], wave + 4 * k, NCB, BN * (KH ? 1 : OB::NPK), KH ? 1 : OB::NPK, OB::CH, true, false, innerB);
   // grouped scales: lane e of wave 0 (A) or wave 1 (B) loads the scale of
   // group e % ngroups of K-block e / ngroups (e < 2 * ngroups)
   const int gsa = GS ? prob.ga : 1, gsb = GS ? prob.gb : 1;
@@ -593,14 +613,19 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
     uint8_t* const stage = arena + st * STAGE;
 #pragma unroll
     for (int k = 0; k < WCA; k++) {
-      const int g = wave + 4 * k, kbi = g * 64 >= BM * OA::NPK;
-      dma16(rs[0], g < NCA ? stage + g * 1024 : arena + DUMMY, voff(ca[k], ka, P::kGeoA, inA, la0, la1),
+      const int g = wave + 4 * k;
+      const int kbi = KH ? g * 64 >= BM : g * 64 >= BM * OA::NPK;
+      // KH: piece 0 of K-block kbi lands at slot (2*kbi)*BM + row
+      const int slot = KH ? g * 64 + kbi * BM : g * 64;
+      dma16(rs[0], g < NCA ? stage + slot * 16 : arena + DUMMY, voff(ca[k], ka, P::kGeoA, inA, la0, la1),
             soff(ka.code, kbi, live, tl));
     }
 #pragma unroll
     for (int k = 0; k < WCB; k++) {
-      const int g = wave + 4 * k, kbi = g * 64 >= BN * OB::NPK;
-      dma16(rs[2], g < NCB ? stage + OFF_B + g * 1024 : arena + DUMMY, voff(cb[k], kb, P::kGeoB, inB, lb0, lb1),
+      const int g = wave + 4 * k;
+      const int kbi = KH ? g * 64 >= BN : g * 64 >= BN * OB::NPK;
+      const int slot = KH ? g * 64 + kbi * BN : g * 64;
+      dma16(rs[2], g < NCB ? stage + OFF_B + slot * 16 : arena + DUMMY, voff(cb[k], kb, P::kGeoB, inB, lb0, lb1),
             soff(kb.code, kbi, live, tl));
     }
     if constexpr (GS) {
@@ -646,13 +671,15 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
 #pragma unroll
     for (int i = 0; i < TM; i++) {
       const int row = (wm * TM + i) * 32 + r32;
-      a[i] = lds_operand<FA, BM>(stage, row, swz, q);
+      if constexpr (KH) a[i] = lds_operand_pm<BM>(stage, row, q);
+      else a[i] = lds_operand<FA, BM>(stage, row, swz, q);
       xa[i] = *reinterpret_cast<const int*>(stage + OFF_SA + (GS ? q * (BM / gsa) + row / gsa : q * BM + row) * 4);
     }
 #pragma unroll
     for (int j = 0; j < TN; j++) {
       const int row = (wn * TN + j) * 32 + r32;
-      b[j] = lds_operand<FB, BN>(stage + OFF_B, row, swz, q);
+      if constexpr (KH) b[j] = lds_operand_pm<BN>(stage + OFF_B, row, q);
+      else b[j] = lds_operand<FB, BN>(stage + OFF_B, row, swz, q);
       xb[j] = *reinterpret_cast<const int*>(stage + OFF_SB + (GS ? q * (BN / gsb) + row / gsb : q * BN + row) * 4);
     }
   };
@@ -669,6 +696,15 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
   // stage s (every wave has waited for its own loads of step s) and retires
   // every wave's reads of stage s-1.
   const int nsteps = s_hi - s_lo;
+  if constexpr (KH) {  // piece 1 of every run in every stage is zero (never loaded)
+    const v4i zero = {0, 0, 0, 0};
+    for (int st = 0; st < NS; st++)
+      for (int i = tid; i < 2 * (BM + BN); i += 256) {
+        const int kb = i / (BM + BN), r = i - kb * (BM + BN);
+        uint8_t* base = arena + st * STAGE + (r < BM ? ((2 * kb + 1) * BM + r) * 16 : OFF_B + ((2 * kb + 1) * BN + r - BM) * 16);
+        *reinterpret_cast<v4i*>(base) = zero;
+      }
+  }
 #pragma unroll
   for (int i = 0; i < NS - 1; i++) issue(i);
   int cs = 0;
@@ -740,18 +776,23 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
   }
 }
 
-template <class P, int WM, int WN, int TM, int TN, int NS, bool GS>
+template <class P, int WM, int WN, int TM, int TN, int NS, bool GS, bool KH>
 hipError_t launch_gemm(int fa, int fb, const P& prob, dim3 grid, hipStream_t st) {
-#define MQ_CASE(A, B)                                                                                     \
-  if (fa == A && fb == B) {                                                                               \
-    hipLaunchKernelGGL((mx_gemm_kernel<A, B, P, WM, WN, TM, TN, NS, GS>), grid, dim3(256), 0, st, prob);  \
-    return hipGetLastError();                                                                             \
+#define MQ_CASE(A, B)                                                                                         \
+  if (fa == A && fb == B) {                                                                                   \
+    hipLaunchKernelGGL((mx_gemm_kernel<A, B, P, WM, WN, TM, TN, NS, GS, KH>), grid, dim3(256), 0, st, prob);  \
+    return hipGetLastError();                                                                                 \
   }
+  if constexpr (KH) {
+    MQ_CASE(0, 0) MQ_CASE(0, 1) MQ_CASE(1, 0) MQ_CASE(1, 1)
+    return hipErrorInvalidValue;
+  } else {
   MQ_CASE(0, 0) MQ_CASE(0, 1) MQ_CASE(0, 2) MQ_CASE(0, 3) MQ_CASE(0, 4)
   MQ_CASE(1, 0) MQ_CASE(1, 1) MQ_CASE(1, 2) MQ_CASE(1, 3) MQ_CASE(1, 4)
   MQ_CASE(2, 0) MQ_CASE(2, 1) MQ_CASE(2, 2) MQ_CASE(2, 3) MQ_CASE(2, 4)
   MQ_CASE(3, 0) MQ_CASE(3, 1) MQ_CASE(3, 2) MQ_CASE(3, 3) MQ_CASE(3, 4)
   MQ_CASE(4, 0) MQ_CASE(4, 1) MQ_CASE(4, 2) MQ_CASE(4, 3) MQ_CASE(4, 4)
+  }
 #undef MQ_CASE
   return hipErrorInvalidValue;
 }
@@ -780,13 +821,13 @@ inline TileChoice choose_tile(long long M, long long Ncols, long long Z) {
   return tile_shape(1);
 }
 
-template <class P, bool GS>
+template <class P, bool GS, bool KH>
 hipError_t launch_tile_id(int id, int fa, int fb, const P& prob, dim3 grid, hipStream_t st) {
   switch (id) {
-    case 0: return launch_gemm<P, 4, 1, 2, 2, 3, GS>(fa, fb, prob, grid, st);
-    case 1: return launch_gemm<P, 2, 2, 2, 2, 3, GS>(fa, fb, prob, grid, st);
-    case 2: return launch_gemm<P, 2, 2, 4, 2, 3, GS>(fa, fb, prob, grid, st);
-    default: return launch_gemm<P, 1, 4, 2, 2, 3, GS>(fa, fb, prob, grid, st);
+    case 0: return launch_gemm<P, 4, 1, 2, 2, 3, GS, KH>(fa, fb, prob, grid, st);
+    case 1: return launch_gemm<P, 2, 2, 2, 2, 3, GS, KH>(fa, fb, prob, grid, st);
+    case 2: return launch_gemm<P, 2, 2, 4, 2, 3, GS, KH>(fa, fb, prob, grid, st);
+    default: return launch_gemm<P, 1, 4, 2, 2, 3, GS, KH>(fa, fb, prob, grid, st);
   }
 }
 
@@ -810,9 +851,12 @@ hipError_t launch_tiled(int fa, int fb, const P& prob_in, int M, int Ncols, int 
   if constexpr (P::kCanGroup) {
     // one 64-lane load holds both K-blocks' group scales of a 256-row tile
     // when groups have at least 8 rows
-    if (prob.ga >= 8 && prob.gb >= 8) return launch_tile_id<P, true>(t.id, fa, fb, prob, grid, st);
+    if (prob.ga >= 8 && prob.gb >= 8) {
+      if (prob.khalf && fa <= 1 && fb <= 1) return launch_tile_id<P, true, true>(t.id, fa, fb, prob, grid, st);
+      return launch_tile_id<P, true, false>(t.id, fa, fb, prob, grid, st);
+    }
   }
-  return launch_tile_id<P, false>(t.id, fa, fb, prob, grid, st);
+  return launch_tile_id<P, false, false>(t.id, fa, fb, prob, grid, st);
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }

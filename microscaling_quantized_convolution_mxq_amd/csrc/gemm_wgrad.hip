@@ -120,6 +120,7 @@ hipError_t launch_backward_weight(const Conv& cv, MxView dy, MxView x, float* dw
   // rows of A are Cout (32 to a block); rows of B are (tap, Cin), whose
   // 32-channel blocks line up with 32-row groups when Cin is a multiple of 32
   p.dCin = make_fastdiv(cv.cin); p.dKW = make_fastdiv(cv.kw);
+  p.khalf = cv.n <= 16;
   p.ga = 32;
   p.gb = cv.cin % 32 == 0 ? 32 : 0;
   const long long nj = (long long)p.T * cv.cin;

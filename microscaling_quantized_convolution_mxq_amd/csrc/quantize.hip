@@ -79,11 +79,17 @@ __device__ __forceinline__ void convert_store_half_run(uint8_t* dst, const float
 // MODE 2: square blocks over a partner extent P in {1, 2, 4, 8, 16} with
 //         B = 1: a tile is 32 consecutive memory rows = 32/P whole pixels,
 //         and each pixel's P rows form one block (no idle lanes for small N).
-template <int F, int MODE>
+// ST: the tile's 32 rows are consecutive in memory (B = 1) and short
+// (at most 8 channel blocks): the wave packs them in LDS and writes the
+// tile's bytes as one contiguous stretch, so every store covers whole
+// cache lines (6-bit runs are 24 bytes, which direct stores would split).
+constexpr int kStageCB = 8;
+template <int F, int MODE, bool ST>
 __global__ __launch_bounds__(256) void mxq_quantize_kernel(const float* __restrict__ src,
                                                           uint8_t* __restrict__ codes,
                                                           uint8_t* __restrict__ scales, int A, int P,
                                                           int B, int C, int bp, long long ntiles) {
+  __shared__ __attribute__((aligned(16))) uint8_t stage_buf[ST ? 4 : 1][ST ? 32 * kStageCB * 32 : 16];
   const int lane = threadIdx.x & 63;
   const long long tile = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (tile >= ntiles) return;
@@ -156,10 +162,24 @@ __global__ __launch_bounds__(256) void mxq_quantize_kernel(const float* __restri
     float v[16];
 #pragma unroll
     for (int i = 0; i < 16; i++) v[i] = S == 255u ? 0.0f : fminf(fmaxf(x[i] * inv, -maxv), maxv);
-    if (row_ok) {
+    if constexpr (ST) {
+      convert_store_half_run<F>(&stage_buf[threadIdx.x >> 6][r * row_bytes + cb * RB + half * (RB / 2)], v);
+      if (row_ok && writes_scale) scales[sidx + cb] = (uint8_t)S;
+    } else if (row_ok) {
       convert_store_half_run<F>(codes + row * row_bytes + (long long)cb * RB + half * (RB / 2), v);
       if (writes_scale) scales[sidx + cb] = (uint8_t)S;
     }
+  }
+  if constexpr (ST) {
+    // rows row0 .. row0 + nvalid - 1 of this tile are valid and consecutive
+    const long long row0 = __shfl(row, 0);
+    const int nvalid = __popcll(__ballot(row_ok && half == 0));
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's packed rows are in LDS
+    __builtin_amdgcn_wave_barrier();
+    const int words = (int)(nvalid * row_bytes / 4);
+    const uint32_t* from = reinterpret_cast<const uint32_t*>(stage_buf[threadIdx.x >> 6]);
+    uint32_t* to = reinterpret_cast<uint32_t*>(codes + row0 * row_bytes);
+    for (int i = lane; i < words; i += 64) to[i] = from[i];
   }
 }
 
@@ -168,8 +188,12 @@ static hipError_t launch_q(const float* src, uint8_t* codes, uint8_t* scales, in
                            int C, int bp, hipStream_t st) {
   const long long ntiles = MODE == 2 ? ((long long)A * P + 31) / 32 : (long long)A * B * ((P + 31) / 32);
   const long long blocks = (ntiles + 3) / 4;
-  hipLaunchKernelGGL((mxq_quantize_kernel<F, MODE>), dim3((unsigned)blocks), dim3(256), 0, st, src,
-                     codes, scales, A, P, B, C, bp, ntiles);
+  if (B == 1 && (C + 31) / 32 <= kStageCB)
+    hipLaunchKernelGGL((mxq_quantize_kernel<F, MODE, true>), dim3((unsigned)blocks), dim3(256), 0, st, src,
+                       codes, scales, A, P, B, C, bp, ntiles);
+  else
+    hipLaunchKernelGGL((mxq_quantize_kernel<F, MODE, false>), dim3((unsigned)blocks), dim3(256), 0, st, src,
+                       codes, scales, A, P, B, C, bp, ntiles);
   return hipGetLastError();
 }
 
