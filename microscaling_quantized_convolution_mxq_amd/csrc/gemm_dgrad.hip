@@ -6,16 +6,21 @@ namespace mq {
 hipError_t launch_backward_data(const Conv& cv, MxView dy, MxView w, float* dx, void* ws, size_t,
                                 hipStream_t st) {
   uint8_t* wt = static_cast<uint8_t*>(ws);
-  hipError_t e = launch_transpose_codes(w.codes, wt, w.fmt, 1, cv.cout, cv.kh * cv.kw, cv.cin, st);
-  if (e != hipSuccess) return e;
   DgradProb p;
+  // rows of A are (pixel, n); rows of B are Cin, 32 to a block
+  p.khalf = cv.cout <= 16;
+  p.ga = scale_group_rows(dy.bp, cv.n);
+  p.gb = 32;
+  const bool half = half_k_blocks(p.ga, p.gb, p.khalf, dy.fmt, w.fmt);
+  hipError_t e = launch_transpose_codes(w.codes, wt, w.fmt, half, 1, cv.cout, cv.kh * cv.kw, cv.cin, st);
+  if (e != hipSuccess) return e;
   p.dyc = dy.codes; p.dys = dy.scales; p.wtc = wt; p.ws = w.scales; p.dx = dx;
   p.N = cv.n; p.H = cv.h; p.W = cv.w; p.Cin = cv.cin; p.Cout = cv.cout; p.KH = cv.kh; p.KW = cv.kw;
   p.sh = cv.sh; p.sw = cv.sw; p.ph = cv.ph; p.pw = cv.pw; p.Ho = cv.ho(); p.Wo = cv.wo();
   p.ncob = ceil_div(cv.cout, 32);
   p.npair = (p.ncob + 1) / 2;
   p.dyRB = (int)run_bytes(dy.fmt); p.dyrb = p.ncob * p.dyRB; p.dybp = dy.bp; p.dynPB = ceil_div(cv.n, dy.bp);
-  p.wRB = (int)run_bytes(w.fmt); p.ncbi = ceil_div(cv.cin, 32);
+  p.wRB = half ? 16 : (int)run_bytes(w.fmt); p.ncbi = ceil_div(cv.cin, 32);
   const long long T = (long long)cv.kh * cv.kw;
   p.dyc_bytes = (long long)p.Ho * p.Wo * cv.n * p.dyrb; p.dys_bytes = (long long)p.Ho * p.Wo * p.dynPB * p.ncob;
   p.wtc_bytes = T * cv.cin * p.ncob * p.wRB; p.ws_bytes = T * p.ncob * p.ncbi;
@@ -23,16 +28,15 @@ hipError_t launch_backward_data(const Conv& cv, MxView dy, MxView w, float* dx, 
   const long long dmax = (long long)(ceil_div(cv.kh, cv.sh) - 1) * p.Wo + (ceil_div(cv.kw, cv.sw) - 1);
   p.dycb = (int)(dmax * cv.n * p.dyrb); p.dysb = (int)(dmax * p.dynPB * p.ncob);
   if (!offsets_fit(p.dyc_bytes, p.dycb) || !offsets_fit(p.dys_bytes, p.dysb)) return hipErrorInvalidValue;
-  // rows of A are (pixel, n); rows of B are Cin, 32 to a block
   p.dybps = dy.bp == 32 ? 5 : 0;
-  p.dN = make_fastdiv(cv.n);
-  for (int c = 0; c < 8; c++) {  // width of the parity class with column offset c (c < sw)
+  p.dN = make_fastdiv(cv.n); p.dnp = make_fastdiv(p.npair);
+  for (int c = 0; c < 8; c++) {  // parity class with column offset c (c < sw): width, tap columns
     const int wc = c < cv.sw && cv.w > c ? (cv.w - c + cv.sw - 1) / cv.sw : 1;
     p.dWc[c] = make_fastdiv((unsigned)(wc > 0 ? wc : 1));
+    const int kw0 = c < cv.sw ? (c + cv.pw) % cv.sw : 0;
+    const int nkw = kw0 < cv.kw ? (cv.kw - kw0 + cv.sw - 1) / cv.sw : 0;
+    p.dNkw[c] = make_fastdiv((unsigned)(nkw > 0 ? nkw : 1));
   }
-  p.khalf = cv.cout <= 16;
-  p.ga = scale_group_rows(dy.bp, cv.n);
-  p.gb = 32;
   const int maxHc = ceil_div(cv.h, cv.sh), maxWc = ceil_div(cv.w, cv.sw);
   return launch_tiled(dy.fmt, w.fmt, p, maxHc * maxWc * cv.n, cv.cin, cv.sh * cv.sw, st);
 }

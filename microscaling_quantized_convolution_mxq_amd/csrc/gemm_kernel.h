@@ -26,8 +26,9 @@ namespace mq {
 
 // Byte offsets into a problem's code and scale buffers are the sum of a
 // per-row part (fixed per lane, the buffer load's vector offset) and a
-// per-step part (uniform across the workgroup, advanced incrementally in
-// scalar registers, the load's scalar offset):
+// per-step part (uniform across the workgroup, the load's scalar offset; the
+// kernel computes it for 64 steps at a time, one step per lane, from
+// kstart/k_a/k_b, and reads each step's into scalar registers):
 //   code  = row.code + k.code,   scale = row.scale + k.scale
 // Both parts are kept non-negative: where a row or a step moves backwards
 // (padding, backward taps) the problem adds a bias to one part and the
@@ -72,10 +73,7 @@ struct FwdProb {
   GridDivs grid;
   static constexpr bool kGeoA = true, kGeoB = false, kCanGroup = true;
   struct Ctx {};
-  struct KS {
-    int kh, kw, v;
-    __device__ void uniform() { kh = __builtin_amdgcn_readfirstlane(kh); kw = __builtin_amdgcn_readfirstlane(kw); v = __builtin_amdgcn_readfirstlane(v); }
-  };
+  struct KS { int kh, kw, v; };
   __device__ Ctx ctx(int) const { return Ctx{}; }
   __device__ int rows_a(const Ctx&) const { return M; }
   __device__ int ncols() const { return Cout; }
@@ -83,14 +81,6 @@ struct FwdProb {
   __device__ KS kstart(const Ctx&, int s) const {
     const int u = (int)fdiv((unsigned)s, dnp); KS k; k.v = 2 * (s - u * npair);
     k.kh = (int)fdiv((unsigned)u, dKW); k.kw = u - k.kh * KW; return k;
-  }
-  // advances k by one step when go (field-wise selects: no branch, no memory)
-  __device__ void knext(const Ctx&, KS& k, bool go) const {
-    const int v = k.v + 2;
-    const bool w1 = v >= ncb;
-    const int kw = k.kw + (w1 ? 1 : 0);
-    const bool w2 = kw == KW;
-    k.v = go ? (w1 ? 0 : v) : k.v; k.kw = go ? (w2 ? 0 : kw) : k.kw; k.kh += (go & w2) ? 1 : 0;
   }
   __device__ bool tail(const Ctx&, const KS& k) const { return k.v + 1 >= ncb; }
   __device__ PairDelta pd_a() const { return PairDelta{xRB, 1, 0, 0}; }
@@ -142,14 +132,12 @@ struct DgradProb {
   int ga, gb;                                // rows sharing one scale (A, B); 0: per-row scales
   int dybps;                                 // log2 of the gradient bp
   int khalf;                                 // every K-block holds at most 16 valid codes
-  FastDiv dN, dWc[8];                        // reciprocals of N and of each class's width (by pw_c)
+  FastDiv dN, dnp;                           // reciprocals of N and npair
+  FastDiv dWc[8], dNkw[8];                   // reciprocals of each class's width and tap columns (by pw_c)
   GridDivs grid;
   static constexpr bool kGeoA = true, kGeoB = false, kCanGroup = true;
   struct Ctx { int ph_c, pw_c, Hc, Wc, kh0, kw0, nkh, nkw, M; };
-  struct KS {
-    int ih, iw, v;
-    __device__ void uniform() { ih = __builtin_amdgcn_readfirstlane(ih); iw = __builtin_amdgcn_readfirstlane(iw); v = __builtin_amdgcn_readfirstlane(v); }
-  };
+  struct KS { int ih, iw, v; };
   __device__ Ctx ctx(int z) const {
     Ctx c; c.ph_c = z / sw; c.pw_c = z - c.ph_c * sw;
     c.Hc = H > c.ph_c ? (H - c.ph_c + sh - 1) / sh : 0;
@@ -164,15 +152,8 @@ struct DgradProb {
   __device__ int ncols() const { return Cin; }
   __device__ void steps(const Ctx& c, int, int& lo, int& hi) const { lo = 0; hi = c.nkh * c.nkw * npair; }
   __device__ KS kstart(const Ctx& c, int s) const {
-    const int nkw = c.nkw > 0 ? c.nkw : 1;
-    const int u = s / npair; KS k; k.v = 2 * (s - u * npair); k.ih = u / nkw; k.iw = u - k.ih * nkw; return k;
-  }
-  __device__ void knext(const Ctx& c, KS& k, bool go) const {
-    const int v = k.v + 2;
-    const bool w1 = v >= ncob;
-    const int iw = k.iw + (w1 ? 1 : 0);
-    const bool w2 = iw == c.nkw;
-    k.v = go ? (w1 ? 0 : v) : k.v; k.iw = go ? (w2 ? 0 : iw) : k.iw; k.ih += (go & w2) ? 1 : 0;
+    const int u = (int)fdiv((unsigned)s, dnp); KS k; k.v = 2 * (s - u * npair);
+    k.ih = (int)fdiv((unsigned)u, dNkw[c.pw_c]); k.iw = u - k.ih * c.nkw; return k;
   }
   __device__ bool tail(const Ctx&, const KS& k) const { return k.v + 1 >= ncob; }
   __device__ PairDelta pd_a() const { return PairDelta{dyRB, 1, 0, 0}; }
@@ -233,14 +214,12 @@ struct WgradProb {
   int xtcb, xsb;       // bias of the activation row offsets (padding)
   int ga, gb;          // rows sharing one scale (A, B); 0: per-row scales
   FastDiv dCin, dKW;   // reciprocals of Cin and KW
+  FastDiv dnsub, dWo;  // reciprocals of nsub and Wo
   int khalf;           // every K-block holds at most 16 valid codes (N <= 16)
   GridDivs grid;
   static constexpr bool kGeoA = false, kGeoB = true, kCanGroup = true;
   struct Ctx {};
-  struct KS {
-    int ho, wo, v;
-    __device__ void uniform() { ho = __builtin_amdgcn_readfirstlane(ho); wo = __builtin_amdgcn_readfirstlane(wo); v = __builtin_amdgcn_readfirstlane(v); }
-  };
+  struct KS { int ho, wo, v; };
   __device__ Ctx ctx(int) const { return Ctx{}; }
   __device__ int rows_a(const Ctx&) const { return Cout; }
   __device__ int ncols() const { return T * Cin; }
@@ -249,16 +228,10 @@ struct WgradProb {
   }
   __device__ KS kstart(const Ctx&, int s) const {
     KS k;
-    if (pair_w) { k.ho = s / nsub; k.wo = 2 * (s - k.ho * nsub); k.v = 0; }
-    else { const int pix = s / nsub; k.v = 2 * (s - pix * nsub); k.ho = pix / Wo; k.wo = pix - k.ho * Wo; }
+    const int u = (int)fdiv((unsigned)s, dnsub);
+    if (pair_w) { k.ho = u; k.wo = 2 * (s - u * nsub); k.v = 0; }
+    else { k.v = 2 * (s - u * nsub); k.ho = (int)fdiv((unsigned)u, dWo); k.wo = u - k.ho * Wo; }
     return k;
-  }
-  __device__ void knext(const Ctx&, KS& k, bool go) const {
-    const int v = k.v + (pair_w ? 0 : 2);
-    const bool wv = !pair_w & (v >= nNB);
-    const int wo = k.wo + (pair_w ? 2 : (wv ? 1 : 0));
-    const bool ww = pair_w ? (wo >= Wo) : (wo == Wo);
-    k.v = go ? (wv ? 0 : v) : k.v; k.wo = go ? (ww ? 0 : wo) : k.wo; k.ho += (go & ww) ? 1 : 0;
   }
   __device__ bool tail(const Ctx&, const KS& k) const { return pair_w ? k.wo + 1 >= Wo : k.v + 1 >= nNB; }
   __device__ PairDelta pd_a() const {
@@ -317,10 +290,7 @@ struct PlainProb {
   GridDivs grid;
   static constexpr bool kGeoA = false, kGeoB = false, kCanGroup = false;
   struct Ctx {};
-  struct KS {
-    int u;
-    __device__ void uniform() { u = __builtin_amdgcn_readfirstlane(u); }
-  };
+  struct KS { int u; };
   __device__ Ctx ctx(int) const { return Ctx{}; }
   __device__ int rows_a(const Ctx&) const { return Ma; }
   __device__ int ncols() const { return Nb; }
@@ -329,7 +299,6 @@ struct PlainProb {
     lo = min(np, z * pairs_per_split); hi = min(np, lo + pairs_per_split);
   }
   __device__ KS kstart(const Ctx&, int s) const { return KS{2 * s}; }
-  __device__ void knext(const Ctx&, KS& k, bool go) const { k.u += go ? 2 : 0; }
   __device__ bool tail(const Ctx&, const KS& k) const { return k.u + 1 >= nkb; }
   __device__ PairDelta pd_a() const { return PairDelta{aRB, 1, 0, 0}; }
   __device__ PairDelta pd_b() const { return PairDelta{bRB, 1, 0, 0}; }
@@ -420,13 +389,13 @@ __device__ __forceinline__ v8i lds_operand(const uint8_t* stage, int row, int sw
   return r;
 }
 
-// Operand image of an 8-bit row from a piece-major stage ([kb][piece][row]
-// 16-byte slots), used when only piece 0 of each run is loaded (K-blocks
-// with at most 16 valid codes; piece 1 holds zeros).
+// Operand image of an 8-bit row from a stage that holds only the first 16
+// codes of each run ([kb][row] 16-byte slots), for K-blocks with at most 16
+// valid codes: lanes of the upper half (q = 1) read a 16-byte zero slot.
 template <int BR>
-__device__ __forceinline__ v8i lds_operand_pm(const uint8_t* stage, int row, int q) {
-  const v4i lo = *reinterpret_cast<const v4i*>(stage + (q * BR + row) * 16);
-  const v4i hi = *reinterpret_cast<const v4i*>(stage + ((2 + q) * BR + row) * 16);
+__device__ __forceinline__ v8i lds_operand_half(const uint8_t* stage, const uint8_t* zero, int row, int q) {
+  const v4i lo = *reinterpret_cast<const v4i*>(q ? zero : stage + row * 16);
+  const v4i hi = *reinterpret_cast<const v4i*>(q ? zero : stage + (BR + row) * 16);
   v8i r = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return r;
 }
@@ -468,16 +437,16 @@ __device__ __forceinline__ void stage_barrier() {
 // one 64-lane load per operand fetches them: wave 0 the A scales, wave 1 the
 // B scales; waves 2 and 3 issue a zero-reading load to keep every wave's
 // load count equal.
-// KH: every K-block has at most 16 valid codes (8-bit formats only): the
-// stages are piece-major and only piece 0 of each run is loaded; piece 1 is
-// zeroed once.
+// KH: every K-block has at most 16 valid codes (8-bit formats only): a
+// stage holds only the first 16-byte piece of each run, which halves it, so
+// the ring can be deeper for the same LDS.
 template <int FA, int FB, class P, int WM, int WN, int TM, int TN, int NS, bool GS, bool KH>
 __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
   static_assert(!KH || (FA <= 1 && FB <= 1), "half K-blocks only for 8-bit codes");
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
   using OA = Op<FA>;
   using OB = Op<FB>;
-  constexpr int A_BYTES = 2 * BM * OA::NPK * 16, B_BYTES = 2 * BN * OB::NPK * 16;
+  constexpr int A_BYTES = 2 * BM * (KH ? 1 : OA::NPK) * 16, B_BYTES = 2 * BN * (KH ? 1 : OB::NPK) * 16;
   constexpr int SA_BYTES = GS ? 256 : 8 * BM, SB_BYTES = GS ? 256 : 8 * BN;
   constexpr int OFF_B = A_BYTES, OFF_SA = OFF_B + B_BYTES, OFF_SB = OFF_SA + SA_BYTES;
   constexpr int STAGE = OFF_SB + SB_BYTES;
@@ -490,8 +459,9 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
   constexpr int WPS = WCA + WCB + WSA + WSB;
   // 1 KB sink for the loads a wave issues only to keep its count uniform
   constexpr int DUMMY = NS * STAGE;
+  constexpr int ZERO = DUMMY + 1024;  // KH: 16 zero bytes for the empty upper pieces
   constexpr int STRIP = 32 * (TN * 32 + 8) * 4;  // one wave's epilogue strip (bytes)
-  constexpr int ARENA = (DUMMY + 1024) > 4 * STRIP ? (DUMMY + 1024) : 4 * STRIP;
+  constexpr int ARENA = (ZERO + 16) > 4 * STRIP ? (ZERO + 16) : 4 * STRIP;
   __shared__ __attribute__((aligned(16))) uint8_t arena[ARENA];
 
   const int tid = threadIdx.x;
@@ -585,11 +555,23 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
 
   int s_lo, s_hi;
   prob.steps(cx, z, s_lo, s_hi);
-  // The step state is uniform; readfirstlane keeps it in scalar registers
-  // (integer division by runtime values leaves it in vector ones, and a
-  // vector-held scalar offset would turn each load into a loop).
-  typename P::KS kit = prob.kstart(cx, s_lo);
-  kit.uniform();
+  // Step descriptors, 64 steps at a time: lane l of every wave holds those
+  // of step tb + l (its K-block offsets and flags), and a step reads its own
+  // into scalar registers with v_readlane. Steps past the last repeat it
+  // (their loads read zeros).
+  struct Tab { int ac, as, ag0, ag1, bc, bs, bg0, bg1, fl; };
+  auto fill = [&](int base) {
+    Tab t;
+    const int s = min(base + lane, max(s_hi - 1, s_lo));
+    const typename P::KS k = prob.kstart(cx, s);
+    const KInfo ka = prob.k_a(cx, k), kb = prob.k_b(cx, k);
+    t.ac = ka.code; t.as = ka.scale; t.ag0 = ka.g0; t.ag1 = ka.g1;
+    t.bc = kb.code; t.bs = kb.scale; t.bg0 = kb.g0; t.bg1 = kb.g1;
+    t.fl = (prob.tail(cx, k) ? 1 : 0) | (prob.step_interior_a(cx, k) ? 2 : 0) | (prob.step_interior_b(cx, k) ? 4 : 0);
+    return t;
+  };
+  Tab tab = fill(s_lo);
+  int tb = s_lo;
   int s_next = s_lo;
 
   // lane offset of a load at this step (branch-free): the border test is
@@ -606,26 +588,27 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
   // step read zeros, so every wave issues WPS loads per step.
   auto issue = [&](int st) {
     const bool live = s_next < s_hi;
-    const KInfo ka = prob.k_a(cx, kit), kb = prob.k_b(cx, kit);
-    const bool tl = prob.tail(cx, kit);
-    const bool inA = waveA || prob.step_interior_a(cx, kit);
-    const bool inB = waveB || prob.step_interior_b(cx, kit);
+    const int li = s_next - tb;
+    auto rl = [li](int v) { return __builtin_amdgcn_readlane(v, li); };
+    const KInfo ka{rl(tab.ac), rl(tab.as), P::kGeoA ? rl(tab.ag0) : 0, P::kGeoA ? rl(tab.ag1) : 0};
+    const KInfo kb{rl(tab.bc), rl(tab.bs), P::kGeoB ? rl(tab.bg0) : 0, P::kGeoB ? rl(tab.bg1) : 0};
+    const int fl = rl(tab.fl);
+    const bool tl = fl & 1;
+    const bool inA = waveA || (fl & 2);
+    const bool inB = waveB || (fl & 4);
     uint8_t* const stage = arena + st * STAGE;
 #pragma unroll
     for (int k = 0; k < WCA; k++) {
       const int g = wave + 4 * k;
       const int kbi = KH ? g * 64 >= BM : g * 64 >= BM * OA::NPK;
-      // KH: piece 0 of K-block kbi lands at slot (2*kbi)*BM + row
-      const int slot = KH ? g * 64 + kbi * BM : g * 64;
-      dma16(rs[0], g < NCA ? stage + slot * 16 : arena + DUMMY, voff(ca[k], ka, P::kGeoA, inA, la0, la1),
+      dma16(rs[0], g < NCA ? stage + g * 64 * 16 : arena + DUMMY, voff(ca[k], ka, P::kGeoA, inA, la0, la1),
             soff(ka.code, kbi, live, tl));
     }
 #pragma unroll
     for (int k = 0; k < WCB; k++) {
       const int g = wave + 4 * k;
       const int kbi = KH ? g * 64 >= BN : g * 64 >= BN * OB::NPK;
-      const int slot = KH ? g * 64 + kbi * BN : g * 64;
-      dma16(rs[2], g < NCB ? stage + OFF_B + slot * 16 : arena + DUMMY, voff(cb[k], kb, P::kGeoB, inB, lb0, lb1),
+      dma16(rs[2], g < NCB ? stage + OFF_B + g * 64 * 16 : arena + DUMMY, voff(cb[k], kb, P::kGeoB, inB, lb0, lb1),
             soff(kb.code, kbi, live, tl));
     }
     if constexpr (GS) {
@@ -649,8 +632,6 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
              soff(kb.scale, kbi, live, tl));
       }
     }
-    prob.knext(cx, kit, live);
-    kit.uniform();
     s_next++;
   };
 
@@ -671,14 +652,14 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
 #pragma unroll
     for (int i = 0; i < TM; i++) {
       const int row = (wm * TM + i) * 32 + r32;
-      if constexpr (KH) a[i] = lds_operand_pm<BM>(stage, row, q);
+      if constexpr (KH) a[i] = lds_operand_half<BM>(stage, arena + ZERO, row, q);
       else a[i] = lds_operand<FA, BM>(stage, row, swz, q);
       xa[i] = *reinterpret_cast<const int*>(stage + OFF_SA + (GS ? q * (BM / gsa) + row / gsa : q * BM + row) * 4);
     }
 #pragma unroll
     for (int j = 0; j < TN; j++) {
       const int row = (wn * TN + j) * 32 + r32;
-      if constexpr (KH) b[j] = lds_operand_pm<BN>(stage + OFF_B, row, q);
+      if constexpr (KH) b[j] = lds_operand_half<BN>(stage + OFF_B, arena + ZERO, row, q);
       else b[j] = lds_operand<FB, BN>(stage + OFF_B, row, swz, q);
       xb[j] = *reinterpret_cast<const int*>(stage + OFF_SB + (GS ? q * (BN / gsb) + row / gsb : q * BN + row) * 4);
     }
@@ -696,14 +677,11 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
   // stage s (every wave has waited for its own loads of step s) and retires
   // every wave's reads of stage s-1.
   const int nsteps = s_hi - s_lo;
-  if constexpr (KH) {  // piece 1 of every run in every stage is zero (never loaded)
-    const v4i zero = {0, 0, 0, 0};
-    for (int st = 0; st < NS; st++)
-      for (int i = tid; i < 2 * (BM + BN); i += 256) {
-        const int kb = i / (BM + BN), r = i - kb * (BM + BN);
-        uint8_t* base = arena + st * STAGE + (r < BM ? ((2 * kb + 1) * BM + r) * 16 : OFF_B + ((2 * kb + 1) * BN + r - BM) * 16);
-        *reinterpret_cast<v4i*>(base) = zero;
-      }
+  if constexpr (KH) {  // the zero slot; the first step's wait and barrier publish it
+    if (tid == 0) {
+      const v4i zero = {0, 0, 0, 0};
+      *reinterpret_cast<v4i*>(arena + ZERO) = zero;
+    }
   }
 #pragma unroll
   for (int i = 0; i < NS - 1; i++) issue(i);
@@ -713,21 +691,31 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
   constexpr int NDS = TM * (RDA + 1) + TN * (RDB + 1);
   constexpr int NMF = TM * TN;
   constexpr int VPM = (WPS + NMF - 1) / NMF;  // loads issued after each MFMA
-  for (int s = 0; s < nsteps; s++) {
-    wait_vm_lgkm0<(NS - 2) * WPS>();
-    stage_barrier();
-    read_operands(cs);
-    issue(cs == 0 ? NS - 1 : cs - 1);
-    mfmas();
-    // operand reads first, then the loads of the next stage spread between
-    // the MFMAs so their issue overlaps the matrix pipe
-    __builtin_amdgcn_sched_group_barrier(0x100, NDS, 0);
+  // Chunks of the table: iteration s issues step s_lo + s + NS - 1, which
+  // must lie in [tb, tb + 64); past that the table is refilled (outside the
+  // inner loop, whose body stays one block for the schedule below).
+  for (int s = 0; s < nsteps;) {
+    const int chunk_end = min(nsteps, tb - s_lo + 65 - NS);
+    for (; s < chunk_end; s++) {
+      wait_vm_lgkm0<(NS - 2) * WPS>();
+      stage_barrier();
+      read_operands(cs);
+      issue(cs == 0 ? NS - 1 : cs - 1);
+      mfmas();
+      // operand reads first, then the loads of the next stage spread between
+      // the MFMAs so their issue overlaps the matrix pipe
+      __builtin_amdgcn_sched_group_barrier(0x100, NDS, 0);
 #pragma unroll
-    for (int i = 0; i < NMF; i++) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, VPM, 0);
+      for (int i = 0; i < NMF; i++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, VPM, 0);
+      }
+      cs = cs + 1 == NS ? 0 : cs + 1;
     }
-    cs = cs + 1 == NS ? 0 : cs + 1;
+    if (s < nsteps) {
+      tab = fill(s_next);
+      tb = s_next;
+    }
   }
   wait_vm_lgkm0<0>();
   stage_barrier();
@@ -802,32 +790,39 @@ hipError_t launch_gemm(int fa, int fb, const P& prob, dim3 grid, hipStream_t st)
 //   1: 128 x 128  (2 x 2 waves of 64 x 64)
 //   2: 256 x 128  (2 x 2 waves of 128 x 64)
 //   3: 64 x 256   (1 x 4 waves of 64 x 64)   short outputs
+//   4: 64 x 192   (2 x 2 waves of 32 x 96)   short outputs of 3 x 64 columns
 struct TileChoice { int id, bm, bn; };
 inline TileChoice tile_shape(int id) {
   switch (id) {
     case 0: return {0, 256, 64};
     case 1: return {1, 128, 128};
     case 2: return {2, 256, 128};
+    case 4: return {4, 64, 192};
     default: return {3, 64, 256};
   }
 }
 // Picks the largest tile (fewest re-reads of the operands) that still gives
-// about one workgroup per compute unit.
+// about one workgroup per compute unit. Short outputs take the column width
+// that pads the columns least (576 = 9 taps x 64 channels fills three
+// 192-column tiles, but leaves a 256-column tile three quarters empty).
 inline TileChoice choose_tile(long long M, long long Ncols, long long Z) {
   if (Ncols <= 64) return tile_shape(0);
-  if (M <= 64) return tile_shape(3);
+  if (M <= 64) return ceil_div(Ncols, 192) * 192 < ceil_div(Ncols, 256) * 256 ? tile_shape(4) : tile_shape(3);
   const long long big = (long long)ceil_div(M, 256) * ceil_div(Ncols, 128) * Z;
   if (big >= 240) return tile_shape(2);
   return tile_shape(1);
 }
 
+// Stages in the ring (three: deeper rings measured slower).
 template <class P, bool GS, bool KH>
 hipError_t launch_tile_id(int id, int fa, int fb, const P& prob, dim3 grid, hipStream_t st) {
+  constexpr int NS = 3;
   switch (id) {
-    case 0: return launch_gemm<P, 4, 1, 2, 2, 3, GS, KH>(fa, fb, prob, grid, st);
-    case 1: return launch_gemm<P, 2, 2, 2, 2, 3, GS, KH>(fa, fb, prob, grid, st);
-    case 2: return launch_gemm<P, 2, 2, 4, 2, 3, GS, KH>(fa, fb, prob, grid, st);
-    default: return launch_gemm<P, 1, 4, 2, 2, 3, GS, KH>(fa, fb, prob, grid, st);
+    case 0: return launch_gemm<P, 4, 1, 2, 2, NS, GS, KH>(fa, fb, prob, grid, st);
+    case 1: return launch_gemm<P, 2, 2, 2, 2, NS, GS, KH>(fa, fb, prob, grid, st);
+    case 2: return launch_gemm<P, 2, 2, 4, 2, NS, GS, KH>(fa, fb, prob, grid, st);
+    case 4: return launch_gemm<P, 2, 2, 1, 3, NS, GS, KH>(fa, fb, prob, grid, st);
+    default: return launch_gemm<P, 1, 4, 2, 2, NS, GS, KH>(fa, fb, prob, grid, st);
   }
 }
 
@@ -841,6 +836,13 @@ inline int scale_group_rows(int bp, int partner) {
   return 0;
 }
 
+// The half-K-block kernel runs when both operands have grouped scales and
+// 8-bit codes, and every K-block holds at most 16 valid codes. Re-laid
+// operands then need only 16-byte runs.
+inline bool half_k_blocks(int ga, int gb, int khalf, int fa, int fb) {
+  return ga >= 8 && gb >= 8 && khalf && fa <= 1 && fb <= 1;
+}
+
 template <class P>
 hipError_t launch_tiled(int fa, int fb, const P& prob_in, int M, int Ncols, int Z, hipStream_t st) {
   const TileChoice t = choose_tile(M, Ncols, Z);
@@ -852,7 +854,8 @@ hipError_t launch_tiled(int fa, int fb, const P& prob_in, int M, int Ncols, int 
     // one 64-lane load holds both K-blocks' group scales of a 256-row tile
     // when groups have at least 8 rows
     if (prob.ga >= 8 && prob.gb >= 8) {
-      if (prob.khalf && fa <= 1 && fb <= 1) return launch_tile_id<P, true, true>(t.id, fa, fb, prob, grid, st);
+      if (half_k_blocks(prob.ga, prob.gb, prob.khalf, fa, fb))
+        return launch_tile_id<P, true, true>(t.id, fa, fb, prob, grid, st);
       return launch_tile_id<P, true, false>(t.id, fa, fb, prob, grid, st);
     }
   }

@@ -22,13 +22,29 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 #pragma unroll
   for (int e = 0; e < E; e++) s[e] = 0.0f;
   if (i0 < n) {
-    if constexpr (VEC) {
-      for (int z = g; z < splits; z += kRedG) {
-        const float4 a = *reinterpret_cast<const float4*>(part + (long long)z * n + i0);
-        s[0] += a.x; s[1] += a.y; s[2] += a.z; s[3] += a.w;
+    // U slices in flight per thread: their loads go out together, then they
+    // are added in slice order
+    constexpr int U = 4;
+    for (int z0 = g; z0 < splits; z0 += U * kRedG) {
+      float v[U][E];
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        const int z = z0 + u * kRedG;
+        if constexpr (VEC) {
+          typedef float v4f __attribute__((ext_vector_type(4)));
+          v4f a = {0.0f, 0.0f, 0.0f, 0.0f};
+          if (z < splits) a = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(part + (long long)z * n + i0));
+          v[u][0] = a[0]; v[u][1] = a[1]; v[u][2] = a[2]; v[u][3] = a[3];
+        } else {
+          v[u][0] = z < splits ? __builtin_nontemporal_load(part + (long long)z * n + i0) : 0.0f;
+        }
       }
-    } else {
-      for (int z = g; z < splits; z += kRedG) s[0] += part[(long long)z * n + i0];
+#pragma unroll
+      for (int u = 0; u < U; u++)
+        if (z0 + u * kRedG < splits) {
+#pragma unroll
+          for (int e = 0; e < E; e++) s[e] += v[u][e];
+        }
     }
   }
 #pragma unroll
@@ -98,17 +114,23 @@ hipError_t launch_backward_weight(const Conv& cv, MxView dy, MxView x, float* dw
   uint8_t* xt = base + dyt_b;
   const size_t xt_b = align256(transposed_bytes(x.fmt, (long long)cv.h * cv.w, cv.n, 1, cv.cin));
   float* part = reinterpret_cast<float*>(base + dyt_b + xt_b);
-  hipError_t e = launch_transpose_codes(dy.codes, dyt, dy.fmt, (int)npix_o, cv.n, 1, cv.cout, st);
+  WgradProb p;
+  // rows of A are Cout (32 to a block); rows of B are (tap, Cin), whose
+  // 32-channel blocks line up with 32-row groups when Cin is a multiple of 32
+  p.khalf = cv.n <= 16;
+  p.ga = 32;
+  p.gb = cv.cin % 32 == 0 ? 32 : 0;
+  const bool half = half_k_blocks(p.ga, p.gb, p.khalf, dy.fmt, x.fmt);
+  hipError_t e = launch_transpose_codes(dy.codes, dyt, dy.fmt, half, (int)npix_o, cv.n, 1, cv.cout, st);
   if (e != hipSuccess) return e;
-  e = launch_transpose_codes(x.codes, xt, x.fmt, cv.h * cv.w, cv.n, 1, cv.cin, st);
+  e = launch_transpose_codes(x.codes, xt, x.fmt, half, cv.h * cv.w, cv.n, 1, cv.cin, st);
   if (e != hipSuccess) return e;
   const int S = wgrad_splits(cv, dy.fmt, x.fmt);
-  WgradProb p;
   p.dytc = dyt; p.dys = dy.scales; p.xtc = xt; p.xs = x.scales; p.part = S > 1 ? part : dw;
   p.N = cv.n; p.H = cv.h; p.W = cv.w; p.Cin = cv.cin; p.Cout = cv.cout; p.KW = cv.kw;
   p.T = cv.kh * cv.kw; p.sh = cv.sh; p.sw = cv.sw; p.ph = cv.ph; p.pw = cv.pw; p.Ho = cv.ho(); p.Wo = cv.wo();
   p.nNB = ceil_div(cv.n, 32); p.ncob = ceil_div(cv.cout, 32); p.ncbi = ceil_div(cv.cin, 32);
-  p.dyRB = (int)run_bytes(dy.fmt); p.xRB = (int)run_bytes(x.fmt);
+  p.dyRB = half ? 16 : (int)run_bytes(dy.fmt); p.xRB = half ? 16 : (int)run_bytes(x.fmt);
   const WgradSteps ks = wgrad_steps(cv);
   p.pair_w = ks.pair_w; p.nsub = ks.nsub; p.total_steps = ks.total; p.steps_per_split = ceil_div(ks.total, S);
   p.dytc_bytes = npix_o * cv.cout * p.nNB * p.dyRB; p.dys_bytes = npix_o * p.nNB * p.ncob;
@@ -117,12 +139,8 @@ hipError_t launch_backward_weight(const Conv& cv, MxView dy, MxView x, float* dw
   const long long lead = (long long)cv.ph * cv.w + cv.pw;
   p.xtcb = (int)(lead * cv.cin * p.nNB * p.xRB); p.xsb = (int)(lead * p.nNB * p.ncbi);
   if (!offsets_fit(p.xtc_bytes, p.xtcb) || !offsets_fit(p.xs_bytes, p.xsb)) return hipErrorInvalidValue;
-  // rows of A are Cout (32 to a block); rows of B are (tap, Cin), whose
-  // 32-channel blocks line up with 32-row groups when Cin is a multiple of 32
   p.dCin = make_fastdiv(cv.cin); p.dKW = make_fastdiv(cv.kw);
-  p.khalf = cv.n <= 16;
-  p.ga = 32;
-  p.gb = cv.cin % 32 == 0 ? 32 : 0;
+  p.dnsub = make_fastdiv(ks.nsub); p.dWo = make_fastdiv(p.Wo);
   const long long nj = (long long)p.T * cv.cin;
   e = launch_tiled(dy.fmt, x.fmt, p, cv.cout, (int)nj, S, st);
   if (e != hipSuccess) return e;

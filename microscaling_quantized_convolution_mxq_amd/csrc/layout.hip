@@ -182,10 +182,12 @@ __global__ __launch_bounds__(256) void transpose_codes_kernel(const uint8_t* __r
 // group of 16 lanes, lanes 2i and 2i+1 address the two 8-byte halves of row
 // r0+i, and lane t receives rows r0..r0+7 of column t of the group. Four such
 // reads give every lane the 32 partner codes of one channel: one output run,
-// stored as 32 contiguous bytes (consecutive lanes, consecutive channels).
+// stored as RS contiguous bytes (consecutive lanes, consecutive channels):
+// 32, or 16 when P <= 16 (only the first 16 codes can be nonzero).
 __global__ __launch_bounds__(256) void transpose_codes8_kernel(const uint8_t* __restrict__ in,
                                                               uint8_t* __restrict__ out, int P, int B,
-                                                              int C, int nPB, int nCC, long long ntiles) {
+                                                              int C, int nPB, int nCC, long long ntiles,
+                                                              int RS) {
   constexpr int PITCH = 72;
   __shared__ __attribute__((aligned(16))) uint8_t lds[4][32 * PITCH];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -227,19 +229,20 @@ __global__ __launch_bounds__(256) void transpose_codes8_kernel(const uint8_t* __
   }
   const int c = c0 + lane;
   if (c < C) {
-    uint4* dst = reinterpret_cast<uint4*>(out + ((ab * C + c) * nPB + pb) * 32);
+    uint4* dst = reinterpret_cast<uint4*>(out + ((ab * C + c) * nPB + pb) * RS);
     dst[0] = make_uint4(run[0], run[1], run[2], run[3]);
-    dst[1] = make_uint4(run[4], run[5], run[6], run[7]);
+    if (RS == 32) dst[1] = make_uint4(run[4], run[5], run[6], run[7]);
   }
 }
 
-hipError_t launch_transpose_codes(const uint8_t* in, uint8_t* out, int fmt, int A, int P, int B,
+hipError_t launch_transpose_codes(const uint8_t* in, uint8_t* out, int fmt, bool half, int A, int P, int B,
                                   int C, hipStream_t st) {
+  if (half && (fmt > 1 || P > 16)) return hipErrorInvalidValue;
   if (fmt <= 1) {  // 8-bit codes
     const int nPB = ceil_div(P, 32), nCC = ceil_div(ceil_div(C, 32) * 32, 64);
     const long long ntiles = (long long)A * B * nPB * nCC;
     hipLaunchKernelGGL(transpose_codes8_kernel, dim3((unsigned)((ntiles + 3) / 4)), dim3(256), 0, st, in, out,
-                       P, B, C, nPB, nCC, ntiles);
+                       P, B, C, nPB, nCC, ntiles, half ? 16 : 32);
     return hipGetLastError();
   }
   const int nPB = ceil_div(P, 32);

@@ -54,8 +54,12 @@ hipError_t launch_cbf_im2col(const Conv& cv, MxView x, uint8_t* col_codes, uint8
 
 // Codes of a [A][P][B] x C tensor re-laid out so that runs of 32 codes run
 // along P: out[((a*B + b)*C + c)*nPB*RB + pb*RB ...] (zeros for p >= P).
-hipError_t launch_transpose_codes(const uint8_t* in, uint8_t* out, int fmt, int A, int P, int B,
+// half: 8-bit codes with P <= 16 stored as 16-byte runs (the upper 16 codes
+// of a 32-code run would all be zero)
+hipError_t launch_transpose_codes(const uint8_t* in, uint8_t* out, int fmt, bool half, int A, int P, int B,
                                   int C, hipStream_t st);
+// Workspace bytes of a re-laid tensor (runs along the partner index P). The
+// 16-byte runs of the half-block case fit in the same space.
 inline size_t transposed_bytes(int fmt, long long A, long long P, long long B, long long C) {
   return (size_t)(A * B * C * ((P + 31) / 32) * run_bytes(fmt));
 }
