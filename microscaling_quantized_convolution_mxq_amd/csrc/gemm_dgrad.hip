@@ -11,9 +11,14 @@ hipError_t launch_backward_data(const Conv& cv, MxView dy, MxView w, float* dx, 
   p.khalf = cv.cout <= 16;
   p.ga = scale_group_rows(dy.bp, cv.n);
   p.gb = 32;
-  const bool half = half_k_blocks(p.ga, p.gb, p.khalf, dy.fmt, w.fmt);
-  hipError_t e = launch_transpose_codes(w.codes, wt, w.fmt, half, 1, cv.cout, cv.kh * cv.kw, cv.cin, st);
-  if (e != hipSuccess) return e;
+  // 8-bit weight codes are read where quantization left them (K-major
+  // staging); other formats are first re-laid with runs along Cout
+  const bool natural = w.fmt <= 1;
+  const bool half = !natural && half_k_blocks(p.ga, p.gb, p.khalf, dy.fmt, w.fmt);
+  if (!natural) {
+    hipError_t e = launch_transpose_codes(w.codes, wt, w.fmt, half, 1, cv.cout, cv.kh * cv.kw, cv.cin, st);
+    if (e != hipSuccess) return e;
+  }
   p.dyc = dy.codes; p.dys = dy.scales; p.wtc = wt; p.ws = w.scales; p.dx = dx;
   p.N = cv.n; p.H = cv.h; p.W = cv.w; p.Cin = cv.cin; p.Cout = cv.cout; p.KH = cv.kh; p.KW = cv.kw;
   p.sh = cv.sh; p.sw = cv.sw; p.ph = cv.ph; p.pw = cv.pw; p.Ho = cv.ho(); p.Wo = cv.wo();
@@ -38,6 +43,14 @@ hipError_t launch_backward_data(const Conv& cv, MxView dy, MxView w, float* dx, 
     p.dNkw[c] = make_fastdiv((unsigned)(nkw > 0 ? nkw : 1));
   }
   const int maxHc = ceil_div(cv.h, cv.sh), maxWc = ceil_div(cv.w, cv.sw);
+  if (natural) {
+    DgradNatProb q;
+    static_cast<DgradProb&>(q) = p;
+    q.khalf = 0;
+    q.T = (int)T; q.wrb = (int)row_bytes(w.fmt, cv.cin);
+    q.wtc = w.codes; q.wtc_bytes = (long long)cv.cout * T * q.wrb;
+    return launch_tiled(dy.fmt, w.fmt, q, maxHc * maxWc * cv.n, cv.cin, cv.sh * cv.sw, st);
+  }
   return launch_tiled(dy.fmt, w.fmt, p, maxHc * maxWc * cv.n, cv.cin, cv.sh * cv.sw, st);
 }
 

@@ -19,6 +19,8 @@
 // step s+NS-1 are in flight while the MFMAs of step s run, with one
 // workgroup barrier per step.
 #pragma once
+#include <type_traits>
+
 #include "mx_common.h"
 #include "mqconv_internal.h"
 
@@ -72,6 +74,7 @@ struct FwdProb {
   FastDiv dN, dWo, dKW, dnp;             // reciprocals of N, Wo, KW, npair
   GridDivs grid;
   static constexpr bool kGeoA = true, kGeoB = false, kCanGroup = true;
+  static constexpr bool kKMajA = false, kKMajB = false;
   struct Ctx {};
   struct KS { int kh, kw, v; };
   __device__ Ctx ctx(int) const { return Ctx{}; }
@@ -136,6 +139,7 @@ struct DgradProb {
   FastDiv dWc[8], dNkw[8];                   // reciprocals of each class's width and tap columns (by pw_c)
   GridDivs grid;
   static constexpr bool kGeoA = true, kGeoB = false, kCanGroup = true;
+  static constexpr bool kKMajA = false, kKMajB = false;
   struct Ctx { int ph_c, pw_c, Hc, Wc, kh0, kw0, nkh, nkw, M; };
   struct KS { int ih, iw, v; };
   __device__ Ctx ctx(int z) const {
@@ -218,6 +222,7 @@ struct WgradProb {
   int khalf;           // every K-block holds at most 16 valid codes (N <= 16)
   GridDivs grid;
   static constexpr bool kGeoA = false, kGeoB = true, kCanGroup = true;
+  static constexpr bool kKMajA = false, kKMajB = false;
   struct Ctx {};
   struct KS { int ho, wo, v; };
   __device__ Ctx ctx(int) const { return Ctx{}; }
@@ -289,6 +294,7 @@ struct PlainProb {
   int ga = 0, gb = 0;
   GridDivs grid;
   static constexpr bool kGeoA = false, kGeoB = false, kCanGroup = false;
+  static constexpr bool kKMajA = false, kKMajB = false;
   struct Ctx {};
   struct KS { int u; };
   __device__ Ctx ctx(int) const { return Ctx{}; }
@@ -322,6 +328,69 @@ struct PlainProb {
   __device__ bool step_interior_b(const Ctx&, const KS&) const { return true; }
   __device__ float* out_row(const Ctx&, int z, int m) const {
     return m < Ma ? out + ((long long)z * Ma + m) * Nb : nullptr;
+  }
+};
+
+// Backward-data reading the weight codes where quantization left them
+// ([Cout][Kh][Kw][Cin], runs along Cin): the B operand (rows ci, K = co of
+// one tap) is staged K-major, one line of Cin codes per co. wtc, wtc_bytes
+// and wRB are unused; wrb is the weight row bytes (Cin padded to 32).
+// Lines past Cout lie past the end of the buffer and read zeros.
+struct DgradNatProb : DgradProb {
+  int T, wrb;
+  static constexpr bool kKMajA = false, kKMajB = true;
+  __device__ int kext_b() const { return 32; }
+  __device__ int kstride_b() const { return T * wrb; }
+  __device__ PairDelta pd_b() const { return PairDelta{32 * T * wrb, ncbi, 0, 0}; }
+  __device__ RowInfo row_b(const Ctx&, int c) const {
+    RowInfo r; r.ok = c < Cin; const int cc = r.ok ? c : 0;
+    r.code = cc; r.scale = cc / 32; r.p0 = 0; r.p1 = 0; return r;
+  }
+  __device__ KInfo k_b(const Ctx& c, const KS& k) const {
+    const int tap = (c.kh0 + sh * k.ih) * KW + (c.kw0 + sw * k.iw);
+    return KInfo{(32 * k.v * T + tap) * wrb, (tap * ncob + k.v) * ncbi, 0, 0};
+  }
+};
+
+// Backward-weight reading the gradient and activation codes where
+// quantization left them ([H][W][N][C], runs along C): both operands (rows
+// co, and j = (kh, kw, ci)) are staged K-major, one line of channel codes
+// per n. dytc / xtc point at the natural codes with dyrb / xrb row bytes;
+// dyRB and xRB are unused. Needs Cin % 16 == 0 (a 16-row chunk of B stays in
+// one tap) and N <= 32 or N % 32 == 0 (a K-block's lines are N values of one
+// pixel; lines past N, when N < 32, read zeros).
+struct WgradNatProb : WgradProb {
+  int dyrb, xrb;
+  static constexpr bool kKMajA = true, kKMajB = true;
+  __device__ int kext_a() const { return N < 32 ? N : 32; }
+  __device__ int kext_b() const { return N < 32 ? N : 32; }
+  __device__ int kstride_a() const { return dyrb; }
+  __device__ int kstride_b() const { return xrb; }
+  __device__ PairDelta pd_a() const {
+    return pair_w ? PairDelta{N * dyrb, nNB * ncob, 0, 0} : PairDelta{32 * dyrb, ncob, 0, 0};
+  }
+  __device__ PairDelta pd_b() const {
+    return pair_w ? PairDelta{sw * N * xrb, sw * nNB * ncbi, 0, sw} : PairDelta{32 * xrb, ncbi, 0, 0};
+  }
+  __device__ RowInfo row_a(const Ctx&, int m) const {
+    RowInfo r; r.ok = m < Cout; const int co = r.ok ? m : 0;
+    r.code = co; r.scale = co / 32; r.p0 = 0; r.p1 = 0; return r;
+  }
+  __device__ KInfo k_a(const Ctx&, const KS& k) const {
+    const int pix = k.ho * Wo + k.wo;
+    return KInfo{(pix * N + 32 * k.v) * dyrb, (pix * nNB + k.v) * ncob, 0, 0};
+  }
+  __device__ RowInfo row_b(const Ctx&, int j) const {
+    RowInfo r; r.ok = j < T * Cin; const int jj = r.ok ? j : 0;
+    const int tap = (int)fdiv((unsigned)jj, dCin), ci = jj - tap * Cin;
+    const int kh = (int)fdiv((unsigned)tap, dKW), kw = tap - kh * KW;
+    r.p0 = kh - ph; r.p1 = kw - pw;
+    const int p = r.p0 * W + r.p1;
+    r.code = p * N * xrb + ci + xtcb; r.scale = p * nNB * ncbi + ci / 32 + xsb; return r;
+  }
+  __device__ KInfo k_b(const Ctx&, const KS& k) const {
+    const int g0 = k.ho * sh, g1 = k.wo * sw, d = g0 * W + g1;
+    return KInfo{(d * N + 32 * k.v) * xrb, (d * nNB + k.v) * ncbi, g0, g1};
   }
 };
 
@@ -400,6 +469,36 @@ __device__ __forceinline__ v8i lds_operand_half(const uint8_t* stage, const uint
   return r;
 }
 
+// K-major stage of an 8-bit operand with BR rows: [kb][k][BR] bytes, one
+// line of BR codes per K index k (the operand's rows side by side, as they
+// lie in memory when the contraction runs along the partner or the tap
+// dimension). Its 16-byte chunks are permuted within each aligned group of
+// four by kswz(k), so that the transposing reads below hit distinct banks.
+__device__ __forceinline__ int kswz(int k) { return (k >> 1) & 3; }
+// Operand image of rows r0..r0+31 from a K-major stage with ds_read_b64_tr_b8:
+// in each 16-lane group, lanes 2i and 2i+1 address the two halves of the
+// 16-byte chunk of line k0+i that holds the group's 16 rows, and lane t
+// receives lines k0..k0+7 of row t. Lane (r, q) gets K indices 16q..16q+15
+// of both K-blocks: four such reads.
+template <int BR>
+__device__ __forceinline__ v8i lds_operand_k(const uint8_t* stage, int r0, int lane) {
+  typedef v2i __attribute__((address_space(3)))* lds_v2i_ptr;
+  const int g = lane >> 4, t = lane & 15, q = g >> 1;
+  const int chunk = (r0 >> 4) + (g & 1);
+  // k = 16q + 8h + t/2, so kswz(k) = (t >> 2) & 3 for every read
+  const uint8_t* base = stage + (16 * q + (t >> 1)) * BR + 16 * (chunk ^ ((t >> 2) & 3)) + 8 * (t & 1);
+  v8i r;
+#pragma unroll
+  for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+      const v2i x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_ptr)(base + (kb * 32 + 8 * h) * BR));
+      r[4 * kb + 2 * h] = x[0];
+      r[4 * kb + 2 * h + 1] = x[1];
+    }
+  return r;
+}
+
 // Per-lane part of one LDS-writing load: byte offset of the lane's piece
 // relative to the step's uniform offset (kOOB when the row is outside the
 // problem or the load only keeps the count uniform) and the row's border
@@ -443,6 +542,10 @@ __device__ __forceinline__ void stage_barrier() {
 template <int FA, int FB, class P, int WM, int WN, int TM, int TN, int NS, bool GS, bool KH>
 __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
   static_assert(!KH || (FA <= 1 && FB <= 1), "half K-blocks only for 8-bit codes");
+  // K-major operands (8-bit codes, full runs): the staging order of the
+  // contraction's natural layout, read back with transposing LDS reads
+  constexpr bool TA = P::kKMajA, TB = P::kKMajB;
+  static_assert((!TA || (FA <= 1 && !KH)) && (!TB || (FB <= 1 && !KH)), "K-major staging: 8-bit codes");
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
   using OA = Op<FA>;
   using OB = Op<FB>;
@@ -514,12 +617,45 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
     inner = inner & (!ok | ((l.p0 + gr.min0 >= 0) & (l.p0 + gr.max0 < L0) & (l.p1 + gr.min1 >= 0) &
                             (l.p1 + gr.max1 < L1)));
   };
+  // K-major: slot t of the operand's stage holds K-block kb = t / (2 BR),
+  // line k and chunk c (rows 16c..16c+15), the chunk permuted by kswz(k);
+  // lines past the operand's K extent read zeros
+  auto make_lane_k = [&](LaneLd& l, int g, int ngl, auto BRc, auto IsA, bool& inner, const auto& pr) {
+    constexpr int BR = decltype(BRc)::value, CPR = BR / 16;
+    constexpr bool is_a = decltype(IsA)::value;
+    const bool real = g < ngl;
+    const int t = real ? 64 * g + lane : 0;
+    const int kb = t / (2 * BR), u = t - kb * 2 * BR;
+    const int k = u / CPR, chunk = (u - k * CPR) ^ kswz(k);
+    const PairDelta& d = is_a ? dA : dB;
+    RowInfo r;
+    int kext, ks;
+    if constexpr (is_a) {
+      r = pr.row_a(cx, m0 + 16 * chunk); kext = pr.kext_a(); ks = pr.kstride_a();
+    } else {
+      r = pr.row_b(cx, n0 + 16 * chunk); kext = pr.kext_b(); ks = pr.kstride_b();
+    }
+    const bool ok = r.ok & real & (k < kext);
+    l.off = ok ? r.code + k * ks + kb * d.code : kOOB;
+    l.p0 = r.p0 + kb * d.g0;
+    l.p1 = r.p1 + kb * d.g1;
+    const GRange& gr = is_a ? gA : gB;
+    const int L0 = is_a ? la0 : lb0, L1 = is_a ? la1 : lb1;
+    inner = inner & (!ok | ((l.p0 + gr.min0 >= 0) & (l.p0 + gr.max0 < L0) & (l.p1 + gr.min1 >= 0) &
+                            (l.p1 + gr.max1 < L1)));
+  };
 #pragma unroll
-  for (int k = 0; k < WCA; k++)
-    make_lane(ca[k], wave + 4 * k, NCA, BM * (KH ? 1 : OA::NPK), KH ? 1 : OA::NPK, OA::CH, true, true, innerA);
+  for (int k = 0; k < WCA; k++) {
+    if constexpr (TA)
+      make_lane_k(ca[k], wave + 4 * k, NCA, std::integral_constant<int, BM>{}, std::true_type{}, innerA, prob);
+    else make_lane(ca[k], wave + 4 * k, NCA, BM * (KH ? 1 : OA::NPK), KH ? 1 : OA::NPK, OA::CH, true, true, innerA);
+  }
 #pragma unroll
-  for (int k = 0; k < WCB; k++)
-    make_lane(cb[k], wave + 4 * k, NCB, BN * (KH ? 1 : OB::NPK), KH ? 1 : OB::NPK, OB::CH, true, false, innerB);
+  for (int k = 0; k < WCB; k++) {
+    if constexpr (TB)
+      make_lane_k(cb[k], wave + 4 * k, NCB, std::integral_constant<int, BN>{}, std::false_type{}, innerB, prob);
+    else make_lane(cb[k], wave + 4 * k, NCB, BN * (KH ? 1 : OB::NPK), KH ? 1 : OB::NPK, OB::CH, true, false, innerB);
+  }
   // grouped scales: lane e of wave 0 (A) or wave 1 (B) loads the scale of
   // group e % ngroups of K-block e / ngroups (e < 2 * ngroups)
   const int gsa = GS ? prob.ga : 1, gsb = GS ? prob.gb : 1;
@@ -652,14 +788,16 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
 #pragma unroll
     for (int i = 0; i < TM; i++) {
       const int row = (wm * TM + i) * 32 + r32;
-      if constexpr (KH) a[i] = lds_operand_half<BM>(stage, arena + ZERO, row, q);
+      if constexpr (TA) a[i] = lds_operand_k<BM>(stage, (wm * TM + i) * 32, lane);
+      else if constexpr (KH) a[i] = lds_operand_half<BM>(stage, arena + ZERO, row, q);
       else a[i] = lds_operand<FA, BM>(stage, row, swz, q);
       xa[i] = *reinterpret_cast<const int*>(stage + OFF_SA + (GS ? q * (BM / gsa) + row / gsa : q * BM + row) * 4);
     }
 #pragma unroll
     for (int j = 0; j < TN; j++) {
       const int row = (wn * TN + j) * 32 + r32;
-      if constexpr (KH) b[j] = lds_operand_half<BN>(stage + OFF_B, arena + ZERO, row, q);
+      if constexpr (TB) b[j] = lds_operand_k<BN>(stage + OFF_B, (wn * TN + j) * 32, lane);
+      else if constexpr (KH) b[j] = lds_operand_half<BN>(stage + OFF_B, arena + ZERO, row, q);
       else b[j] = lds_operand<FB, BN>(stage + OFF_B, row, swz, q);
       xb[j] = *reinterpret_cast<const int*>(stage + OFF_SB + (GS ? q * (BN / gsb) + row / gsb : q * BN + row) * 4);
     }
@@ -687,7 +825,7 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
   for (int i = 0; i < NS - 1; i++) issue(i);
   int cs = 0;
   // LDS reads per step of a wave, for the instruction schedule below
-  constexpr int RDA = F_READS<FA>(), RDB = F_READS<FB>();
+  constexpr int RDA = TA ? 4 : F_READS<FA>(), RDB = TB ? 4 : F_READS<FB>();
   constexpr int NDS = TM * (RDA + 1) + TN * (RDB + 1);
   constexpr int NMF = TM * TN;
   constexpr int VPM = (WPS + NMF - 1) / NMF;  // loads issued after each MFMA
@@ -771,8 +909,12 @@ hipError_t launch_gemm(int fa, int fb, const P& prob, dim3 grid, hipStream_t st)
     hipLaunchKernelGGL((mx_gemm_kernel<A, B, P, WM, WN, TM, TN, NS, GS, KH>), grid, dim3(256), 0, st, prob);  \
     return hipGetLastError();                                                                                 \
   }
-  if constexpr (KH) {
+  if constexpr (KH || (P::kKMajA && P::kKMajB)) {
     MQ_CASE(0, 0) MQ_CASE(0, 1) MQ_CASE(1, 0) MQ_CASE(1, 1)
+    return hipErrorInvalidValue;
+  } else if constexpr (P::kKMajB) {
+    MQ_CASE(0, 0) MQ_CASE(0, 1) MQ_CASE(1, 0) MQ_CASE(1, 1) MQ_CASE(2, 0) MQ_CASE(2, 1)
+    MQ_CASE(3, 0) MQ_CASE(3, 1) MQ_CASE(4, 0) MQ_CASE(4, 1)
     return hipErrorInvalidValue;
   } else {
   MQ_CASE(0, 0) MQ_CASE(0, 1) MQ_CASE(0, 2) MQ_CASE(0, 3) MQ_CASE(0, 4)
@@ -854,8 +996,10 @@ hipError_t launch_tiled(int fa, int fb, const P& prob_in, int M, int Ncols, int 
     // one 64-lane load holds both K-blocks' group scales of a 256-row tile
     // when groups have at least 8 rows
     if (prob.ga >= 8 && prob.gb >= 8) {
-      if (half_k_blocks(prob.ga, prob.gb, prob.khalf, fa, fb))
-        return launch_tile_id<P, true, true>(t.id, fa, fb, prob, grid, st);
+      if constexpr (!P::kKMajA && !P::kKMajB) {
+        if (half_k_blocks(prob.ga, prob.gb, prob.khalf, fa, fb))
+          return launch_tile_id<P, true, true>(t.id, fa, fb, prob, grid, st);
+      }
       return launch_tile_id<P, true, false>(t.id, fa, fb, prob, grid, st);
     }
   }

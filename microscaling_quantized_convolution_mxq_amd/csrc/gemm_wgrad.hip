@@ -120,11 +120,19 @@ hipError_t launch_backward_weight(const Conv& cv, MxView dy, MxView x, float* dw
   p.khalf = cv.n <= 16;
   p.ga = 32;
   p.gb = cv.cin % 32 == 0 ? 32 : 0;
-  const bool half = half_k_blocks(p.ga, p.gb, p.khalf, dy.fmt, x.fmt);
-  hipError_t e = launch_transpose_codes(dy.codes, dyt, dy.fmt, half, (int)npix_o, cv.n, 1, cv.cout, st);
-  if (e != hipSuccess) return e;
-  e = launch_transpose_codes(x.codes, xt, x.fmt, half, cv.h * cv.w, cv.n, 1, cv.cin, st);
-  if (e != hipSuccess) return e;
+  // 8-bit codes are read where quantization left them (K-major staging)
+  // when a 16-channel chunk of B stays in one tap and a K-block's lines are
+  // the N values of one pixel; otherwise both are first re-laid with runs
+  // along N
+  const bool natural = dy.fmt <= 1 && x.fmt <= 1 && cv.cin % 16 == 0 && (cv.n <= 32 || cv.n % 32 == 0);
+  const bool half = !natural && half_k_blocks(p.ga, p.gb, p.khalf, dy.fmt, x.fmt);
+  hipError_t e = hipSuccess;
+  if (!natural) {
+    e = launch_transpose_codes(dy.codes, dyt, dy.fmt, half, (int)npix_o, cv.n, 1, cv.cout, st);
+    if (e != hipSuccess) return e;
+    e = launch_transpose_codes(x.codes, xt, x.fmt, half, cv.h * cv.w, cv.n, 1, cv.cin, st);
+    if (e != hipSuccess) return e;
+  }
   const int S = wgrad_splits(cv, dy.fmt, x.fmt);
   p.dytc = dyt; p.dys = dy.scales; p.xtc = xt; p.xs = x.scales; p.part = S > 1 ? part : dw;
   p.N = cv.n; p.H = cv.h; p.W = cv.w; p.Cin = cv.cin; p.Cout = cv.cout; p.KW = cv.kw;
@@ -142,7 +150,19 @@ hipError_t launch_backward_weight(const Conv& cv, MxView dy, MxView x, float* dw
   p.dCin = make_fastdiv(cv.cin); p.dKW = make_fastdiv(cv.kw);
   p.dnsub = make_fastdiv(ks.nsub); p.dWo = make_fastdiv(p.Wo);
   const long long nj = (long long)p.T * cv.cin;
-  e = launch_tiled(dy.fmt, x.fmt, p, cv.cout, (int)nj, S, st);
+  if (natural) {
+    WgradNatProb q;
+    static_cast<WgradProb&>(q) = p;
+    q.khalf = 0;
+    q.dyrb = (int)row_bytes(dy.fmt, cv.cout); q.xrb = (int)row_bytes(x.fmt, cv.cin);
+    q.dytc = dy.codes; q.dytc_bytes = npix_o * cv.n * q.dyrb;
+    q.xtc = x.codes; q.xtc_bytes = (long long)cv.h * cv.w * cv.n * q.xrb;
+    q.xtcb = (int)(lead * cv.n * q.xrb);
+    if (!offsets_fit(q.xtc_bytes, q.xtcb)) return hipErrorInvalidValue;
+    e = launch_tiled(dy.fmt, x.fmt, q, cv.cout, (int)nj, S, st);
+  } else {
+    e = launch_tiled(dy.fmt, x.fmt, p, cv.cout, (int)nj, S, st);
+  }
   if (e != hipSuccess) return e;
   if (S > 1) {
     const long long n = (long long)cv.cout * nj;

@@ -87,6 +87,30 @@ def test_gemm_small_shapes(label, shape, fmts):
     _compare_full(shape, x, w, dy, *fmts, 32, ("fwd", "dgrad", "wgrad"), label)
 
 
+# 8-bit codes read in their quantized layout (K-major staging with
+# transposing LDS reads): backward-data whenever W is 8-bit, backward-weight
+# when dY and X are 8-bit, Cin % 16 == 0 and N <= 32 or N % 32 == 0
+NATURAL = [
+    # N = 32 (one K-block per pixel), Cin = 48 (per-row B scales), Cout = 40
+    ("n32_s2", ConvShape(32, 48, 9, 11, 40, 3, 3, 2, 1), (0, 0, 1)),
+    # N = 64: K-blocks paired along N; Cout = 24 < 32 (short K-blocks in dgrad)
+    ("n64", ConvShape(64, 32, 6, 7, 24, 3, 3, 1, 1), (1, 1, 0)),
+    # N = 5: lines past N read zeros; one tap is one 16-channel chunk
+    ("n5_pad2", ConvShape(5, 16, 8, 9, 48, 5, 3, 1, 2), (0, 1, 1)),
+    # 128-row tiles (Cout = 160) and a 256-column backward-data tile (Cin = 256)
+    ("cout160", ConvShape(8, 32, 7, 6, 160, 3, 3, 1, 1), (1, 0, 1)),
+    ("cin256", ConvShape(2, 256, 4, 4, 32, 3, 3, 1, 1), (0, 0, 1)),
+    # 1x1 stride 2, N = 16
+    ("1x1s2_n16", ConvShape(16, 64, 10, 9, 32, 1, 1, 2, 0), (0, 0, 1)),
+]
+
+
+@pytest.mark.parametrize("label,shape,fmts", NATURAL, ids=[s[0] for s in NATURAL])
+def test_gemm_natural_layout_shapes(label, shape, fmts):
+    x, w, dy = _inputs(shape, 17)
+    _compare_full(shape, x, w, dy, *fmts, 32, ("fwd", "dgrad", "wgrad"), "natural " + label)
+
+
 @pytest.mark.parametrize("fx", range(5))
 @pytest.mark.parametrize("fw", range(5))
 def test_gemm_format_matrix(fx, fw):
