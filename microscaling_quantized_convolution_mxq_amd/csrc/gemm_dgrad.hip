@@ -46,7 +46,6 @@ hipError_t launch_backward_data(const Conv& cv, MxView dy, MxView w, float* dx, 
   if (natural) {
     DgradNatProb q;
     static_cast<DgradProb&>(q) = p;
-    q.khalf = 0;
     q.T = (int)T; q.wrb = (int)row_bytes(w.fmt, cv.cin);
     q.wtc = w.codes; q.wtc_bytes = (long long)cv.cout * T * q.wrb;
     return launch_tiled(dy.fmt, w.fmt, q, maxHc * maxWc * cv.n, cv.cin, cv.sh * cv.sw, st);

@@ -479,11 +479,16 @@ __device__ __forceinline__ int kswz(int k) { return (k >> 1) & 3; }
 // in each 16-lane group, lanes 2i and 2i+1 address the two halves of the
 // 16-byte chunk of line k0+i that holds the group's 16 rows, and lane t
 // receives lines k0..k0+7 of row t. Lane (r, q) gets K indices 16q..16q+15
-// of both K-blocks: four such reads.
-template <int BR>
+// of both K-blocks: four such reads. HALF: the stage holds 16 lines per
+// K-block (K-blocks of at most 16 values); the upper lanes (q = 1) repeat the
+// lower lanes' reads, and with ZQ1 their image is then zeroed. A product of
+// the upper K halves vanishes when one of the two operands is zero there
+// (codes are always finite), so only one operand needs ZQ1.
+template <int BR, bool HALF, bool ZQ1>
 __device__ __forceinline__ v8i lds_operand_k(const uint8_t* stage, int r0, int lane) {
   typedef v2i __attribute__((address_space(3)))* lds_v2i_ptr;
-  const int g = lane >> 4, t = lane & 15, q = g >> 1;
+  constexpr int KL = HALF ? 16 : 32;  // lines per K-block
+  const int g = lane >> 4, t = lane & 15, q = HALF ? 0 : g >> 1;
   const int chunk = (r0 >> 4) + (g & 1);
   // k = 16q + 8h + t/2, so kswz(k) = (t >> 2) & 3 for every read
   const uint8_t* base = stage + (16 * q + (t >> 1)) * BR + 16 * (chunk ^ ((t >> 2) & 3)) + 8 * (t & 1);
@@ -492,10 +497,15 @@ __device__ __forceinline__ v8i lds_operand_k(const uint8_t* stage, int r0, int l
   for (int kb = 0; kb < 2; kb++)
 #pragma unroll
     for (int h = 0; h < 2; h++) {
-      const v2i x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_ptr)(base + (kb * 32 + 8 * h) * BR));
+      const v2i x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_ptr)(base + (kb * KL + 8 * h) * BR));
       r[4 * kb + 2 * h] = x[0];
       r[4 * kb + 2 * h + 1] = x[1];
     }
+  if constexpr (HALF && ZQ1) {
+    const bool upper = lane >= 32;
+#pragma unroll
+    for (int e = 0; e < 8; e++) r[e] = upper ? 0 : r[e];
+  }
   return r;
 }
 
@@ -545,7 +555,7 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
   // K-major operands (8-bit codes, full runs): the staging order of the
   // contraction's natural layout, read back with transposing LDS reads
   constexpr bool TA = P::kKMajA, TB = P::kKMajB;
-  static_assert((!TA || (FA <= 1 && !KH)) && (!TB || (FB <= 1 && !KH)), "K-major staging: 8-bit codes");
+  static_assert((!TA || FA <= 1) && (!TB || FB <= 1), "K-major staging: 8-bit codes");
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
   using OA = Op<FA>;
   using OB = Op<FB>;
@@ -617,15 +627,16 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
     inner = inner & (!ok | ((l.p0 + gr.min0 >= 0) & (l.p0 + gr.max0 < L0) & (l.p1 + gr.min1 >= 0) &
                             (l.p1 + gr.max1 < L1)));
   };
-  // K-major: slot t of the operand's stage holds K-block kb = t / (2 BR),
+  // K-major: slot t of the operand's stage holds K-block kb = t / (KL BR / 16),
   // line k and chunk c (rows 16c..16c+15), the chunk permuted by kswz(k);
-  // lines past the operand's K extent read zeros
+  // KL = 32 lines per K-block (16 with KH); lines past the operand's K
+  // extent read zeros
   auto make_lane_k = [&](LaneLd& l, int g, int ngl, auto BRc, auto IsA, bool& inner, const auto& pr) {
-    constexpr int BR = decltype(BRc)::value, CPR = BR / 16;
+    constexpr int BR = decltype(BRc)::value, CPR = BR / 16, KBS = (KH ? 16 : 32) * CPR;
     constexpr bool is_a = decltype(IsA)::value;
     const bool real = g < ngl;
     const int t = real ? 64 * g + lane : 0;
-    const int kb = t / (2 * BR), u = t - kb * 2 * BR;
+    const int kb = t / KBS, u = t - kb * KBS;
     const int k = u / CPR, chunk = (u - k * CPR) ^ kswz(k);
     const PairDelta& d = is_a ? dA : dB;
     RowInfo r;
@@ -788,7 +799,7 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
 #pragma unroll
     for (int i = 0; i < TM; i++) {
       const int row = (wm * TM + i) * 32 + r32;
-      if constexpr (TA) a[i] = lds_operand_k<BM>(stage, (wm * TM + i) * 32, lane);
+      if constexpr (TA) a[i] = lds_operand_k<BM, KH, true>(stage, (wm * TM + i) * 32, lane);
       else if constexpr (KH) a[i] = lds_operand_half<BM>(stage, arena + ZERO, row, q);
       else a[i] = lds_operand<FA, BM>(stage, row, swz, q);
       xa[i] = *reinterpret_cast<const int*>(stage + OFF_SA + (GS ? q * (BM / gsa) + row / gsa : q * BM + row) * 4);
@@ -796,7 +807,9 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
 #pragma unroll
     for (int j = 0; j < TN; j++) {
       const int row = (wn * TN + j) * 32 + r32;
-      if constexpr (TB) b[j] = lds_operand_k<BN>(stage + OFF_B, (wn * TN + j) * 32, lane);
+      // (with KH the other operand's upper lanes are zero: a K-major A is
+      // zeroed above, a row-major A reads the zero slot)
+      if constexpr (TB) b[j] = lds_operand_k<BN, KH, false>(stage + OFF_B, (wn * TN + j) * 32, lane);
       else if constexpr (KH) b[j] = lds_operand_half<BN>(stage + OFF_B, arena + ZERO, row, q);
       else b[j] = lds_operand<FB, BN>(stage + OFF_B, row, swz, q);
       xb[j] = *reinterpret_cast<const int*>(stage + OFF_SB + (GS ? q * (BN / gsb) + row / gsb : q * BN + row) * 4);
@@ -996,10 +1009,8 @@ hipError_t launch_tiled(int fa, int fb, const P& prob_in, int M, int Ncols, int 
     // one 64-lane load holds both K-blocks' group scales of a 256-row tile
     // when groups have at least 8 rows
     if (prob.ga >= 8 && prob.gb >= 8) {
-      if constexpr (!P::kKMajA && !P::kKMajB) {
-        if (half_k_blocks(prob.ga, prob.gb, prob.khalf, fa, fb))
-          return launch_tile_id<P, true, true>(t.id, fa, fb, prob, grid, st);
-      }
+      if (half_k_blocks(prob.ga, prob.gb, prob.khalf, fa, fb))
+        return launch_tile_id<P, true, true>(t.id, fa, fb, prob, grid, st);
       return launch_tile_id<P, true, false>(t.id, fa, fb, prob, grid, st);
     }
   }

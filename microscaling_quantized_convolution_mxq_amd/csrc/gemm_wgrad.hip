@@ -153,7 +153,6 @@ hipError_t launch_backward_weight(const Conv& cv, MxView dy, MxView x, float* dw
   if (natural) {
     WgradNatProb q;
     static_cast<WgradProb&>(q) = p;
-    q.khalf = 0;
     q.dyrb = (int)row_bytes(dy.fmt, cv.cout); q.xrb = (int)row_bytes(x.fmt, cv.cin);
     q.dytc = dy.codes; q.dytc_bytes = npix_o * cv.n * q.dyrb;
     q.xtc = x.codes; q.xtc_bytes = (long long)cv.h * cv.w * cv.n * q.xrb;
