@@ -1,11 +1,16 @@
 """HBM traffic of the quantize-once path and of the naive path, from rocprofv3
 counters.
 
-Three modes:
+Modes:
   step       run one training step of a workload (every layer for the YOLOv8n
              backbone) through one path, so that rocprofv3 --pmc can count it
+  call       quantize the inputs, then run one entry point once (its own
+             kernels are the dispatches that are not quantize kernels)
   copy       run a plain device-to-device copy of known size (calibration)
-  summarize  read the counter CSVs of those runs and write a summary
+  summarize  read the counter CSVs of the step runs and write a summary
+  summarize-call
+             read the counter CSVs of a call run and write the HBM bytes of
+             one call of that entry point (profiles/traffic_<workload>_<call>.json)
 
 Counter passes (one counter group per run, as rocprofv3 requires), e.g. for
 the 3x3 YOLOv8n-style layer:
@@ -74,6 +79,46 @@ def run_step(workload: str, path: str) -> None:
             mq.mqconv_naive_backward_weight(s, DY, X, wl.fdy, wl.fx, dw, ws[2])
         torch.cuda.synchronize()
         print(f"step {path} {wl.name}", flush=True)
+
+
+CALL_NAMES = ("cbf_im2col", "forward", "backward_data", "backward_weight")
+
+
+def run_call(workload: str, call: str) -> None:
+    import torch
+    import microscaling_quantized_convolution_mxq_amd as mq
+    from microscaling_quantized_convolution_mxq_amd.workloads import draw_inputs
+
+    wl = WORKLOADS_ONE(workload)
+    s = wl.shape
+    x, w, dy = draw_inputs(wl)
+    X, Wt, DY = (torch.from_numpy(a).cuda() for a in (x, w, dy))
+    xq = mq.MxTensor.empty(mq.ROLE_ACT, wl.fx, wl.bp, x.shape)
+    wq = mq.MxTensor.empty(mq.ROLE_WEIGHT, wl.fw, wl.bp, w.shape)
+    gq = mq.MxTensor.empty(mq.ROLE_GRAD, wl.fdy, wl.bp, dy.shape)
+    mq.mqconv_quantize(X, xq)
+    mq.mqconv_quantize(Wt, wq)
+    mq.mqconv_quantize(DY, gq)
+    torch.cuda.synchronize()
+    if call == "cbf_im2col":
+        cc = torch.empty(mq.mqconv_im2col_codes_bytes(s, wl.fx), dtype=torch.uint8, device="cuda")
+        cs = torch.empty(mq.mqconv_im2col_scales_bytes(s, wl.bp), dtype=torch.uint8, device="cuda")
+        mq.mqconv_cbf_im2col(s, xq, cc, cs)
+    elif call == "forward":
+        mq.mqconv_forward(s, xq, wq, torch.empty((s.ho, s.wo, s.n, s.cout), device="cuda"))
+    elif call == "backward_data":
+        ws = torch.empty(max(1, mq.mqconv_workspace_bytes(s, 1, wl.fdy, wl.fw)), dtype=torch.uint8, device="cuda")
+        mq.mqconv_backward_data(s, gq, wq, torch.empty(x.shape, device="cuda"), ws)
+    else:
+        ws = torch.empty(max(1, mq.mqconv_workspace_bytes(s, 2, wl.fdy, wl.fx)), dtype=torch.uint8, device="cuda")
+        mq.mqconv_backward_weight(s, gq, xq, torch.empty(w.shape, device="cuda"), ws)
+    torch.cuda.synchronize()
+    print(f"call {call} {wl.name}", flush=True)
+
+
+def WORKLOADS_ONE(name):
+    from microscaling_quantized_convolution_mxq_amd.workloads import WORKLOADS
+    return WORKLOADS[name]
 
 
 def run_copy() -> None:
@@ -151,13 +196,50 @@ def summarize(d: str, workload: str, out_dir: str) -> dict:
     return res
 
 
+def summarize_call(d: str, workload: str, call: str, out_dir: str, command: str) -> dict:
+    """HBM bytes of one call: FETCH_SIZE and WRITE_SIZE of its own dispatches
+    (every mq:: dispatch of the call run except the quantize kernels of the
+    prelude), each divided by the copy's factor."""
+    copy_bytes = COPY_MB * (1 << 20)
+    f_fetch = max(v for k, v in _read(d, "copy_fetch", "FETCH_SIZE") if "mq::" not in k) / copy_bytes
+    f_write = max(v for k, v in _read(d, "copy_write", "WRITE_SIZE") if "mq::" not in k) / copy_bytes
+    own = lambda k: "mq::" in k and "mxq_quantize_kernel" not in k
+    fe = [(k, v / f_fetch) for k, v in _read(d, "call_fetch", "FETCH_SIZE") if own(k)]
+    wr = [(k, v / f_write) for k, v in _read(d, "call_write", "WRITE_SIZE") if own(k)]
+    per = {}
+    for k, v in fe:
+        per.setdefault(k.split("(")[0].replace("void ", ""), [0.0, 0.0])[0] += v
+    for k, v in wr:
+        per.setdefault(k.split("(")[0].replace("void ", ""), [0.0, 0.0])[1] += v
+    tf, tw = sum(v for _, v in fe), sum(v for _, v in wr)
+    wl = WORKLOADS_ONE(workload)
+    rec = {"workload": wl.name, "call": call, "dispatches": len(fe), "fetch_bytes": tf, "write_bytes": tw,
+           "traffic_bytes": tf + tw, "fetch_factor": round(f_fetch, 4), "write_factor": round(f_write, 4),
+           "copy_MiB": COPY_MB, "kernels": {k: {"fetch": v[0], "write": v[1]} for k, v in per.items()},
+           "source_sha": _source_sha(), "command": command}
+    os.makedirs(out_dir, exist_ok=True)
+    with open(os.path.join(out_dir, f"traffic_{wl.name}_{call}.json"), "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec, indent=1))
+    return rec
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="mode", required=True)
     a = sub.add_parser("step")
     a.add_argument("--workload", default="c2")
     a.add_argument("--path", choices=("microqonv", "naive"), default="microqonv")
+    b = sub.add_parser("call")
+    b.add_argument("--workload", default="c2")
+    b.add_argument("--call", choices=CALL_NAMES, default="backward_weight")
     sub.add_parser("copy")
+    e = sub.add_parser("summarize-call")
+    e.add_argument("--dir", required=True)
+    e.add_argument("--workload", default="c2")
+    e.add_argument("--call", choices=CALL_NAMES, default="backward_weight")
+    e.add_argument("--out", default=os.path.join(ROOT, "profiles"))
+    e.add_argument("--command", default="")
     c = sub.add_parser("summarize")
     c.add_argument("--dir", required=True)
     c.add_argument("--workload", default="c2")
@@ -165,8 +247,12 @@ def main(argv=None):
     args = ap.parse_args(argv)
     if args.mode == "step":
         run_step(args.workload, args.path)
+    elif args.mode == "call":
+        run_call(args.workload, args.call)
     elif args.mode == "copy":
         run_copy()
+    elif args.mode == "summarize-call":
+        summarize_call(args.dir, args.workload, args.call, args.out, args.command)
     else:
         summarize(args.dir, args.workload, args.out)
 
