@@ -42,9 +42,10 @@ CALL_KERNELS = {
     "quantize_x": ["mxq_quantize_kernel"], "quantize_w": ["mxq_quantize_kernel"],
     "quantize_dy": ["mxq_quantize_kernel"], "cbf_im2col": ["cbf_im2col_kernel"],
     "forward": ["mx_gemm_kernel<FwdProb>"],
-    "backward_data": ["transpose_codes_kernel (W)", "mx_gemm_kernel<DgradProb>"],
-    "backward_weight": ["transpose_codes_kernel (dY)", "transpose_codes_kernel (X)",
-                        "mx_gemm_kernel<WgradProb>", "splitk_reduce_kernel (when split)"],
+    # 8-bit codes are read in place; other formats are first re-laid by transpose_codes_kernel
+    "backward_data": ["mx_gemm_kernel<DgradNatProb> (8-bit W; else transpose_codes_kernel + mx_gemm_kernel<DgradProb>)"],
+    "backward_weight": ["mx_gemm_kernel<WgradNatProb> (8-bit dY, X; else 2 x transpose_codes_kernel + "
+                        "mx_gemm_kernel<WgradProb>)", "splitk_reduce_kernel (when split)"],
 }
 
 
