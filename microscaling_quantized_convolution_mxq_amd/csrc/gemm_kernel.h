@@ -75,6 +75,7 @@ struct FwdProb {
   GridDivs grid;
   static constexpr bool kGeoA = true, kGeoB = false, kCanGroup = true;
   static constexpr bool kKMajA = false, kKMajB = false;
+  static constexpr bool kQuad = false;
   struct Ctx {};
   struct KS { int kh, kw, v; };
   __device__ Ctx ctx(int) const { return Ctx{}; }
@@ -85,7 +86,7 @@ struct FwdProb {
     const int u = (int)fdiv((unsigned)s, dnp); KS k; k.v = 2 * (s - u * npair);
     k.kh = (int)fdiv((unsigned)u, dKW); k.kw = u - k.kh * KW; return k;
   }
-  __device__ bool tail(const Ctx&, const KS& k) const { return k.v + 1 >= ncb; }
+  __device__ int nvalid(const Ctx&, const KS& k) const { return k.v + 1 >= ncb ? 1 : 2; }
   __device__ PairDelta pd_a() const { return PairDelta{xRB, 1, 0, 0}; }
   __device__ PairDelta pd_b() const { return PairDelta{wRB, 1, 0, 0}; }
   __device__ RowInfo row_a(const Ctx&, int m) const {
@@ -140,6 +141,7 @@ struct DgradProb {
   GridDivs grid;
   static constexpr bool kGeoA = true, kGeoB = false, kCanGroup = true;
   static constexpr bool kKMajA = false, kKMajB = false;
+  static constexpr bool kQuad = false;
   struct Ctx { int ph_c, pw_c, Hc, Wc, kh0, kw0, nkh, nkw, M; };
   struct KS { int ih, iw, v; };
   __device__ Ctx ctx(int z) const {
@@ -159,7 +161,7 @@ struct DgradProb {
     const int u = (int)fdiv((unsigned)s, dnp); KS k; k.v = 2 * (s - u * npair);
     k.ih = (int)fdiv((unsigned)u, dNkw[c.pw_c]); k.iw = u - k.ih * c.nkw; return k;
   }
-  __device__ bool tail(const Ctx&, const KS& k) const { return k.v + 1 >= ncob; }
+  __device__ int nvalid(const Ctx&, const KS& k) const { return k.v + 1 >= ncob ? 1 : 2; }
   __device__ PairDelta pd_a() const { return PairDelta{dyRB, 1, 0, 0}; }
   __device__ PairDelta pd_b() const { return PairDelta{wRB, ncbi, 0, 0}; }
   __device__ RowInfo row_a(const Ctx& c, int m) const {
@@ -203,18 +205,20 @@ struct DgradProb {
 };
 
 // Backward-weight on codes re-laid with runs along N: rows co (A) and
-// j = (kh, kw, ci) (B); K-block (ho, wo, nb). A step pairs N blocks (nb,
-// nb+1) of one output pixel, or, when N fits one block, the output pixels
-// (ho, wo) and (ho, wo+1). Slice z covers steps [z*steps_per_split, ...).
+// j = (kh, kw, ci) (B); K-block (ho, wo, nb). A step takes kps N blocks
+// (nb .. nb+kps-1) of one output pixel, or, when N fits one block, the
+// output pixels (ho, wo) .. (ho, wo+kps-1); the last step of a pixel or row
+// takes fewer. Slice z covers steps [z*steps_per_split, ...).
 struct WgradProb {
   const uint8_t *dytc, *dys, *xtc, *xs;
   float* part;
   long long dytc_bytes, dys_bytes, xtc_bytes, xs_bytes;
   int N, H, W, Cin, Cout, KW, T, sh, sw, ph, pw, Ho, Wo, nNB, ncob, ncbi;
   int dyRB, xRB;
-  int pair_w;          // 1: pairs along wo (nNB == 1), 0: pairs along nb
-  int nsub;            // pairs per pixel (pair_w 0) or per output row (pair_w 1)
+  int pair_w;          // 1: steps along wo (nNB == 1), 0: steps along nb
+  int nsub;            // steps per pixel (pair_w 0) or per output row (pair_w 1)
   int total_steps, steps_per_split;
+  int kps;             // K-blocks per step: 4 with half K-blocks, else 2
   int xtcb, xsb;       // bias of the activation row offsets (padding)
   int ga, gb;          // rows sharing one scale (A, B); 0: per-row scales
   FastDiv dCin, dKW;   // reciprocals of Cin and KW
@@ -223,6 +227,7 @@ struct WgradProb {
   GridDivs grid;
   static constexpr bool kGeoA = false, kGeoB = true, kCanGroup = true;
   static constexpr bool kKMajA = false, kKMajB = false;
+  static constexpr bool kQuad = true;  // four K-blocks per step with half K-blocks
   struct Ctx {};
   struct KS { int ho, wo, v; };
   __device__ Ctx ctx(int) const { return Ctx{}; }
@@ -234,11 +239,11 @@ struct WgradProb {
   __device__ KS kstart(const Ctx&, int s) const {
     KS k;
     const int u = (int)fdiv((unsigned)s, dnsub);
-    if (pair_w) { k.ho = u; k.wo = 2 * (s - u * nsub); k.v = 0; }
-    else { k.v = 2 * (s - u * nsub); k.ho = (int)fdiv((unsigned)u, dWo); k.wo = u - k.ho * Wo; }
+    if (pair_w) { k.ho = u; k.wo = kps * (s - u * nsub); k.v = 0; }
+    else { k.v = kps * (s - u * nsub); k.ho = (int)fdiv((unsigned)u, dWo); k.wo = u - k.ho * Wo; }
     return k;
   }
-  __device__ bool tail(const Ctx&, const KS& k) const { return pair_w ? k.wo + 1 >= Wo : k.v + 1 >= nNB; }
+  __device__ int nvalid(const Ctx&, const KS& k) const { return min(kps, pair_w ? Wo - k.wo : nNB - k.v); }
   __device__ PairDelta pd_a() const {
     return pair_w ? PairDelta{Cout * nNB * dyRB, nNB * ncob, 0, 0} : PairDelta{dyRB, ncob, 0, 0};
   }
@@ -272,9 +277,9 @@ struct WgradProb {
   __device__ GRange g_range_a(const Ctx&) const { return GRange{0, 0, 0, 0}; }
   __device__ GRange g_range_b(const Ctx&) const { return GRange{0, (Ho - 1) * sh, 0, (Wo - 1) * sw}; }
   __device__ bool step_interior_a(const Ctx&, const KS&) const { return true; }
-  // every tap of every row in range for this step (both pixels of a pair)
+  // every tap of every row in range for this step (all its pixels along wo)
   __device__ bool step_interior_b(const Ctx&, const KS& k) const {
-    const int h0 = k.ho * sh - ph, w0 = k.wo * sw - pw, w1 = w0 + (pair_w ? sw : 0);
+    const int h0 = k.ho * sh - ph, w0 = k.wo * sw - pw, w1 = w0 + (pair_w ? (kps - 1) * sw : 0);
     return (h0 >= 0) & (h0 + T / KW - 1 < H) & (w0 >= 0) & (w1 + KW - 1 < W);
   }
   __device__ float* out_row(const Ctx&, int z, int m) const {
@@ -295,6 +300,7 @@ struct PlainProb {
   GridDivs grid;
   static constexpr bool kGeoA = false, kGeoB = false, kCanGroup = false;
   static constexpr bool kKMajA = false, kKMajB = false;
+  static constexpr bool kQuad = false;
   struct Ctx {};
   struct KS { int u; };
   __device__ Ctx ctx(int) const { return Ctx{}; }
@@ -305,7 +311,7 @@ struct PlainProb {
     lo = min(np, z * pairs_per_split); hi = min(np, lo + pairs_per_split);
   }
   __device__ KS kstart(const Ctx&, int s) const { return KS{2 * s}; }
-  __device__ bool tail(const Ctx&, const KS& k) const { return k.u + 1 >= nkb; }
+  __device__ int nvalid(const Ctx&, const KS& k) const { return k.u + 1 >= nkb ? 1 : 2; }
   __device__ PairDelta pd_a() const { return PairDelta{aRB, 1, 0, 0}; }
   __device__ PairDelta pd_b() const { return PairDelta{bRB, 1, 0, 0}; }
   __device__ RowInfo row_a(const Ctx&, int m) const {
@@ -549,7 +555,7 @@ __device__ __forceinline__ void stage_barrier() {
 // KH: every K-block has at most 16 valid codes (8-bit formats only): a
 // stage holds only the first 16-byte piece of each run, which halves it, so
 // the ring can be deeper for the same LDS.
-template <int FA, int FB, class P, int WM, int WN, int TM, int TN, int NS, bool GS, bool KH>
+template <int FA, int FB, class P, int WM, int WN, int TM, int TN, int NS, bool GS, bool KH, int KPS>
 __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
   static_assert(!KH || (FA <= 1 && FB <= 1), "half K-blocks only for 8-bit codes");
   // K-major operands (8-bit codes, full runs): the staging order of the
@@ -559,14 +565,16 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
   using OA = Op<FA>;
   using OB = Op<FB>;
-  constexpr int A_BYTES = 2 * BM * (KH ? 1 : OA::NPK) * 16, B_BYTES = 2 * BN * (KH ? 1 : OB::NPK) * 16;
-  constexpr int SA_BYTES = GS ? 256 : 8 * BM, SB_BYTES = GS ? 256 : 8 * BN;
+  // KPS: K-blocks per step (a pair, or two pairs)
+  static_assert(KPS == 2 || KPS == 4, "K-blocks per step");
+  constexpr int A_BYTES = KPS * BM * (KH ? 1 : OA::NPK) * 16, B_BYTES = KPS * BN * (KH ? 1 : OB::NPK) * 16;
+  constexpr int SA_BYTES = GS ? 256 : 4 * KPS * BM, SB_BYTES = GS ? 256 : 4 * KPS * BN;
   constexpr int OFF_B = A_BYTES, OFF_SA = OFF_B + B_BYTES, OFF_SB = OFF_SA + SA_BYTES;
   constexpr int STAGE = OFF_SB + SB_BYTES;
   // LDS-writing loads (64 lanes each) per stage and per wave; load g of a
   // kind belongs to K-block g / (loads per K-block)
-  constexpr int NCA = 2 * BM * (KH ? 1 : OA::NPK) / 64, NCB = 2 * BN * (KH ? 1 : OB::NPK) / 64;
-  constexpr int NSA = GS ? 1 : 2 * BM / 64, NSB = GS ? 1 : 2 * BN / 64;
+  constexpr int NCA = KPS * BM * (KH ? 1 : OA::NPK) / 64, NCB = KPS * BN * (KH ? 1 : OB::NPK) / 64;
+  constexpr int NSA = GS ? 1 : KPS * BM / 64, NSB = GS ? 1 : KPS * BN / 64;
   constexpr int WCA = (NCA + 3) / 4, WCB = (NCB + 3) / 4;
   constexpr int WSA = GS ? 1 : (NSA + 3) / 4, WSB = GS ? 0 : (NSB + 3) / 4;
   constexpr int WPS = WCA + WCB + WSA + WSB;
@@ -668,14 +676,14 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
     else make_lane(cb[k], wave + 4 * k, NCB, BN * (KH ? 1 : OB::NPK), KH ? 1 : OB::NPK, OB::CH, true, false, innerB);
   }
   // grouped scales: lane e of wave 0 (A) or wave 1 (B) loads the scale of
-  // group e % ngroups of K-block e / ngroups (e < 2 * ngroups)
+  // group e % ngroups of K-block e / ngroups (e < KPS * ngroups <= 64)
   const int gsa = GS ? prob.ga : 1, gsb = GS ? prob.gb : 1;
-  bool second_s = false;
+  int s_kb = 0;  // K-block of this lane's grouped-scale load
   if constexpr (GS) {
     const bool isA = wave == 0, isB = wave == 1;
     const int rows = isA ? BM : BN, grp = isA ? gsa : gsb;
     const int ng = rows / grp;
-    const bool real = (isA | isB) & (lane < 2 * ng);
+    const bool real = (isA | isB) & (lane < KPS * ng);
     const int kb = real ? lane / ng : 0, row = real ? (lane - kb * ng) * grp : 0;
     const PairDelta& d = isA ? dA : dB;
     const RowInfo r = isA ? prob.row_a(cx, m0 + row) : prob.row_b(cx, n0 + row);
@@ -683,7 +691,7 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
     sa[0].off = ok ? r.scale + kb * d.scale : kOOB;
     sa[0].p0 = r.p0 + kb * d.g0;
     sa[0].p1 = r.p1 + kb * d.g1;
-    second_s = kb != 0;
+    s_kb = kb;
     const GRange& gr = isA ? gA : gB;
     const int L0 = isA ? la0 : lb0, L1 = isA ? la1 : lb1;
     const bool inner = !ok | ((sa[0].p0 + gr.min0 >= 0) & (sa[0].p0 + gr.max0 < L0) & (sa[0].p1 + gr.min1 >= 0) &
@@ -714,7 +722,7 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
     const KInfo ka = prob.k_a(cx, k), kb = prob.k_b(cx, k);
     t.ac = ka.code; t.as = ka.scale; t.ag0 = ka.g0; t.ag1 = ka.g1;
     t.bc = kb.code; t.bs = kb.scale; t.bg0 = kb.g0; t.bg1 = kb.g1;
-    t.fl = (prob.tail(cx, k) ? 1 : 0) | (prob.step_interior_a(cx, k) ? 2 : 0) | (prob.step_interior_b(cx, k) ? 4 : 0);
+    t.fl = prob.nvalid(cx, k) | (prob.step_interior_a(cx, k) ? 8 : 0) | (prob.step_interior_b(cx, k) ? 16 : 0);
     return t;
   };
   Tab tab = fill(s_lo);
@@ -728,8 +736,9 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
     const bool ok = inside | (((unsigned)(l.p0 + k.g0) < (unsigned)L0) & ((unsigned)(l.p1 + k.g1) < (unsigned)L1));
     return ok ? l.off : kOOB;
   };
-  // uniform offset of a load of K-block kb at this step (kOOB: the load reads zeros)
-  auto soff = [](int kofs, int kb, bool live, bool tl) { return (live & !(kb & tl)) ? kofs : kOOB; };
+  // uniform offset of a load of K-block kb at this step (kOOB: the load reads
+  // zeros); nv = valid K-blocks of the step
+  auto soff = [](int kofs, int kb, bool live, int nv) { return (live & (kb < nv)) ? kofs : kOOB; };
 
   // Issue the loads of the next step into stage `st`. Loads past the last
   // step read zeros, so every wave issues WPS loads per step.
@@ -740,43 +749,43 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
     const KInfo ka{rl(tab.ac), rl(tab.as), P::kGeoA ? rl(tab.ag0) : 0, P::kGeoA ? rl(tab.ag1) : 0};
     const KInfo kb{rl(tab.bc), rl(tab.bs), P::kGeoB ? rl(tab.bg0) : 0, P::kGeoB ? rl(tab.bg1) : 0};
     const int fl = rl(tab.fl);
-    const bool tl = fl & 1;
-    const bool inA = waveA || (fl & 2);
-    const bool inB = waveB || (fl & 4);
+    const int nv = fl & 7;
+    const bool inA = waveA || (fl & 8);
+    const bool inB = waveB || (fl & 16);
     uint8_t* const stage = arena + st * STAGE;
 #pragma unroll
     for (int k = 0; k < WCA; k++) {
       const int g = wave + 4 * k;
-      const int kbi = KH ? g * 64 >= BM : g * 64 >= BM * OA::NPK;
+      const int kbi = (g * 64) / (BM * (KH ? 1 : OA::NPK));
       dma16(rs[0], g < NCA ? stage + g * 64 * 16 : arena + DUMMY, voff(ca[k], ka, P::kGeoA, inA, la0, la1),
-            soff(ka.code, kbi, live, tl));
+            soff(ka.code, kbi, live, nv));
     }
 #pragma unroll
     for (int k = 0; k < WCB; k++) {
       const int g = wave + 4 * k;
-      const int kbi = KH ? g * 64 >= BN : g * 64 >= BN * OB::NPK;
+      const int kbi = (g * 64) / (BN * (KH ? 1 : OB::NPK));
       dma16(rs[2], g < NCB ? stage + OFF_B + g * 64 * 16 : arena + DUMMY, voff(cb[k], kb, P::kGeoB, inB, lb0, lb1),
-            soff(kb.code, kbi, live, tl));
+            soff(kb.code, kbi, live, nv));
     }
     if constexpr (GS) {
       // wave 0: A scales, wave 1: B scales, waves 2-3: zero-reading filler
       const bool isA = wave == 0;
       const int v = isA ? voff(sa[0], ka, P::kGeoA, inA, la0, la1) : voff(sa[0], kb, P::kGeoB, inB, lb0, lb1);
-      const int vt = (second_s & tl) ? kOOB : v;
+      const int vt = s_kb < nv ? v : kOOB;
       dma1(isA ? rs[1] : rs[3], wave == 0 ? stage + OFF_SA : (wave == 1 ? stage + OFF_SB : arena + DUMMY), vt,
            live ? (isA ? ka.scale : kb.scale) : kOOB);
     } else {
 #pragma unroll
       for (int k = 0; k < WSA; k++) {
-        const int g = wave + 4 * k, kbi = g * 64 >= BM;
+        const int g = wave + 4 * k, kbi = (g * 64) / BM;
         dma1(rs[1], g < NSA ? stage + OFF_SA + g * 256 : arena + DUMMY, voff(sa[k], ka, P::kGeoA, inA, la0, la1),
-             soff(ka.scale, kbi, live, tl));
+             soff(ka.scale, kbi, live, nv));
       }
 #pragma unroll
       for (int k = 0; k < WSB; k++) {
-        const int g = wave + 4 * k, kbi = g * 64 >= BN;
+        const int g = wave + 4 * k, kbi = (g * 64) / BN;
         dma1(rs[3], g < NSB ? stage + OFF_SB + g * 256 : arena + DUMMY, voff(sb[k], kb, P::kGeoB, inB, lb0, lb1),
-             soff(kb.scale, kbi, live, tl));
+             soff(kb.scale, kbi, live, nv));
       }
     }
     s_next++;
@@ -792,35 +801,47 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
 
   const int r32 = lane & 31, q = lane >> 5;
   const int swz = slot_swz(r32);  // tile rows start at multiples of 32
-  v8i a[TM], b[TN];
-  int xa[TM], xb[TN];
+  // operand images and scales of the step's KPS / 2 pairs of K-blocks; pair
+  // p starts 2 K-blocks (KBA / KBB bytes each) into the operand's stage
+  constexpr int NP = KPS / 2;
+  constexpr int KBA = BM * (KH ? 1 : OA::NPK) * 16, KBB = BN * (KH ? 1 : OB::NPK) * 16;
+  v8i a[NP][TM], b[NP][TN];
+  int xa[NP][TM], xb[NP][TN];
   auto read_operands = [&](int st) {
     const uint8_t* const stage = arena + st * STAGE;
 #pragma unroll
-    for (int i = 0; i < TM; i++) {
-      const int row = (wm * TM + i) * 32 + r32;
-      if constexpr (TA) a[i] = lds_operand_k<BM, KH, true>(stage, (wm * TM + i) * 32, lane);
-      else if constexpr (KH) a[i] = lds_operand_half<BM>(stage, arena + ZERO, row, q);
-      else a[i] = lds_operand<FA, BM>(stage, row, swz, q);
-      xa[i] = *reinterpret_cast<const int*>(stage + OFF_SA + (GS ? q * (BM / gsa) + row / gsa : q * BM + row) * 4);
-    }
+    for (int p = 0; p < NP; p++) {
+      const uint8_t* const sA = stage + p * 2 * KBA;
+      const uint8_t* const sB = stage + OFF_B + p * 2 * KBB;
+      const int kq = 2 * p + q;  // K-block whose scale this lane supplies
 #pragma unroll
-    for (int j = 0; j < TN; j++) {
-      const int row = (wn * TN + j) * 32 + r32;
-      // (with KH the other operand's upper lanes are zero: a K-major A is
-      // zeroed above, a row-major A reads the zero slot)
-      if constexpr (TB) b[j] = lds_operand_k<BN, KH, false>(stage + OFF_B, (wn * TN + j) * 32, lane);
-      else if constexpr (KH) b[j] = lds_operand_half<BN>(stage + OFF_B, arena + ZERO, row, q);
-      else b[j] = lds_operand<FB, BN>(stage + OFF_B, row, swz, q);
-      xb[j] = *reinterpret_cast<const int*>(stage + OFF_SB + (GS ? q * (BN / gsb) + row / gsb : q * BN + row) * 4);
+      for (int i = 0; i < TM; i++) {
+        const int row = (wm * TM + i) * 32 + r32;
+        if constexpr (TA) a[p][i] = lds_operand_k<BM, KH, true>(sA, (wm * TM + i) * 32, lane);
+        else if constexpr (KH) a[p][i] = lds_operand_half<BM>(sA, arena + ZERO, row, q);
+        else a[p][i] = lds_operand<FA, BM>(sA, row, swz, q);
+        xa[p][i] = *reinterpret_cast<const int*>(stage + OFF_SA + (GS ? kq * (BM / gsa) + row / gsa : kq * BM + row) * 4);
+      }
+#pragma unroll
+      for (int j = 0; j < TN; j++) {
+        const int row = (wn * TN + j) * 32 + r32;
+        // (with KH the other operand's upper lanes are zero: a K-major A is
+        // zeroed above, a row-major A reads the zero slot)
+        if constexpr (TB) b[p][j] = lds_operand_k<BN, KH, false>(sB, (wn * TN + j) * 32, lane);
+        else if constexpr (KH) b[p][j] = lds_operand_half<BN>(sB, arena + ZERO, row, q);
+        else b[p][j] = lds_operand<FB, BN>(sB, row, swz, q);
+        xb[p][j] = *reinterpret_cast<const int*>(stage + OFF_SB + (GS ? kq * (BN / gsb) + row / gsb : kq * BN + row) * 4);
+      }
     }
   };
   auto mfmas = [&]() {
 #pragma unroll
-    for (int i = 0; i < TM; i++)
+    for (int p = 0; p < NP; p++)
 #pragma unroll
-      for (int j = 0; j < TN; j++)
-        acc[i][j] = mfma_scaled_32x32x64<FA, FB>(a[i], b[j], xa[i], xb[j], acc[i][j]);
+      for (int i = 0; i < TM; i++)
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+          acc[i][j] = mfma_scaled_32x32x64<FA, FB>(a[p][i], b[p][j], xa[p][i], xb[p][j], acc[i][j]);
   };
 
   // Ring of NS stages: at step s the loads of step s+NS-1 go into the stage
@@ -839,8 +860,8 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
   int cs = 0;
   // LDS reads per step of a wave, for the instruction schedule below
   constexpr int RDA = TA ? 4 : F_READS<FA>(), RDB = TB ? 4 : F_READS<FB>();
-  constexpr int NDS = TM * (RDA + 1) + TN * (RDB + 1);
-  constexpr int NMF = TM * TN;
+  constexpr int NDS = NP * (TM * (RDA + 1) + TN * (RDB + 1));
+  constexpr int NMF = NP * TM * TN;
   constexpr int VPM = (WPS + NMF - 1) / NMF;  // loads issued after each MFMA
   // Chunks of the table: iteration s issues step s_lo + s + NS - 1, which
   // must lie in [tb, tb + 64); past that the table is refilled (outside the
@@ -917,10 +938,11 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
 
 template <class P, int WM, int WN, int TM, int TN, int NS, bool GS, bool KH>
 hipError_t launch_gemm(int fa, int fb, const P& prob, dim3 grid, hipStream_t st) {
-#define MQ_CASE(A, B)                                                                                         \
-  if (fa == A && fb == B) {                                                                                   \
-    hipLaunchKernelGGL((mx_gemm_kernel<A, B, P, WM, WN, TM, TN, NS, GS, KH>), grid, dim3(256), 0, st, prob);  \
-    return hipGetLastError();                                                                                 \
+  constexpr int KPS = (P::kQuad && KH) ? 4 : 2;
+#define MQ_CASE(A, B)                                                                                              \
+  if (fa == A && fb == B) {                                                                                        \
+    hipLaunchKernelGGL((mx_gemm_kernel<A, B, P, WM, WN, TM, TN, NS, GS, KH, KPS>), grid, dim3(256), 0, st, prob);  \
+    return hipGetLastError();                                                                                      \
   }
   if constexpr (KH || (P::kKMajA && P::kKMajB)) {
     MQ_CASE(0, 0) MQ_CASE(0, 1) MQ_CASE(1, 0) MQ_CASE(1, 1)

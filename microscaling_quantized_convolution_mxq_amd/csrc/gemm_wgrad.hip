@@ -69,14 +69,15 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 // Format and tile dispatch
 // ---------------------------------------------------------------------------
 
-// K-steps of the backward-weight GEMM: pairs of N blocks per output pixel,
-// or pairs of output pixels along wo when N fits one block.
+// K-steps of the backward-weight GEMM: kps N blocks per output pixel, or
+// kps output pixels along wo when N fits one block (kps = 4 when the
+// K-blocks are half blocks, else 2).
 struct WgradSteps { int pair_w, nsub, total; };
-static WgradSteps wgrad_steps(const Conv& cv) {
+static WgradSteps wgrad_steps(const Conv& cv, int kps) {
   const int nNB = ceil_div(cv.n, 32);
   WgradSteps s;
   s.pair_w = nNB == 1;
-  s.nsub = s.pair_w ? (cv.wo() + 1) / 2 : (nNB + 1) / 2;
+  s.nsub = s.pair_w ? ceil_div(cv.wo(), kps) : ceil_div(nNB, kps);
   s.total = s.pair_w ? cv.ho() * s.nsub : cv.ho() * cv.wo() * s.nsub;
   return s;
 }
@@ -85,8 +86,11 @@ static int wgrad_splits(const Conv& cv, int fdy, int fx) {
   const long long npix = (long long)cv.ho() * cv.wo();
   const long long nNB = ceil_div(cv.n, 32);
   const long long ops = npix * cv.cout * nNB * run_bytes(fdy) + (long long)cv.h * cv.w * cv.cin * nNB * run_bytes(fx);
-  const WgradSteps ks = wgrad_steps(cv);
-  int s = splitk_slices(cv.cout, (long long)cv.kh * cv.kw * cv.cin, 2LL * ks.total, ops);
+  // the same count for either step size (the workspace size depends on it):
+  // capped by the number of four-block steps
+  const WgradSteps ks = wgrad_steps(cv, 4);
+  const long long nkb = (long long)cv.ho() * cv.wo() * ceil_div(cv.n, 32);
+  int s = splitk_slices(cv.cout, (long long)cv.kh * cv.kw * cv.cin, nkb, ops);
   if (s > ks.total) s = ks.total;
   if (s < 1) s = 1;
   return s;
@@ -139,7 +143,8 @@ hipError_t launch_backward_weight(const Conv& cv, MxView dy, MxView x, float* dw
   p.T = cv.kh * cv.kw; p.sh = cv.sh; p.sw = cv.sw; p.ph = cv.ph; p.pw = cv.pw; p.Ho = cv.ho(); p.Wo = cv.wo();
   p.nNB = ceil_div(cv.n, 32); p.ncob = ceil_div(cv.cout, 32); p.ncbi = ceil_div(cv.cin, 32);
   p.dyRB = half ? 16 : (int)run_bytes(dy.fmt); p.xRB = half ? 16 : (int)run_bytes(x.fmt);
-  const WgradSteps ks = wgrad_steps(cv);
+  p.kps = half_k_blocks(p.ga, p.gb, p.khalf, dy.fmt, x.fmt) ? 4 : 2;  // as the kernel choice below
+  const WgradSteps ks = wgrad_steps(cv, p.kps);
   p.pair_w = ks.pair_w; p.nsub = ks.nsub; p.total_steps = ks.total; p.steps_per_split = ceil_div(ks.total, S);
   p.dytc_bytes = npix_o * cv.cout * p.nNB * p.dyRB; p.dys_bytes = npix_o * p.nNB * p.ncob;
   p.xtc_bytes = (long long)cv.h * cv.w * cv.cin * p.nNB * p.xRB; p.xs_bytes = (long long)cv.h * cv.w * p.nNB * p.ncbi;
