@@ -147,25 +147,26 @@ def main():
         torch.cuda.synchronize()
         return g
 
-    # One graph runs R steps, one per buffer set (graph launches cost ~8 us
-    # each, so they are amortized over the R steps); single-step graphs make
-    # up a count that is not a multiple of R.
+    # One graph runs G = 4R steps, cycling over the buffer sets (a graph
+    # launch costs ~8 us, so it is amortized over G steps); single-step graphs
+    # make up a count that is not a multiple of G.
+    G = 4 * R
     if args.eager:
         step_graphs = multi_graph = None
     else:
         step_graphs = [capture(lambda d=d: step(d)) for d in sets]
-        multi_graph = capture(lambda: [step(d) for d in sets])
+        multi_graph = capture(lambda: [step(sets[i % R]) for i in range(G)])
 
     def launch_steps(n):
-        """Exactly n steps, in set order."""
+        """Exactly n steps, cycling over the buffer sets."""
         if multi_graph is None:
             for i in range(n):
                 step(sets[i % R])
             return
-        for _ in range(n // R):
+        for _ in range(n // G):
             multi_graph.replay()
-        for i in range(n % R):
-            step_graphs[i].replay()
+        for i in range(n % G):
+            step_graphs[i % R].replay()
 
     # ---- warm-up, then exactly K timed steps -----------------------------------
     with torch.cuda.stream(stream):
@@ -323,7 +324,7 @@ def main():
         "config": {"workload": wl.name, "n": s.n, "cin": s.cin, "cout": s.cout, "h": s.h, "w": s.w,
                    "kernel": f"{s.kh}x{s.kw}", "stride": s.stride, "pad": s.pad, "block": f"32 ch x {bp} batch",
                    "rotated_sets": R, "launch": "eager" if args.eager else "hip_graph",
-                   "steps_per_graph": 1 if args.eager else R},
+                   "steps_per_graph": 1 if args.eager else G},
         "roofline": roof,
         "cpu_baseline": cpu,
         "quantize_im2col_GB/s": round(q_im_bytes / (q_im_ms * 1e-3) / 1e9, 1),

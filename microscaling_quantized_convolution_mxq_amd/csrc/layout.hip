@@ -43,17 +43,26 @@ __global__ __launch_bounds__(256) void cbf_im2col_kernel(
   // blockIdx.y splits a pixel's chunks when there are few pixels
   const unsigned per = (nch + gridDim.y - 1) / gridDim.y;
   const unsigned c_lo = blockIdx.y * per, c_hi = min(nch, c_lo + per);
-  for (unsigned c = c_lo + threadIdx.x; c < c_hi; c += 256) {
-    const unsigned n = fdiv(c, div_tc);
-    const unsigned r = c - n * per_n;
-    const unsigned t = fdiv(r, div_c);
-    const unsigned ch = r - t * cpr;
-    const unsigned kh = fdiv(t, div_kw), kw = t - kh * div_kw.d;
-    const int hi = hb + (int)kh, wi = wb + (int)kw;
-    V v = {};
-    if ((unsigned)hi < (unsigned)H && (unsigned)wi < (unsigned)W)
-      v = src[((unsigned long long)(hi * W + wi) * N + n) * cpr + ch];
-    dst[c] = v;
+  // U chunks per thread in flight: all loads first, then the stores
+  constexpr int U = 4;
+  for (unsigned c0 = c_lo + threadIdx.x; c0 < c_hi; c0 += U * 256) {
+    V v[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const unsigned c = c0 + u * 256;
+      const unsigned n = fdiv(c, div_tc);
+      const unsigned r = c - n * per_n;
+      const unsigned t = fdiv(r, div_c);
+      const unsigned ch = r - t * cpr;
+      const unsigned kh = fdiv(t, div_kw), kw = t - kh * div_kw.d;
+      const int hi = hb + (int)kh, wi = wb + (int)kw;
+      v[u] = V{};
+      if (c < c_hi && (unsigned)hi < (unsigned)H && (unsigned)wi < (unsigned)W)
+        v[u] = src[((unsigned long long)(hi * W + wi) * N + n) * cpr + ch];
+    }
+#pragma unroll
+    for (int u = 0; u < U; u++)
+      if (c0 + u * 256 < c_hi) dst[c0 + u * 256] = v[u];
   }
   const unsigned ns = T * nsb;
   for (unsigned c = threadIdx.x; blockIdx.y == 0 && c < ns; c += 256) {
