@@ -555,8 +555,12 @@ __device__ __forceinline__ void stage_barrier() {
 // KH: every K-block has at most 16 valid codes (8-bit formats only): a
 // stage holds only the first 16-byte piece of each run, which halves it, so
 // the ring can be deeper for the same LDS.
-template <int FA, int FB, class P, int WM, int WN, int TM, int TN, int NS, bool GS, bool KH, int KPS>
-__global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
+// NG: wave groups of 4 waves per workgroup; group g runs the g-th part of
+// the workgroup's K range in its own ring of stages, and the groups' sums
+// are added (in group order) before the epilogue, so the workgroup covers
+// NG times the K range with NG times the waves.
+template <int FA, int FB, class P, int WM, int WN, int TM, int TN, int NS, bool GS, bool KH, int KPS, int NG>
+__global__ __launch_bounds__(256 * NG) void mx_gemm_kernel(P prob) {
   static_assert(!KH || (FA <= 1 && FB <= 1), "half K-blocks only for 8-bit codes");
   // K-major operands (8-bit codes, full runs): the staging order of the
   // contraction's natural layout, read back with transposing LDS reads
@@ -579,16 +583,20 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
   constexpr int WSA = GS ? 1 : (NSA + 3) / 4, WSB = GS ? 0 : (NSB + 3) / 4;
   constexpr int WPS = WCA + WCB + WSA + WSB;
   // 1 KB sink for the loads a wave issues only to keep its count uniform
-  constexpr int DUMMY = NS * STAGE;
+  constexpr int DUMMY = NG * NS * STAGE;
   constexpr int ZERO = DUMMY + 1024;  // KH: 16 zero bytes for the empty upper pieces
   constexpr int STRIP = 32 * (TN * 32 + 8) * 4;  // one wave's epilogue strip (bytes)
-  constexpr int ARENA = (ZERO + 16) > 4 * STRIP ? (ZERO + 16) : 4 * STRIP;
+  constexpr int XCH = NG > 1 ? 4 * TM * TN * 16 * 64 * 4 : 0;  // group 1's accumulators
+  constexpr int EPI = XCH > 4 * STRIP ? XCH : 4 * STRIP;
+  constexpr int ARENA = (ZERO + 16) > EPI ? (ZERO + 16) : EPI;
   __shared__ __attribute__((aligned(16))) uint8_t arena[ARENA];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = __builtin_amdgcn_readfirstlane(tid >> 8);          // wave group
+  const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);   // wave within the group
   const int wm = wave % WM, wn = wave / WM;
+  uint8_t* const ring = arena + grp * NS * STAGE;  // this group's stages
   // XCD-aware tile order: the hardware hands consecutive workgroups to the 8
   // XCDs in turn, each with its own L2. Remap so that every XCD works on a
   // contiguous range of tiles (x fastest): neighbouring row tiles share the
@@ -710,6 +718,11 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
 
   int s_lo, s_hi;
   prob.steps(cx, z, s_lo, s_hi);
+  // group g takes the g-th of NG equal parts; every group runs the same
+  // number of iterations (steps past its part read zeros)
+  const int per_grp = (s_hi - s_lo + NG - 1) / NG;
+  s_lo = s_lo + grp * per_grp;
+  s_hi = min(s_hi, s_lo + per_grp);
   // Step descriptors, 64 steps at a time: lane l of every wave holds those
   // of step tb + l (its K-block offsets and flags), and a step reads its own
   // into scalar registers with v_readlane. Steps past the last repeat it
@@ -752,7 +765,7 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
     const int nv = fl & 7;
     const bool inA = waveA || (fl & 8);
     const bool inB = waveB || (fl & 16);
-    uint8_t* const stage = arena + st * STAGE;
+    uint8_t* const stage = ring + st * STAGE;
 #pragma unroll
     for (int k = 0; k < WCA; k++) {
       const int g = wave + 4 * k;
@@ -808,7 +821,7 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
   v8i a[NP][TM], b[NP][TN];
   int xa[NP][TM], xb[NP][TN];
   auto read_operands = [&](int st) {
-    const uint8_t* const stage = arena + st * STAGE;
+    const uint8_t* const stage = ring + st * STAGE;
 #pragma unroll
     for (int p = 0; p < NP; p++) {
       const uint8_t* const sA = stage + p * 2 * KBA;
@@ -848,7 +861,7 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
   // that step s-1 computed from. The barrier before them both completes
   // stage s (every wave has waited for its own loads of step s) and retires
   // every wave's reads of stage s-1.
-  const int nsteps = s_hi - s_lo;
+  const int nsteps = per_grp;
   if constexpr (KH) {  // the zero slot; the first step's wait and barrier publish it
     if (tid == 0) {
       const v4i zero = {0, 0, 0, 0};
@@ -891,6 +904,34 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
   }
   wait_vm_lgkm0<0>();
   stage_barrier();
+  if constexpr (NG > 1) {
+    // group 1 hands its sums to group 0 through LDS (lane-major, no bank
+    // conflicts), group 0 adds them, and group 1 is done
+    float* xch = reinterpret_cast<float*>(arena) + wave * (TM * TN * 16 * 64);
+    if (grp == 1) {
+#pragma unroll
+      for (int i = 0; i < TM; i++)
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+#pragma unroll
+          for (int e = 0; e < 16; e++) xch[((i * TN + j) * 16 + e) * 64 + lane] = acc[i][j][e];
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    stage_barrier();
+    if (grp == 0) {
+#pragma unroll
+      for (int i = 0; i < TM; i++)
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+#pragma unroll
+          for (int e = 0; e < 16; e++) acc[i][j][e] += xch[((i * TN + j) * 16 + e) * 64 + lane];
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    // the strips below reuse the exchange area: every group-0 wave must have
+    // read its part first (all waves of both groups take this barrier)
+    stage_barrier();
+    if (grp == 1) return;
+  }
 
   // Epilogue through LDS (the stages are free now). For each 32-row strip i
   // a wave writes its TN accumulator tiles as a 32 x (TN*32) fp32 block
@@ -938,11 +979,15 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(P prob) {
 
 template <class P, int WM, int WN, int TM, int TN, int NS, bool GS, bool KH>
 hipError_t launch_gemm(int fa, int fb, const P& prob, dim3 grid, hipStream_t st) {
+  // the backward-weight problem with half K-blocks: four K-blocks per step
+  // and two wave groups per workgroup
   constexpr int KPS = (P::kQuad && KH) ? 4 : 2;
-#define MQ_CASE(A, B)                                                                                              \
-  if (fa == A && fb == B) {                                                                                        \
-    hipLaunchKernelGGL((mx_gemm_kernel<A, B, P, WM, WN, TM, TN, NS, GS, KH, KPS>), grid, dim3(256), 0, st, prob);  \
-    return hipGetLastError();                                                                                      \
+  constexpr int NG = (P::kQuad && KH) ? 2 : 1;
+#define MQ_CASE(A, B)                                                                                   \
+  if (fa == A && fb == B) {                                                                             \
+    hipLaunchKernelGGL((mx_gemm_kernel<A, B, P, WM, WN, TM, TN, NS, GS, KH, KPS, NG>), grid, dim3(256 * NG), 0, \
+                       st, prob);                                                                       \
+    return hipGetLastError();                                                                           \
   }
   if constexpr (KH || (P::kKMajA && P::kKMajB)) {
     MQ_CASE(0, 0) MQ_CASE(0, 1) MQ_CASE(1, 0) MQ_CASE(1, 1)

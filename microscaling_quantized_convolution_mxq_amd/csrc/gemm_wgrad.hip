@@ -137,13 +137,16 @@ hipError_t launch_backward_weight(const Conv& cv, MxView dy, MxView x, float* dw
     e = launch_transpose_codes(x.codes, xt, x.fmt, half, cv.h * cv.w, cv.n, 1, cv.cin, st);
     if (e != hipSuccess) return e;
   }
-  const int S = wgrad_splits(cv, dy.fmt, x.fmt);
+  // as the kernel choice below: half K-blocks take four K-blocks per step and
+  // two wave groups per workgroup, so half as many slices cover the K range
+  p.kps = half_k_blocks(p.ga, p.gb, p.khalf, dy.fmt, x.fmt) ? 4 : 2;
+  const int S0 = wgrad_splits(cv, dy.fmt, x.fmt);  // the workspace holds S0 slices
+  const int S = p.kps == 4 ? ceil_div(S0, 2) : S0;
   p.dytc = dyt; p.dys = dy.scales; p.xtc = xt; p.xs = x.scales; p.part = S > 1 ? part : dw;
   p.N = cv.n; p.H = cv.h; p.W = cv.w; p.Cin = cv.cin; p.Cout = cv.cout; p.KW = cv.kw;
   p.T = cv.kh * cv.kw; p.sh = cv.sh; p.sw = cv.sw; p.ph = cv.ph; p.pw = cv.pw; p.Ho = cv.ho(); p.Wo = cv.wo();
   p.nNB = ceil_div(cv.n, 32); p.ncob = ceil_div(cv.cout, 32); p.ncbi = ceil_div(cv.cin, 32);
   p.dyRB = half ? 16 : (int)run_bytes(dy.fmt); p.xRB = half ? 16 : (int)run_bytes(x.fmt);
-  p.kps = half_k_blocks(p.ga, p.gb, p.khalf, dy.fmt, x.fmt) ? 4 : 2;  // as the kernel choice below
   const WgradSteps ks = wgrad_steps(cv, p.kps);
   p.pair_w = ks.pair_w; p.nsub = ks.nsub; p.total_steps = ks.total; p.steps_per_split = ceil_div(ks.total, S);
   p.dytc_bytes = npix_o * cv.cout * p.nNB * p.dyRB; p.dys_bytes = npix_o * p.nNB * p.ncob;
