@@ -60,9 +60,13 @@ __global__ __launch_bounds__(256) void cbf_im2col_kernel(
       if (c < c_hi && (unsigned)hi < (unsigned)H && (unsigned)wi < (unsigned)W)
         v[u] = src[((unsigned long long)(hi * W + wi) * N + n) * cpr + ch];
     }
+    // streaming stores: the expanded tensor is not read back by this step,
+    // and keeping it out of the caches leaves them to the source rows
+    typedef unsigned NV __attribute__((ext_vector_type(CH / 4)));
 #pragma unroll
     for (int u = 0; u < U; u++)
-      if (c0 + u * 256 < c_hi) dst[c0 + u * 256] = v[u];
+      if (c0 + u * 256 < c_hi)
+        __builtin_nontemporal_store(*reinterpret_cast<const NV*>(&v[u]), reinterpret_cast<NV*>(&dst[c0 + u * 256]));
   }
   const unsigned ns = T * nsb;
   for (unsigned c = threadIdx.x; blockIdx.y == 0 && c < ns; c += 256) {
