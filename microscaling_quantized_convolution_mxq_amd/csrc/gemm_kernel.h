@@ -142,7 +142,10 @@ struct DgradProb {
   static constexpr bool kGeoA = true, kGeoB = false, kCanGroup = true;
   static constexpr bool kKMajA = false, kKMajB = false;
   static constexpr bool kQuad = false;
-  struct Ctx { int ph_c, pw_c, Hc, Wc, kh0, kw0, nkh, nkw, M; };
+  // the class's divisors and output-pixel offsets are taken out of the
+  // argument arrays once per workgroup (a dynamic index into them would
+  // reload them from memory at every use)
+  struct Ctx { int ph_c, pw_c, Hc, Wc, kh0, kw0, nkh, nkw, M, hoff, woff; FastDiv dwc, dnkw; };
   struct KS { int ih, iw, v; };
   __device__ Ctx ctx(int z) const {
     Ctx c; c.ph_c = z / sw; c.pw_c = z - c.ph_c * sw;
@@ -152,6 +155,8 @@ struct DgradProb {
     c.nkh = c.kh0 < KH ? (KH - c.kh0 + sh - 1) / sh : 0;
     c.nkw = c.kw0 < KW ? (KW - c.kw0 + sw - 1) / sw : 0;
     c.M = c.Hc * c.Wc * N;
+    c.hoff = (c.ph_c + ph - c.kh0) / sh; c.woff = (c.pw_c + pw - c.kw0) / sw;
+    c.dwc = dWc[c.pw_c]; c.dnkw = dNkw[c.pw_c];
     return c;
   }
   __device__ int rows_a(const Ctx& c) const { return c.M; }
@@ -159,7 +164,7 @@ struct DgradProb {
   __device__ void steps(const Ctx& c, int, int& lo, int& hi) const { lo = 0; hi = c.nkh * c.nkw * npair; }
   __device__ KS kstart(const Ctx& c, int s) const {
     const int u = (int)fdiv((unsigned)s, dnp); KS k; k.v = 2 * (s - u * npair);
-    k.ih = (int)fdiv((unsigned)u, dNkw[c.pw_c]); k.iw = u - k.ih * c.nkw; return k;
+    k.ih = (int)fdiv((unsigned)u, c.dnkw); k.iw = u - k.ih * c.nkw; return k;
   }
   __device__ int nvalid(const Ctx&, const KS& k) const { return k.v + 1 >= ncob ? 1 : 2; }
   __device__ PairDelta pd_a() const { return PairDelta{dyRB, 1, 0, 0}; }
@@ -168,10 +173,10 @@ struct DgradProb {
     RowInfo r; r.ok = m < c.M; const int mm = r.ok ? m : 0;
     const int wc = c.Wc > 0 ? c.Wc : 1;
     const int pix = (int)fdiv((unsigned)mm, dN), n = mm - pix * N;
-    const int hq = (int)fdiv((unsigned)pix, dWc[c.pw_c]), wq = pix - hq * wc;
+    const int hq = (int)fdiv((unsigned)pix, c.dwc), wq = pix - hq * wc;
     // output pixel of tap (kh0, kw0); exact division by the class choice
-    r.p0 = hq + (c.ph_c + ph - c.kh0) / sh;
-    r.p1 = wq + (c.pw_c + pw - c.kw0) / sw;
+    r.p0 = hq + c.hoff;
+    r.p1 = wq + c.woff;
     const int p = r.p0 * Wo + r.p1;
     r.code = (p * N + n) * dyrb; r.scale = (p * dynPB + (n >> dybps)) * ncob; return r;
   }
@@ -197,8 +202,9 @@ struct DgradProb {
   __device__ bool step_interior_b(const Ctx&, const KS&) const { return true; }
   __device__ float* out_row(const Ctx& c, int, int m) const {
     if (m >= c.M) return nullptr;
+    if (sh == 1 && sw == 1) return dx + (long long)m * Cin;  // one class: rows in dX order
     const int pix = (int)fdiv((unsigned)m, dN), n = m - pix * N;
-    const int hq = (int)fdiv((unsigned)pix, dWc[c.pw_c]), wq = pix - hq * c.Wc;
+    const int hq = (int)fdiv((unsigned)pix, c.dwc), wq = pix - hq * c.Wc;
     const int h = hq * sh + c.ph_c, w = wq * sw + c.pw_c;
     return dx + (((long long)h * W + w) * N + n) * Cin;
   }
