@@ -733,18 +733,21 @@ __global__ __launch_bounds__(256 * NG) void mx_gemm_kernel(P prob) {
   // of step tb + l (its K-block offsets and flags), and a step reads its own
   // into scalar registers with v_readlane. Steps past the last repeat it
   // (their loads read zeros).
+  // descriptors of step s: K-block offsets of both operands, and flags
+  // (valid K-blocks, step interior for A and for B)
+  struct StepD { KInfo ka, kb; int fl; };
+  auto step_desc = [&](int s_any) {
+    const int s = min(s_any, max(s_hi - 1, s_lo));
+    const typename P::KS k = prob.kstart(cx, s);
+    return StepD{prob.k_a(cx, k), prob.k_b(cx, k),
+                 prob.nvalid(cx, k) | (prob.step_interior_a(cx, k) ? 8 : 0) | (prob.step_interior_b(cx, k) ? 16 : 0)};
+  };
   struct Tab { int ac, as, ag0, ag1, bc, bs, bg0, bg1, fl; };
   auto fill = [&](int base) {
-    Tab t;
-    const int s = min(base + lane, max(s_hi - 1, s_lo));
-    const typename P::KS k = prob.kstart(cx, s);
-    const KInfo ka = prob.k_a(cx, k), kb = prob.k_b(cx, k);
-    t.ac = ka.code; t.as = ka.scale; t.ag0 = ka.g0; t.ag1 = ka.g1;
-    t.bc = kb.code; t.bs = kb.scale; t.bg0 = kb.g0; t.bg1 = kb.g1;
-    t.fl = prob.nvalid(cx, k) | (prob.step_interior_a(cx, k) ? 8 : 0) | (prob.step_interior_b(cx, k) ? 16 : 0);
-    return t;
+    const StepD d = step_desc(base + lane);
+    return Tab{d.ka.code, d.ka.scale, d.ka.g0, d.ka.g1, d.kb.code, d.kb.scale, d.kb.g0, d.kb.g1, d.fl};
   };
-  Tab tab = fill(s_lo);
+  Tab tab;
   int tb = s_lo;
   int s_next = s_lo;
 
@@ -761,13 +764,8 @@ __global__ __launch_bounds__(256 * NG) void mx_gemm_kernel(P prob) {
 
   // Issue the loads of the next step into stage `st`. Loads past the last
   // step read zeros, so every wave issues WPS loads per step.
-  auto issue = [&](int st) {
+  auto issue_d = [&](int st, const KInfo& ka, const KInfo& kb, int fl) {
     const bool live = s_next < s_hi;
-    const int li = s_next - tb;
-    auto rl = [li](int v) { return __builtin_amdgcn_readlane(v, li); };
-    const KInfo ka{rl(tab.ac), rl(tab.as), P::kGeoA ? rl(tab.ag0) : 0, P::kGeoA ? rl(tab.ag1) : 0};
-    const KInfo kb{rl(tab.bc), rl(tab.bs), P::kGeoB ? rl(tab.bg0) : 0, P::kGeoB ? rl(tab.bg1) : 0};
-    const int fl = rl(tab.fl);
     const int nv = fl & 7;
     const bool inA = waveA || (fl & 8);
     const bool inB = waveB || (fl & 16);
@@ -808,6 +806,14 @@ __global__ __launch_bounds__(256 * NG) void mx_gemm_kernel(P prob) {
       }
     }
     s_next++;
+  };
+  // a step of the ring: its descriptors from the table
+  auto issue = [&](int st) {
+    const int li = s_next - tb;
+    auto rl = [li](int v) { return __builtin_amdgcn_readlane(v, li); };
+    const KInfo ka{rl(tab.ac), rl(tab.as), P::kGeoA ? rl(tab.ag0) : 0, P::kGeoA ? rl(tab.ag1) : 0};
+    const KInfo kb{rl(tab.bc), rl(tab.bs), P::kGeoB ? rl(tab.bg0) : 0, P::kGeoB ? rl(tab.bg1) : 0};
+    issue_d(st, ka, kb, rl(tab.fl));
   };
 
   v16f acc[TM][TN];
@@ -874,8 +880,14 @@ __global__ __launch_bounds__(256 * NG) void mx_gemm_kernel(P prob) {
       *reinterpret_cast<v4i*>(arena + ZERO) = zero;
     }
   }
+  // the first NS-1 steps' descriptors are computed directly (uniform, in
+  // scalar registers), so their loads leave before the table is filled
 #pragma unroll
-  for (int i = 0; i < NS - 1; i++) issue(i);
+  for (int i = 0; i < NS - 1; i++) {
+    const StepD d = step_desc(s_lo + i);
+    issue_d(i, d.ka, d.kb, d.fl);
+  }
+  tab = fill(s_lo);
   int cs = 0;
   // LDS reads per step of a wave, for the instruction schedule below
   constexpr int RDA = TA ? 4 : F_READS<FA>(), RDB = TB ? 4 : F_READS<FB>();
