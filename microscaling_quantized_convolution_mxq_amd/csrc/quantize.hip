@@ -127,7 +127,9 @@ __global__ __launch_bounds__(256) void mxq_quantize_kernel(const float* __restri
   const bool vec = (C & 3) == 0;
   constexpr float maxv = Fmt<F>::maxv;
 
-  for (int cb = 0; cb < nCB; cb++) {
+  // blockIdx.y splits the channel blocks of small tensors over workgroups
+  // (gridDim.y is 1 with LDS staging, which needs a tile's whole rows)
+  for (int cb = blockIdx.y; cb < nCB; cb += gridDim.y) {
     const int c0 = cb * 32 + half * 16;
     float x[16];
     if (row_ok && vec && c0 + 16 <= C) {
@@ -191,8 +193,9 @@ static hipError_t launch_q(const float* src, uint8_t* codes, uint8_t* scales, in
   if (B == 1 && (C + 31) / 32 <= kStageCB)
     hipLaunchKernelGGL((mxq_quantize_kernel<F, MODE, true>), dim3((unsigned)blocks), dim3(256), 0, st, src,
                        codes, scales, A, P, B, C, bp, ntiles);
-  else
-    hipLaunchKernelGGL((mxq_quantize_kernel<F, MODE, false>), dim3((unsigned)blocks), dim3(256), 0, st, src,
+  else  // small tensors: one workgroup per channel block as well (one memory round trip)
+    hipLaunchKernelGGL((mxq_quantize_kernel<F, MODE, false>),
+                       dim3((unsigned)blocks, blocks < 512 ? (unsigned)((C + 31) / 32) : 1u), dim3(256), 0, st, src,
                        codes, scales, A, P, B, C, bp, ntiles);
   return hipGetLastError();
 }
