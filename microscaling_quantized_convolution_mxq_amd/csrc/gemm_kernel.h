@@ -119,6 +119,8 @@ struct FwdProb {
   __device__ bool step_interior_a(const Ctx&, const KS&) const { return false; }
   __device__ bool step_interior_b(const Ctx&, const KS&) const { return true; }
   __device__ float* out_row(const Ctx&, int, int m) const { return m < M ? y + (long long)m * Cout : nullptr; }
+  // rows m .. m + run - 1 lie at out_row(m) + j * ncols()
+  __device__ int row_run(const Ctx&, int) const { return 1 << 30; }
 };
 
 // Backward-data: rows of parity class z are h = hq*sh + ph_c, w = wq*sw + pw_c
@@ -200,6 +202,12 @@ struct DgradProb {
   __device__ GRange g_range_b(const Ctx&) const { return GRange{0, 0, 0, 0}; }
   __device__ bool step_interior_a(const Ctx&, const KS&) const { return false; }
   __device__ bool step_interior_b(const Ctx&, const KS&) const { return true; }
+  // rows m .. m + run - 1 lie at out_row(m) + j * ncols(): the rest of the
+  // pixel (all rows with stride 1)
+  __device__ int row_run(const Ctx&, int m) const {
+    if (sh == 1 && sw == 1) return 1 << 30;
+    return N - (m - (int)fdiv((unsigned)m, dN) * N);
+  }
   __device__ float* out_row(const Ctx& c, int, int m) const {
     if (m >= c.M) return nullptr;
     if (sh == 1 && sw == 1) return dx + (long long)m * Cin;  // one class: rows in dX order
@@ -288,6 +296,7 @@ struct WgradProb {
     const int h0 = k.ho * sh - ph, w0 = k.wo * sw - pw, w1 = w0 + (pair_w ? (kps - 1) * sw : 0);
     return (h0 >= 0) & (h0 + T / KW - 1 < H) & (w0 >= 0) & (w1 + KW - 1 < W);
   }
+  __device__ int row_run(const Ctx&, int) const { return 1 << 30; }
   __device__ float* out_row(const Ctx&, int z, int m) const {
     return m < Cout ? part + ((long long)z * Cout + m) * ((long long)T * Cin) : nullptr;
   }
@@ -338,6 +347,7 @@ struct PlainProb {
   __device__ GRange g_range_b(const Ctx&) const { return GRange{0, 0, 0, 0}; }
   __device__ bool step_interior_a(const Ctx&, const KS&) const { return true; }
   __device__ bool step_interior_b(const Ctx&, const KS&) const { return true; }
+  __device__ int row_run(const Ctx&, int) const { return 1 << 30; }
   __device__ float* out_row(const Ctx&, int z, int m) const {
     return m < Ma ? out + ((long long)z * Ma + m) * Nb : nullptr;
   }
@@ -565,8 +575,10 @@ __device__ __forceinline__ void stage_barrier() {
 // the workgroup's K range in its own ring of stages, and the groups' sums
 // are added (in group order) before the epilogue, so the workgroup covers
 // NG times the K range with NG times the waves.
+// At least two waves per SIMD: the register budget (VGPRs + accumulation
+// registers) stays within 256, so two 256x128 workgroups share a CU.
 template <int FA, int FB, class P, int WM, int WN, int TM, int TN, int NS, bool GS, bool KH, int KPS, int NG>
-__global__ __launch_bounds__(256 * NG) void mx_gemm_kernel(P prob) {
+__global__ __launch_bounds__(256 * NG) __attribute__((amdgpu_waves_per_eu(2))) void mx_gemm_kernel(P prob) {
   static_assert(!KH || (FA <= 1 && FB <= 1), "half K-blocks only for 8-bit codes");
   // K-major operands (8-bit codes, full runs): the staging order of the
   // contraction's natural layout, read back with transposing LDS reads
@@ -973,12 +985,17 @@ __global__ __launch_bounds__(256 * NG) void mx_gemm_kernel(P prob) {
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the strip is written (same wave)
     __builtin_amdgcn_wave_barrier();
     constexpr int V = 32 * EW / 4;  // float4 pieces in the strip
+    // the strip's first row and the run of rows that follow it at a fixed
+    // stride: one address computation per strip instead of one per row
+    const int ms = m0 + (wm * TM + i) * 32;
+    float* const sbase = prob.out_row(cx, z, ms);
+    const int run = prob.row_run(cx, ms), mlim = prob.rows_a(cx);
 #pragma unroll
     for (int t = 0; t < V / 64; t++) {
       const int flat = t * 64 + lane;
       const int rr = flat / (EW / 4), c4 = flat % (EW / 4);
-      const int m = m0 + (wm * TM + i) * 32 + rr;
-      float* row = prob.out_row(cx, z, m);
+      const int m = ms + rr;
+      float* row = rr < run ? (m < mlim ? sbase + (long long)rr * ncols : nullptr) : prob.out_row(cx, z, m);
       const v4f val = *reinterpret_cast<const v4f*>(&strip[rr * EP + c4 * 4]);
       if (row) {
         const int c = c_wave + c4 * 4;
@@ -1060,7 +1077,9 @@ hipError_t launch_tile_id(int id, int fa, int fb, const P& prob, dim3 grid, hipS
   switch (id) {
     case 0: return launch_gemm<P, 4, 1, 2, 2, NS, GS, KH>(fa, fb, prob, grid, st);
     case 1: return launch_gemm<P, 2, 2, 2, 2, NS, GS, KH>(fa, fb, prob, grid, st);
-    case 2: return launch_gemm<P, 2, 2, 4, 2, NS, GS, KH>(fa, fb, prob, grid, st);
+    case 2:
+      if constexpr (P::kQuad && KH) return hipErrorInvalidValue;  // not chosen (see launch_tiled)
+      else return launch_gemm<P, 2, 2, 4, 2, NS, GS, KH>(fa, fb, prob, grid, st);
     case 4: return launch_gemm<P, 2, 2, 1, 3, NS, GS, KH>(fa, fb, prob, grid, st);
     default: return launch_gemm<P, 1, 4, 2, 2, NS, GS, KH>(fa, fb, prob, grid, st);
   }
@@ -1085,7 +1104,12 @@ inline bool half_k_blocks(int ga, int gb, int khalf, int fa, int fb) {
 
 template <class P>
 hipError_t launch_tiled(int fa, int fb, const P& prob_in, int M, int Ncols, int Z, hipStream_t st) {
-  const TileChoice t = choose_tile(M, Ncols, Z);
+  TileChoice t = choose_tile(M, Ncols, Z);
+  // four K-blocks per step double the operand registers: the 256 x 128 tile
+  // would then exceed the budget of two waves per SIMD
+  if constexpr (P::kQuad) {
+    if (t.id == 2 && half_k_blocks(prob_in.ga, prob_in.gb, prob_in.khalf, fa, fb)) t = tile_shape(1);
+  }
   dim3 grid(ceil_div(M, t.bm), ceil_div(Ncols, t.bn), Z);
   P prob = prob_in;
   prob.grid.nx = make_fastdiv(grid.x);
