@@ -12,12 +12,14 @@
 // one E8M0 scale, which is the block-scaled dot product of Eq. (7): the MFMA
 // multiplies the codes and applies both block scales per K-block.
 //
-// Kernel: 256 threads = 4 waves in a WM x WN grid; each wave owns TM x TN
-// MFMA tiles of 32 x 32. A K-step is a pair of K-blocks (64 codes per row).
-// Operands go from HBM straight into LDS with buffer loads that write LDS
-// (no register staging): an NS-deep ring of LDS stages, so the loads of
-// step s+NS-1 are in flight while the MFMAs of step s run, with one
-// workgroup barrier per step.
+// Kernel: 256 threads = 4 waves in a WM x WN grid (512 = two such groups
+// splitting the K range, for the weight gradient); each wave owns TM x TN
+// MFMA tiles of 32 x 32. A K-step is a pair of K-blocks (64 codes per row),
+// or two pairs. Operands go from HBM straight into LDS with buffer loads
+// that write LDS (no register staging): an NS-deep ring of LDS stages, so
+// the loads of step s+NS-1 are in flight while the MFMAs of step s run, with
+// one workgroup barrier per step. 8-bit operands whose contraction runs
+// across their rows are staged K-major and transposed by the LDS reads.
 #pragma once
 #include <type_traits>
 
@@ -39,9 +41,9 @@ namespace mq {
 // k.g1) in [0, lim1); the geometric test covers the image borders of the
 // implicit im2col. Invalid (zero) blocks read from past the end of the
 // buffer, where raw buffer loads return 0 (the range check covers the sum of
-// both offsets, per dword). The second K-block of a pair is the first one
-// moved by a problem-wide PairDelta; a step whose pair has no second K-block
-// (odd count) says so with tail().
+// both offsets, per dword). K-block j of a step is the first one moved j
+// times by a problem-wide PairDelta; a step with fewer K-blocks (odd counts,
+// row ends) says how many are valid with nvalid().
 constexpr int kOOB = 0x7fffff00;
 constexpr int kFar = 0x40000000;  // row coordinate that fails every border test
 struct RowInfo { int code, scale, p0, p1; bool ok; };
