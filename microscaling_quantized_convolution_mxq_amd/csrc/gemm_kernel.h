@@ -418,6 +418,28 @@ struct WgradNatProb : WgradProb {
   }
 };
 
+// Backward-weight with the 8-bit gradient codes read where quantization
+// left them (A staged K-major, as in WgradNatProb) and 6- or 4-bit
+// activation codes re-laid with runs along N (B as in WgradProb). dytc
+// points at the natural gradient codes with dyrb row bytes.
+struct WgradMixProb : WgradProb {
+  int dyrb;
+  static constexpr bool kKMajA = true, kKMajB = false;
+  __device__ int kext_a() const { return N < 32 ? N : 32; }
+  __device__ int kstride_a() const { return dyrb; }
+  __device__ PairDelta pd_a() const {
+    return pair_w ? PairDelta{N * dyrb, nNB * ncob, 0, 0} : PairDelta{32 * dyrb, ncob, 0, 0};
+  }
+  __device__ RowInfo row_a(const Ctx&, int m) const {
+    RowInfo r; r.ok = m < Cout; const int co = r.ok ? m : 0;
+    r.code = co; r.scale = co / 32; r.p0 = 0; r.p1 = 0; return r;
+  }
+  __device__ KInfo k_a(const Ctx&, const KS& k) const {
+    const int pix = k.ho * Wo + k.wo;
+    return KInfo{(pix * N + 32 * k.v) * dyrb, (pix * nNB + k.v) * ncob, 0, 0};
+  }
+};
+
 // Buffers of each problem: (A codes, A scales, B codes, B scales).
 __device__ inline void rsrcs(const FwdProb& p, __amdgpu_buffer_rsrc_t (&r)[4]) {
   r[0] = make_rsrc(p.xc - p.xcb, p.xc_bytes + p.xcb); r[1] = make_rsrc(p.xs - p.xsb, p.xs_bytes + p.xsb);
@@ -1032,6 +1054,10 @@ hipError_t launch_gemm(int fa, int fb, const P& prob, dim3 grid, hipStream_t st)
   } else if constexpr (P::kKMajB) {
     MQ_CASE(0, 0) MQ_CASE(0, 1) MQ_CASE(1, 0) MQ_CASE(1, 1) MQ_CASE(2, 0) MQ_CASE(2, 1)
     MQ_CASE(3, 0) MQ_CASE(3, 1) MQ_CASE(4, 0) MQ_CASE(4, 1)
+    return hipErrorInvalidValue;
+  } else if constexpr (P::kKMajA) {
+    MQ_CASE(0, 0) MQ_CASE(0, 1) MQ_CASE(0, 2) MQ_CASE(0, 3) MQ_CASE(0, 4)
+    MQ_CASE(1, 0) MQ_CASE(1, 1) MQ_CASE(1, 2) MQ_CASE(1, 3) MQ_CASE(1, 4)
     return hipErrorInvalidValue;
   } else {
   MQ_CASE(0, 0) MQ_CASE(0, 1) MQ_CASE(0, 2) MQ_CASE(0, 3) MQ_CASE(0, 4)

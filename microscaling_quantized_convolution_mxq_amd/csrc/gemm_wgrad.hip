@@ -128,12 +128,18 @@ hipError_t launch_backward_weight(const Conv& cv, MxView dy, MxView x, float* dw
   // when a 16-channel chunk of B stays in one tap and a K-block's lines are
   // the N values of one pixel; otherwise both are first re-laid with runs
   // along N
-  const bool natural = dy.fmt <= 1 && x.fmt <= 1 && cv.cin % 16 == 0 && (cv.n <= 32 || cv.n % 32 == 0);
+  // along N; with 8-bit gradient codes and other activation codes (mixed)
+  // only the activation is re-laid
+  const bool kext_ok = cv.n <= 32 || cv.n % 32 == 0;
+  const bool natural = dy.fmt <= 1 && x.fmt <= 1 && cv.cin % 16 == 0 && kext_ok;
+  const bool mixed = !natural && dy.fmt <= 1 && kext_ok;
   const bool half = !natural && half_k_blocks(p.ga, p.gb, p.khalf, dy.fmt, x.fmt);
   hipError_t e = hipSuccess;
-  if (!natural) {
+  if (!natural && !mixed) {
     e = launch_transpose_codes(dy.codes, dyt, dy.fmt, half, (int)npix_o, cv.n, 1, cv.cout, st);
     if (e != hipSuccess) return e;
+  }
+  if (!natural) {
     e = launch_transpose_codes(x.codes, xt, x.fmt, half, cv.h * cv.w, cv.n, 1, cv.cin, st);
     if (e != hipSuccess) return e;
   }
@@ -166,6 +172,12 @@ hipError_t launch_backward_weight(const Conv& cv, MxView dy, MxView x, float* dw
     q.xtc = x.codes; q.xtc_bytes = (long long)cv.h * cv.w * cv.n * q.xrb;
     q.xtcb = (int)(lead * cv.n * q.xrb);
     if (!offsets_fit(q.xtc_bytes, q.xtcb)) return hipErrorInvalidValue;
+    e = launch_tiled(dy.fmt, x.fmt, q, cv.cout, (int)nj, S, st);
+  } else if (mixed) {  // (half K-blocks need 8-bit activation codes: never here)
+    WgradMixProb q;
+    static_cast<WgradProb&>(q) = p;
+    q.dyrb = (int)row_bytes(dy.fmt, cv.cout);
+    q.dytc = dy.codes; q.dytc_bytes = npix_o * cv.n * q.dyrb;
     e = launch_tiled(dy.fmt, x.fmt, q, cv.cout, (int)nj, S, st);
   } else {
     e = launch_tiled(dy.fmt, x.fmt, p, cv.cout, (int)nj, S, st);
