@@ -44,8 +44,9 @@ CALL_KERNELS = {
     "forward": ["mx_gemm_kernel<FwdProb>"],
     # 8-bit codes are read in place; other formats are first re-laid by transpose_codes_kernel
     "backward_data": ["mx_gemm_kernel<DgradNatProb> (8-bit W; else transpose_codes_kernel + mx_gemm_kernel<DgradProb>)"],
-    "backward_weight": ["mx_gemm_kernel<WgradNatProb> (8-bit dY, X; else 2 x transpose_codes_kernel + "
-                        "mx_gemm_kernel<WgradProb>)", "splitk_reduce_kernel (when split)"],
+    "backward_weight": ["mx_gemm_kernel<WgradNatProb> (8-bit dY and X; 8-bit dY only: transpose_codes_kernel (X) + "
+                        "mx_gemm_kernel<WgradMixProb>; else 2 x transpose_codes_kernel + mx_gemm_kernel<WgradProb>)",
+                        "splitk_reduce_kernel (when split)"],
 }
 
 
