@@ -1,7 +1,8 @@
 """Benchmark of the MicroQonv training hot path on one MI355X.
 
 One step = one pass of every step of the path over one batch of synthetic
-input: quantize X, W and G_Y once (MX, E8M0 scales), channel-batch-first
+input: quantize X and W (one grouped call, as before a layer's forward
+pass) and G_Y once (MX, E8M0 scales), channel-batch-first
 im2col of the quantized activation, then the forward, backward-data and
 backward-weight block-scaled GEMMs. Inputs are resident in HBM before the
 timed region; R copies of every buffer are rotated so the live set exceeds
@@ -36,10 +37,11 @@ HBM_PEAK_GBS = 8000.0
 # dense MFMA peaks of MI355X (TFLOP/s); mixed 6/4-bit x 8-bit products run at the 8-bit rate
 MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "fp6fp4": 10100.0}
 CSRC = os.path.join(ROOT, "microscaling_quantized_convolution_mxq_amd", "csrc")
-CALLS = ["quantize_x", "quantize_w", "quantize_dy", "cbf_im2col", "forward", "backward_data", "backward_weight"]
+CALLS = ["quantize_xw", "quantize_dy", "cbf_im2col", "forward", "backward_data", "backward_weight"]
 # kernels each entry point launches (see the launchers in csrc/)
 CALL_KERNELS = {
-    "quantize_x": ["mxq_quantize_kernel"], "quantize_w": ["mxq_quantize_kernel"],
+    # X and W share one launch when their formats match, else one launch each
+    "quantize_xw": ["mxq_quantize_group_kernel (same format; else 2 x mxq_quantize_kernel)"],
     "quantize_dy": ["mxq_quantize_kernel"], "cbf_im2col": ["cbf_im2col_kernel"],
     "forward": ["mx_gemm_kernel<FwdProb>"],
     # 8-bit codes are read in place; other formats are first re-laid by transpose_codes_kernel
@@ -114,10 +116,8 @@ def main():
     sets = [first] + [make_set() for _ in range(R - 1)]
 
     def run(d, name):
-        if name == "quantize_x":
-            mq.mqconv_quantize(d["x"], d["xq"])
-        elif name == "quantize_w":
-            mq.mqconv_quantize(d["w"], d["wq"])
+        if name == "quantize_xw":
+            mq.mqconv_quantize_group([(d["x"], d["xq"]), (d["w"], d["wq"])])
         elif name == "quantize_dy":
             mq.mqconv_quantize(d["dy"], d["gq"])
         elif name == "cbf_im2col":
@@ -188,7 +188,7 @@ def main():
     # A graph of 2 x Rc calls rotating over Rc copies of just the buffers the
     # call touches, with Rc chosen so that those copies exceed the 256 MB
     # Infinity Cache as the step's sets do (no call reads cache-resident inputs).
-    NEED = {"quantize_x": ("x", "xq"), "quantize_w": ("w", "wq"), "quantize_dy": ("dy", "gq"),
+    NEED = {"quantize_xw": ("x", "xq", "w", "wq"), "quantize_dy": ("dy", "gq"),
             "cbf_im2col": ("xq", "cc", "cs"), "forward": ("xq", "wq", "y"),
             "backward_data": ("gq", "wq", "dx", "ws1"), "backward_weight": ("gq", "xq", "dw", "ws2")}
 
@@ -229,7 +229,7 @@ def main():
     col_b = mq.mqconv_im2col_codes_bytes(s, wl.fx) + mq.mqconv_im2col_scales_bytes(s, bp)
     # bytes each call must move at least once (inputs read, outputs written)
     alg_bytes = {
-        "quantize_x": 4 * nx + xq_b, "quantize_w": 4 * nw + wq_b, "quantize_dy": 4 * ng + gq_b,
+        "quantize_xw": 4 * nx + xq_b + 4 * nw + wq_b, "quantize_dy": 4 * ng + gq_b,
         "cbf_im2col": xq_b + col_b,
         "forward": xq_b + wq_b + 4 * ng, "backward_data": gq_b + wq_b + 4 * nx, "backward_weight": gq_b + xq_b + 4 * nw,
     }
@@ -273,8 +273,8 @@ def main():
         if rec.get("source_sha") == source_sha():
             roof["traffic"] = rec.get("traffic_bytes")
 
-    q_im_bytes = sum(alg_bytes[c] for c in ("quantize_x", "quantize_w", "quantize_dy", "cbf_im2col"))
-    q_im_ms = sum(per_call[c] for c in ("quantize_x", "quantize_w", "quantize_dy", "cbf_im2col"))
+    q_im_bytes = sum(alg_bytes[c] for c in ("quantize_xw", "quantize_dy", "cbf_im2col"))
+    q_im_ms = sum(per_call[c] for c in ("quantize_xw", "quantize_dy", "cbf_im2col"))
     gemm_ms = sum(per_call[c] for c in alg_flop)
 
     # ---- naive comparison path (not part of the step) ------------------------

@@ -171,6 +171,19 @@ size_t mqconv_im2col_scales_bytes(const mq_conv* cv, int32_t bp);
  *      are fully overwritten (padding codes included). */
 int mqconv_quantize(const float* src, mq_mx dst, void* stream);
 
+/* mqconv_quantize of several tensors at once, e.g. a layer's activation and
+ * weight before its forward pass (each still quantized once, §III-A, §IV-B):
+ * src[i] -> dst[i] for i < count, every pair exactly as mqconv_quantize
+ * would write it. Tensors that share an element format share one launch, so
+ * a small tensor runs beside a large one instead of after it.
+ * src, dst: host arrays of count entries (read during the call only).
+ * count: 1 .. MQ_QUANTIZE_GROUP_MAX, else MQ_ERR_SHAPE.
+ * Every pair is checked (as mqconv_quantize) before anything is enqueued;
+ * the first failing pair's status is returned. Output buffers of different
+ * pairs must not overlap (their bytes would then be undefined). */
+#define MQ_QUANTIZE_GROUP_MAX 8
+int mqconv_quantize_group(int32_t count, const float* const* src, const mq_mx* dst, void* stream);
+
 /* Channel-batch-first im2col of an already-quantized activation (§IV-A):
  *   X'[ho,wo,n,kh,kw,c] = X[ho*s+kh-p, wo*s+kw-p, n, c]
  * Codes and scales are moved unchanged (no requantization): every

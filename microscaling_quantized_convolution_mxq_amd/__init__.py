@@ -62,6 +62,7 @@ def lib() -> ctypes.CDLL:
             "mqconv_im2col_codes_bytes": (S, [CV, I]),
             "mqconv_im2col_scales_bytes": (S, [CV, I32]),
             "mqconv_quantize": (I, [P, mq_mx, P]),
+            "mqconv_quantize_group": (I, [I32, P, ctypes.POINTER(mq_mx), P]),
             "mqconv_cbf_im2col": (I, [CV, mq_mx, P, P, P]),
             "mqconv_workspace_bytes": (S, [CV, I, I, I]),
             "mqconv_forward": (I, [CV, mq_mx, mq_mx, P, P, S, P]),
@@ -81,7 +82,7 @@ def lib() -> ctypes.CDLL:
 
 
 EXPORTED = ("mqconv_abi_version", "mqconv_status_string", "mqconv_codes_bytes", "mqconv_scales_bytes",
-            "mqconv_im2col_codes_bytes", "mqconv_im2col_scales_bytes", "mqconv_quantize",
+            "mqconv_im2col_codes_bytes", "mqconv_im2col_scales_bytes", "mqconv_quantize", "mqconv_quantize_group",
             "mqconv_cbf_im2col", "mqconv_workspace_bytes", "mqconv_forward", "mqconv_backward_data",
             "mqconv_backward_weight", "mqconv_naive_workspace_bytes", "mqconv_naive_forward",
             "mqconv_naive_backward_data", "mqconv_naive_backward_weight")
@@ -167,6 +168,18 @@ def mqconv_im2col_scales_bytes(shape, bp: int) -> int:
 
 def mqconv_quantize(src, dst: MxTensor, stream=None) -> None:
     _check(lib().mqconv_quantize(_ptr(src), dst.c_struct(), _stream(stream)), "mqconv_quantize")
+
+
+QUANTIZE_GROUP_MAX = 8
+
+
+def mqconv_quantize_group(pairs, stream=None) -> None:
+    """mqconv_quantize of several (src, dst MxTensor) pairs in one call."""
+    pairs = list(pairs)
+    n = len(pairs)
+    srcs = (ctypes.c_void_p * max(1, n))(*[_ptr(p[0]) for p in pairs])
+    dsts = (mq_mx * max(1, n))(*[p[1].c_struct() for p in pairs])
+    _check(lib().mqconv_quantize_group(n, srcs, dsts, _stream(stream)), "mqconv_quantize_group")
 
 
 def mqconv_cbf_im2col(shape, xq: MxTensor, col_codes, col_scales, stream=None) -> None:

@@ -127,7 +127,6 @@ hipError_t launch_backward_weight(const Conv& cv, MxView dy, MxView x, float* dw
   // 8-bit codes are read where quantization left them (K-major staging)
   // when a 16-channel chunk of B stays in one tap and a K-block's lines are
   // the N values of one pixel; otherwise both are first re-laid with runs
-  // along N
   // along N; with 8-bit gradient codes and other activation codes (mixed)
   // only the activation is re-laid
   const bool kext_ok = cv.n <= 32 || cv.n % 32 == 0;

@@ -121,7 +121,8 @@ size_t mqconv_im2col_scales_bytes(const mq_conv* cv, int32_t bp) {
   return (size_t)((long long)c.ho() * c.wo() * c.kh * c.kw * ceil_div(c.n, bp) * ceil_div(c.cin, 32));
 }
 
-int mqconv_quantize(const float* src, mq_mx dst, void* stream) {
+// Checks one quantization request and maps its role to the [A][P][B] x C view.
+static int quantize_req(const float* src, const mq_mx& dst, QReq* r) {
   if (!src || !dst.codes || !dst.scales) return MQ_ERR_NULL;
   if (!fmt_ok(dst.fmt)) return MQ_ERR_FORMAT;
   if (dst.role != MQ_ROLE_ACT && dst.role != MQ_ROLE_GRAD && dst.role != MQ_ROLE_WEIGHT) return MQ_ERR_FORMAT;
@@ -132,8 +133,26 @@ int mqconv_quantize(const float* src, mq_mx dst, void* stream) {
   if (dst.role == MQ_ROLE_WEIGHT) { A = 1; P = dst.d0; B = dst.d1 * dst.d2; }
   else if (dst.block_partner == 1) { A = 1; P = dst.d0 * dst.d1 * dst.d2; B = 1; }  // rows independent
   else { A = dst.d0 * dst.d1; P = dst.d2; B = 1; }
-  return hip_status(launch_quantize(src, static_cast<uint8_t*>(dst.codes), dst.scales, dst.fmt,
-                                    dst.block_partner, A, P, B, dst.d3, (hipStream_t)stream));
+  *r = QReq{src, static_cast<uint8_t*>(dst.codes), dst.scales, dst.fmt, dst.block_partner, A, P, B, dst.d3};
+  return MQ_OK;
+}
+
+int mqconv_quantize(const float* src, mq_mx dst, void* stream) {
+  QReq r;
+  const int e = quantize_req(src, dst, &r);
+  if (e != MQ_OK) return e;
+  return hip_status(launch_quantize(r.src, r.codes, r.scales, r.fmt, r.bp, r.A, r.P, r.B, r.C, (hipStream_t)stream));
+}
+
+int mqconv_quantize_group(int32_t count, const float* const* src, const mq_mx* dst, void* stream) {
+  if (!src || !dst) return MQ_ERR_NULL;
+  if (count < 1 || count > MQ_QUANTIZE_GROUP_MAX) return MQ_ERR_SHAPE;
+  QReq r[MQ_QUANTIZE_GROUP_MAX];
+  for (int i = 0; i < count; i++) {
+    const int e = quantize_req(src[i], dst[i], &r[i]);
+    if (e != MQ_OK) return e;
+  }
+  return hip_status(launch_quantize_group(r, count, (hipStream_t)stream));
 }
 
 int mqconv_cbf_im2col(const mq_conv* cv, mq_mx xq, void* col_codes, uint8_t* col_scales, void* stream) {

@@ -48,6 +48,13 @@ inline long long row_bytes(int fmt, long long C) { return ((C + 31) / 32) * run_
 
 hipError_t launch_quantize(const float* src, uint8_t* codes, uint8_t* scales, int fmt, int bp, int A,
                            int P, int B, int C, hipStream_t st);
+// one tensor of a grouped quantization: [A][P][B] x C view as launch_quantize
+struct QReq {
+  const float* src;
+  uint8_t *codes, *scales;
+  int fmt, bp, A, P, B, C;
+};
+hipError_t launch_quantize_group(const QReq* reqs, int count, hipStream_t st);
 
 hipError_t launch_cbf_im2col(const Conv& cv, MxView x, uint8_t* col_codes, uint8_t* col_scales,
                              hipStream_t st);

@@ -16,6 +16,9 @@
 // written by one wave in consecutive iterations. The block maximum is a
 // cross-lane max; the scaled values are clamped to the format's largest
 // finite value and rounded by the hardware conversion instructions.
+#include <algorithm>
+#include <vector>
+
 #include "mx_common.h"
 #include "mqconv_internal.h"
 
@@ -83,15 +86,18 @@ __device__ __forceinline__ void convert_store_half_run(uint8_t* dst, const float
 // (at most 8 channel blocks): the wave packs them in LDS and writes the
 // tile's bytes as one contiguous stretch, so every store covers whole
 // cache lines (6-bit runs are 24 bytes, which direct stores would split).
+// A workgroup quantizes 4 tiles (one per wave), tiles 4 wg .. 4 wg + 3, and
+// of those the channel blocks cb0, cb0 + cbs, ...; `stage` is the wave's
+// packing buffer (ST).
 constexpr int kStageCB = 8;
+constexpr int kStageBytes = 32 * kStageCB * 32;
 template <int F, int MODE, bool ST>
-__global__ __launch_bounds__(256) void mxq_quantize_kernel(const float* __restrict__ src,
-                                                          uint8_t* __restrict__ codes,
-                                                          uint8_t* __restrict__ scales, int A, int P,
-                                                          int B, int C, int bp, long long ntiles) {
-  __shared__ __attribute__((aligned(16))) uint8_t stage_buf[ST ? 4 : 1][ST ? 32 * kStageCB * 32 : 16];
+__device__ __forceinline__ void quantize_tiles(const float* __restrict__ src, uint8_t* __restrict__ codes,
+                                               uint8_t* __restrict__ scales, int A, int P, int B, int C,
+                                               int bp, long long ntiles, long long wg, int cb0, int cbs,
+                                               uint8_t* stage) {
   const int lane = threadIdx.x & 63;
-  const long long tile = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const long long tile = wg * 4 + (threadIdx.x >> 6);
   if (tile >= ntiles) return;
   const int r = lane >> 1, half = lane & 1;
   const int nCB = (C + 31) / 32;
@@ -127,9 +133,9 @@ __global__ __launch_bounds__(256) void mxq_quantize_kernel(const float* __restri
   const bool vec = (C & 3) == 0;
   constexpr float maxv = Fmt<F>::maxv;
 
-  // blockIdx.y splits the channel blocks of small tensors over workgroups
-  // (gridDim.y is 1 with LDS staging, which needs a tile's whole rows)
-  for (int cb = blockIdx.y; cb < nCB; cb += gridDim.y) {
+  // cbs > 1 splits the channel blocks of small tensors over workgroups
+  // (never with LDS staging, which needs a tile's whole rows)
+  for (int cb = cb0; cb < nCB; cb += cbs) {
     const int c0 = cb * 32 + half * 16;
     float x[16];
     if (row_ok && vec && c0 + 16 <= C) {
@@ -165,7 +171,7 @@ __global__ __launch_bounds__(256) void mxq_quantize_kernel(const float* __restri
 #pragma unroll
     for (int i = 0; i < 16; i++) v[i] = S == 255u ? 0.0f : fminf(fmaxf(x[i] * inv, -maxv), maxv);
     if constexpr (ST) {
-      convert_store_half_run<F>(&stage_buf[threadIdx.x >> 6][r * row_bytes + cb * RB + half * (RB / 2)], v);
+      convert_store_half_run<F>(&stage[r * row_bytes + cb * RB + half * (RB / 2)], v);
       if (row_ok && writes_scale) scales[sidx + cb] = (uint8_t)S;
     } else if (row_ok) {
       convert_store_half_run<F>(codes + row * row_bytes + (long long)cb * RB + half * (RB / 2), v);
@@ -179,44 +185,160 @@ __global__ __launch_bounds__(256) void mxq_quantize_kernel(const float* __restri
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's packed rows are in LDS
     __builtin_amdgcn_wave_barrier();
     const int words = (int)(nvalid * row_bytes / 4);
-    const uint32_t* from = reinterpret_cast<const uint32_t*>(stage_buf[threadIdx.x >> 6]);
+    const uint32_t* from = reinterpret_cast<const uint32_t*>(stage);
     uint32_t* to = reinterpret_cast<uint32_t*>(codes + row0 * row_bytes);
     for (int i = lane; i < words; i += 64) to[i] = from[i];
   }
 }
 
-template <int F, int MODE>
-static hipError_t launch_q(const float* src, uint8_t* codes, uint8_t* scales, int A, int P, int B,
-                           int C, int bp, hipStream_t st) {
-  const long long ntiles = MODE == 2 ? ((long long)A * P + 31) / 32 : (long long)A * B * ((P + 31) / 32);
-  const long long blocks = (ntiles + 3) / 4;
-  if (B == 1 && (C + 31) / 32 <= kStageCB)
-    hipLaunchKernelGGL((mxq_quantize_kernel<F, MODE, true>), dim3((unsigned)blocks), dim3(256), 0, st, src,
-                       codes, scales, A, P, B, C, bp, ntiles);
-  else  // small tensors: one workgroup per channel block as well (one memory round trip)
-    hipLaunchKernelGGL((mxq_quantize_kernel<F, MODE, false>),
-                       dim3((unsigned)blocks, blocks < 512 ? (unsigned)((C + 31) / 32) : 1u), dim3(256), 0, st, src,
-                       codes, scales, A, P, B, C, bp, ntiles);
-  return hipGetLastError();
+template <int F, int MODE, bool ST>
+__global__ __launch_bounds__(256) void mxq_quantize_kernel(const float* __restrict__ src,
+                                                          uint8_t* __restrict__ codes,
+                                                          uint8_t* __restrict__ scales, int A, int P,
+                                                          int B, int C, int bp, long long ntiles) {
+  __shared__ __attribute__((aligned(16))) uint8_t stage_buf[ST ? 4 : 1][ST ? kStageBytes : 16];
+  quantize_tiles<F, MODE, ST>(src, codes, scales, A, P, B, C, bp, ntiles, blockIdx.x, blockIdx.y, gridDim.y,
+                              stage_buf[ST ? threadIdx.x >> 6 : 0]);
+}
+
+// Several tensors of one element format in one launch (a small tensor, such
+// as a weight, then runs beside a large one instead of after it): member i
+// owns workgroups [begin, begin + nbx * gy) of the 1-D grid, nbx workgroups
+// of tiles for each of its gy channel-block phases.
+struct QMember {
+  const float* src;
+  uint8_t *codes, *scales;
+  long long ntiles;
+  int A, P, B, C, bp, variant, nbx, gy, begin;  // variant = 2 * MODE + ST
+};
+constexpr int kQGroupMax = 8;
+struct QGroup {
+  QMember m[kQGroupMax];
+  int count;
+};
+
+template <int F>
+__global__ __launch_bounds__(256) void mxq_quantize_group_kernel(QGroup g) {
+  __shared__ __attribute__((aligned(16))) uint8_t stage_buf[4][kStageBytes];
+  const int b = blockIdx.x;
+  QMember q = g.m[0];
+#pragma unroll
+  for (int j = 1; j < kQGroupMax; j++)
+    if (j < g.count && b >= g.m[j].begin) q = g.m[j];
+  const int lb = b - q.begin, by = lb / q.nbx, bx = lb - by * q.nbx;
+  uint8_t* stage = stage_buf[threadIdx.x >> 6];
+#define MQ_QT(MODE, ST) \
+  quantize_tiles<F, MODE, ST>(q.src, q.codes, q.scales, q.A, q.P, q.B, q.C, q.bp, q.ntiles, bx, by, q.gy, stage)
+  switch (q.variant) {
+    case 0: MQ_QT(0, false); break;
+    case 1: MQ_QT(0, true); break;
+    case 2: MQ_QT(1, false); break;
+    case 3: MQ_QT(1, true); break;
+    case 4: MQ_QT(2, false); break;
+    default: MQ_QT(2, true); break;
+  }
+#undef MQ_QT
+}
+
+// Block geometry of one tensor: MODE 0 for line blocks, 2 when a pixel's
+// partner rows (P < 32 dividing 32) form whole square blocks, else 1; LDS
+// staging (ST) when rows are consecutive and short; small tensors also
+// spread their channel blocks over workgroups (gy, one memory round trip).
+struct QPlan {
+  int mode;
+  bool st;
+  long long ntiles, blocks;
+  int gy;
+};
+static QPlan quantize_plan(int A, int P, int B, int C, int bp) {
+  QPlan q;
+  q.mode = bp != 32 ? 0 : (B == 1 && P < 32 && (32 % P) == 0) ? 2 : 1;
+  q.ntiles = q.mode == 2 ? ((long long)A * P + 31) / 32 : (long long)A * B * ((P + 31) / 32);
+  q.blocks = (q.ntiles + 3) / 4;
+  q.st = B == 1 && (C + 31) / 32 <= kStageCB;
+  q.gy = !q.st && q.blocks < 512 ? (C + 31) / 32 : 1;
+  return q;
+}
+
+template <int F, int MODE, bool ST>
+static void launch_one(const QReq& r, const QPlan& q, hipStream_t st) {
+  hipLaunchKernelGGL((mxq_quantize_kernel<F, MODE, ST>), dim3((unsigned)q.blocks, (unsigned)q.gy), dim3(256), 0,
+                     st, r.src, r.codes, r.scales, r.A, r.P, r.B, r.C, r.bp, q.ntiles);
 }
 
 template <int F>
-static hipError_t launch_f(const float* src, uint8_t* codes, uint8_t* scales, int A, int P, int B,
-                           int C, int bp, hipStream_t st) {
-  if (bp != 32) return launch_q<F, 0>(src, codes, scales, A, P, B, C, bp, st);
-  if (B == 1 && P < 32 && (32 % P) == 0) return launch_q<F, 2>(src, codes, scales, A, P, B, C, bp, st);
-  return launch_q<F, 1>(src, codes, scales, A, P, B, C, bp, st);
+static hipError_t launch_f(const QReq& r, hipStream_t st) {
+  const QPlan q = quantize_plan(r.A, r.P, r.B, r.C, r.bp);
+  switch (2 * q.mode + q.st) {
+    case 0: launch_one<F, 0, false>(r, q, st); break;
+    case 1: launch_one<F, 0, true>(r, q, st); break;
+    case 2: launch_one<F, 1, false>(r, q, st); break;
+    case 3: launch_one<F, 1, true>(r, q, st); break;
+    case 4: launch_one<F, 2, false>(r, q, st); break;
+    default: launch_one<F, 2, true>(r, q, st); break;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_quantize(const float* src, uint8_t* codes, uint8_t* scales, int fmt, int bp, int A,
                            int P, int B, int C, hipStream_t st) {
+  const QReq r{src, codes, scales, fmt, bp, A, P, B, C};
   switch (fmt) {
-    case 0: return launch_f<0>(src, codes, scales, A, P, B, C, bp, st);
-    case 1: return launch_f<1>(src, codes, scales, A, P, B, C, bp, st);
-    case 2: return launch_f<2>(src, codes, scales, A, P, B, C, bp, st);
-    case 3: return launch_f<3>(src, codes, scales, A, P, B, C, bp, st);
-    default: return launch_f<4>(src, codes, scales, A, P, B, C, bp, st);
+    case 0: return launch_f<0>(r, st);
+    case 1: return launch_f<1>(r, st);
+    case 2: return launch_f<2>(r, st);
+    case 3: return launch_f<3>(r, st);
+    default: return launch_f<4>(r, st);
   }
+}
+
+// One grouped launch per element format present (and per kQGroupMax
+// members); members in increasing size, so the small ones are dispatched
+// first and finish inside the large ones' time. A format with one member
+// takes the single-tensor launch.
+hipError_t launch_quantize_group(const QReq* reqs, int count, hipStream_t st) {
+  for (int f = 0; f < 5; f++) {
+    std::vector<int> idx;
+    for (int i = 0; i < count; i++)
+      if (reqs[i].fmt == f) idx.push_back(i);
+    if (idx.empty()) continue;
+    if (idx.size() == 1) {
+      const hipError_t e = launch_quantize(reqs[idx[0]].src, reqs[idx[0]].codes, reqs[idx[0]].scales, f,
+                                           reqs[idx[0]].bp, reqs[idx[0]].A, reqs[idx[0]].P, reqs[idx[0]].B,
+                                           reqs[idx[0]].C, st);
+      if (e != hipSuccess) return e;
+      continue;
+    }
+    std::vector<QPlan> plans(count);
+    for (int i : idx) plans[i] = quantize_plan(reqs[i].A, reqs[i].P, reqs[i].B, reqs[i].C, reqs[i].bp);
+    std::stable_sort(idx.begin(), idx.end(),
+                     [&](int a, int b) { return plans[a].blocks * plans[a].gy < plans[b].blocks * plans[b].gy; });
+    for (size_t c0 = 0; c0 < idx.size(); c0 += kQGroupMax) {
+      QGroup g{};
+      long long total = 0;
+      g.count = (int)std::min<size_t>(kQGroupMax, idx.size() - c0);
+      for (int k = 0; k < g.count; k++) {
+        const QReq& r = reqs[idx[c0 + k]];
+        const QPlan& q = plans[idx[c0 + k]];
+        QMember& m = g.m[k];
+        m.src = r.src; m.codes = r.codes; m.scales = r.scales; m.ntiles = q.ntiles;
+        m.A = r.A; m.P = r.P; m.B = r.B; m.C = r.C; m.bp = r.bp;
+        m.variant = 2 * q.mode + q.st; m.nbx = (int)q.blocks; m.gy = q.gy; m.begin = (int)total;
+        total += q.blocks * q.gy;
+        if (total > 0x7fffffffLL) return hipErrorInvalidValue;
+      }
+      switch (f) {
+        case 0: hipLaunchKernelGGL(mxq_quantize_group_kernel<0>, dim3((unsigned)total), dim3(256), 0, st, g); break;
+        case 1: hipLaunchKernelGGL(mxq_quantize_group_kernel<1>, dim3((unsigned)total), dim3(256), 0, st, g); break;
+        case 2: hipLaunchKernelGGL(mxq_quantize_group_kernel<2>, dim3((unsigned)total), dim3(256), 0, st, g); break;
+        case 3: hipLaunchKernelGGL(mxq_quantize_group_kernel<3>, dim3((unsigned)total), dim3(256), 0, st, g); break;
+        default: hipLaunchKernelGGL(mxq_quantize_group_kernel<4>, dim3((unsigned)total), dim3(256), 0, st, g); break;
+      }
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
 }
 
 }  // namespace mq

@@ -64,8 +64,7 @@ def run_step(workload: str, path: str) -> None:
             ws1 = torch.empty(max(1, mq.mqconv_workspace_bytes(s, 1, wl.fdy, wl.fw)), dtype=torch.uint8, device="cuda")
             ws2 = torch.empty(max(1, mq.mqconv_workspace_bytes(s, 2, wl.fdy, wl.fx)), dtype=torch.uint8, device="cuda")
             torch.cuda.synchronize()
-            mq.mqconv_quantize(X, xq)
-            mq.mqconv_quantize(Wt, wq)
+            mq.mqconv_quantize_group([(X, xq), (Wt, wq)])
             mq.mqconv_quantize(DY, gq)
             mq.mqconv_forward(s, xq, wq, y)
             mq.mqconv_backward_data(s, gq, wq, dx, ws1)

@@ -26,7 +26,7 @@ def _declared():
 
 def test_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 16
+    assert len(names) == 17
     out = subprocess.run(["nm", "-D", "--defined-only", mq.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT\s+(mqconv_\w+)", out))
     assert set(names) <= exported
@@ -99,6 +99,13 @@ def test_validation_errors_without_gpu():
     assert _call(mq.mqconv_quantize, FAKE, _mx(mq.ROLE_ACT, (0, s.w, s.n, s.cin))) == -2
     assert _call(mq.mqconv_quantize, FAKE, _mx(mq.ROLE_ACT, (s.h, s.w, s.n, s.cin), codes=FAKE + 8)) == -4
     assert _call(mq.mqconv_quantize, FAKE + 2, x) == -4
+    # grouped quantize: every pair is checked before anything is enqueued
+    assert _call(mq.mqconv_quantize_group, []) == -2
+    assert _call(mq.mqconv_quantize_group, [(FAKE, x)] * (mq.QUANTIZE_GROUP_MAX + 1)) == -2
+    assert _call(mq.mqconv_quantize_group, [(FAKE, x), (0, w)]) == -1
+    assert _call(mq.mqconv_quantize_group, [(FAKE, x), (FAKE, _mx(mq.ROLE_WEIGHT, (s.cout, 3, 3, s.cin), fmt=7))]) == -3
+    assert _call(mq.mqconv_quantize_group, [(FAKE, x), (FAKE + 2, dy)]) == -4
+    assert mq.lib().mqconv_quantize_group(1, None, None, None) == -1
     # im2col
     assert _call(mq.mqconv_cbf_im2col, s, x, 0, FAKE) == -1
     assert _call(mq.mqconv_cbf_im2col, s, w, FAKE, FAKE) == -3

@@ -94,6 +94,53 @@ def test_quantize_c3_layers(layer):
     _check_quant(dy, mq.ROLE_GRAD, wl.fdy, wl.bp, f"c3 L{layer} dY")
 
 
+def _check_group(items, label):
+    """mqconv_quantize_group over (x, role, fmt, bp) items: every tensor's
+    codes and scales equal the oracle's (and so mqconv_quantize's)."""
+    say(f"quantize_group {label}: " + ", ".join(f"role={r} fmt={f} bp={b} {x.shape}" for x, r, f, b in items))
+    ts = []
+    for x, role, fmt, bp in items:
+        t = mq.MxTensor.empty(role, fmt, bp, x.shape)
+        t.codes.fill_(0xAB)
+        t.scales.fill_(0xAB)
+        ts.append((dev(x.astype(np.float32)), t))
+    mq.mqconv_quantize_group(ts)
+    for i, ((x, role, fmt, bp), (_, t)) in enumerate(zip(items, ts)):
+        oc, os_ = oracle_packed(x, role, fmt, bp)
+        np.testing.assert_array_equal(host(t.scales), os_.reshape(-1), err_msg=f"scales {label} #{i}")
+        np.testing.assert_array_equal(host(t.codes), oc.reshape(-1), err_msg=f"codes {label} #{i}")
+
+
+def test_quantize_group_small_mixed():
+    """Members of one format share a launch (every block geometry: line
+    blocks, square blocks over 32 rows, square blocks over pixels, LDS
+    staging and channel-block spreading); other formats launch apart."""
+    rng = np.random.default_rng(42)
+
+    def r(*shp):
+        return (rng.standard_normal(shp) * np.exp(rng.uniform(-6, 6, shp[:-1] + (1,)))).astype(np.float32)
+
+    items = [
+        (r(3, 2, 33, 45), mq.ROLE_ACT, 0, 32),      # square blocks, 33 partner rows (ragged)
+        (r(40, 3, 3, 70), mq.ROLE_WEIGHT, 0, 32),   # weight, channel blocks spread
+        (r(2, 3, 16, 64), mq.ROLE_GRAD, 0, 32),     # a pixel's 16 rows form a block
+        (r(4, 5, 7, 300), mq.ROLE_ACT, 0, 1),       # line blocks, 10 channel blocks (no staging)
+        (r(5, 3, 3, 20), mq.ROLE_WEIGHT, 2, 32),    # alone in its format
+        (r(3, 3, 8, 96), mq.ROLE_ACT, 4, 32),
+        (r(6, 3, 1, 40), mq.ROLE_WEIGHT, 4, 1),
+    ]
+    _check_group(items, "mixed")
+    _check_group(items[:1], "single")
+
+
+@pytest.mark.parametrize("key", ["c2", "c4", "c5"])
+def test_quantize_group_full_configs(key):
+    """A layer's activation and weight quantized in one call, as before the
+    forward pass."""
+    wl, (x, w, dy) = _full_inputs(key)
+    _check_group([(x, mq.ROLE_ACT, wl.fx, wl.bp), (w, mq.ROLE_WEIGHT, wl.fw, wl.bp)], key)
+
+
 def _check_im2col(shape, x, fmt, bp, label, sample_rows=None):
     say(f"im2col {label} shape={shape.as_tuple()} fmt={fmt} bp={bp}")
     t = gpu_quantize(x, mq.ROLE_ACT, fmt, bp)
