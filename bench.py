@@ -14,7 +14,9 @@ TFLOP/s of the whole step (algorithmic FLOPs of the three GEMMs / step
 time). Every entry point is also timed on its own (a graph of repeated
 calls on rotating buffer sets, HIP events on the stream the kernels run
 on); `roofline` covers the entry point that takes the most time per step,
-with its algorithmic bytes or FLOPs per call. `cpu_baseline` times the CPU
+with its algorithmic bytes or FLOPs per call. The forward whose epilogue
+writes Y as MX codes (`mqconv_forward_mx`) is timed the same way and listed
+with `in_step: false`. `cpu_baseline` times the CPU
 oracle on a bounded sample of the same workload.
 
 Prints one JSON line.
@@ -38,12 +40,15 @@ HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "fp6fp4": 10100.0}
 CSRC = os.path.join(ROOT, "microscaling_quantized_convolution_mxq_amd", "csrc")
 CALLS = ["quantize_xw", "quantize_dy", "cbf_im2col", "forward", "backward_data", "backward_weight"]
+# timed on their own too, but not part of the step: the forward whose epilogue
+# writes Y as MX codes and scales (the next layer's activation) instead of fp32
+EXTRA = ["forward_mx"]
 # kernels each entry point launches (see the launchers in csrc/)
 CALL_KERNELS = {
     # X and W share one launch when their formats match, else one launch each
     "quantize_xw": ["mxq_quantize_group_kernel (same format; else 2 x mxq_quantize_kernel)"],
     "quantize_dy": ["mxq_quantize_kernel"], "cbf_im2col": ["cbf_im2col_kernel"],
-    "forward": ["mx_gemm_kernel<FwdProb>"],
+    "forward": ["mx_gemm_kernel<FwdProb>"], "forward_mx": ["mx_gemm_kernel<FwdMxProb>"],
     # 8-bit codes are read in place; other formats are first re-laid by transpose_codes_kernel
     "backward_data": ["mx_gemm_kernel<DgradNatProb> (8-bit W; else transpose_codes_kernel + mx_gemm_kernel<DgradProb>)"],
     "backward_weight": ["mx_gemm_kernel<WgradNatProb> (8-bit dY and X; 8-bit dY only: transpose_codes_kernel (X) + "
@@ -103,6 +108,7 @@ def main():
         d["cc"] = torch.empty(mq.mqconv_im2col_codes_bytes(s, wl.fx), dtype=torch.uint8, device="cuda")
         d["cs"] = torch.empty(mq.mqconv_im2col_scales_bytes(s, bp), dtype=torch.uint8, device="cuda")
         d["y"] = torch.empty((s.ho, s.wo, s.n, s.cout), device="cuda")
+        d["yq"] = mq.MxTensor.empty(mq.ROLE_ACT, wl.fx, bp, (s.ho, s.wo, s.n, s.cout))
         d["dx"] = torch.empty(x.shape, device="cuda")
         d["dw"] = torch.empty(w.shape, device="cuda")
         d["ws1"] = torch.empty(max(1, mq.mqconv_workspace_bytes(s, 1, wl.fdy, wl.fw)), dtype=torch.uint8, device="cuda")
@@ -124,6 +130,8 @@ def main():
             mq.mqconv_cbf_im2col(s, d["xq"], d["cc"], d["cs"])
         elif name == "forward":
             mq.mqconv_forward(s, d["xq"], d["wq"], d["y"])
+        elif name == "forward_mx":
+            mq.mqconv_forward_mx(s, d["xq"], d["wq"], d["yq"])
         elif name == "backward_data":
             mq.mqconv_backward_data(s, d["gq"], d["wq"], d["dx"], d["ws1"])
         elif name == "backward_weight":
@@ -189,7 +197,7 @@ def main():
     # call touches, with Rc chosen so that those copies exceed the 256 MB
     # Infinity Cache as the step's sets do (no call reads cache-resident inputs).
     NEED = {"quantize_xw": ("x", "xq", "w", "wq"), "quantize_dy": ("dy", "gq"),
-            "cbf_im2col": ("xq", "cc", "cs"), "forward": ("xq", "wq", "y"),
+            "cbf_im2col": ("xq", "cc", "cs"), "forward": ("xq", "wq", "y"), "forward_mx": ("xq", "wq", "yq"),
             "backward_data": ("gq", "wq", "dx", "ws1"), "backward_weight": ("gq", "xq", "dw", "ws2")}
 
     def nbytes(v):
@@ -201,7 +209,7 @@ def main():
         return v.clone()
 
     per_call = {}
-    for c in CALLS:
+    for c in CALLS + EXTRA:
         call_bytes = sum(nbytes(sets[0][k]) for k in NEED[c])
         Rc = int(min(64, max(2, np.ceil(args.rotate_mb * 1e6 / call_bytes))))
         csets = [{k: clone(sets[0][k]) for k in NEED[c]} for _ in range(Rc)]
@@ -227,21 +235,26 @@ def main():
     wq_b = mq.mqconv_codes_bytes(mq.ROLE_WEIGHT, wl.fw, *w.shape) + mq.mqconv_scales_bytes(mq.ROLE_WEIGHT, bp, *w.shape)
     gq_b = mq.mqconv_codes_bytes(mq.ROLE_GRAD, wl.fdy, *dy.shape) + mq.mqconv_scales_bytes(mq.ROLE_GRAD, bp, *dy.shape)
     col_b = mq.mqconv_im2col_codes_bytes(s, wl.fx) + mq.mqconv_im2col_scales_bytes(s, bp)
+    yq_dims = (s.ho, s.wo, s.n, s.cout)
+    yq_b = mq.mqconv_codes_bytes(mq.ROLE_ACT, wl.fx, *yq_dims) + mq.mqconv_scales_bytes(mq.ROLE_ACT, bp, *yq_dims)
     # bytes each call must move at least once (inputs read, outputs written)
     alg_bytes = {
         "quantize_xw": 4 * nx + xq_b + 4 * nw + wq_b, "quantize_dy": 4 * ng + gq_b,
         "cbf_im2col": xq_b + col_b,
         "forward": xq_b + wq_b + 4 * ng, "backward_data": gq_b + wq_b + 4 * nx, "backward_weight": gq_b + xq_b + 4 * nw,
+        "forward_mx": xq_b + wq_b + yq_b,
     }
-    alg_flop = {"forward": flop, "backward_data": flop, "backward_weight": flop}
+    alg_flop = {"forward": flop, "backward_data": flop, "backward_weight": flop, "forward_mx": flop}
+    step_gemms = ("forward", "backward_data", "backward_weight")
 
     def mfma_peak(fa, fb):
         return MFMA_PEAK_TFLOPS["fp6fp4"] if (fa >= 2 and fb >= 2) else MFMA_PEAK_TFLOPS["fp8"]
 
-    call_peak = {"forward": mfma_peak(wl.fx, wl.fw), "backward_data": mfma_peak(wl.fdy, wl.fw),
+    call_peak = {"forward": mfma_peak(wl.fx, wl.fw), "forward_mx": mfma_peak(wl.fx, wl.fw),
+                 "backward_data": mfma_peak(wl.fdy, wl.fw),
                  "backward_weight": mfma_peak(wl.fdy, wl.fx)}
     kernels = {}
-    for c in CALLS:
+    for c in CALLS + EXTRA:
         t = per_call[c] * 1e-3
         k = {"ms": round(per_call[c], 5), "GB/s": round(alg_bytes[c] / t / 1e9, 1),
              "hbm_frac": round(alg_bytes[c] / t / 1e9 / HBM_PEAK_GBS, 4), "launches": CALL_KERNELS[c]}
@@ -252,6 +265,7 @@ def main():
             k.update({"TFLOP/s": round(alg_flop[c] / t / 1e12, 2), "mfma_frac": round(alg_flop[c] / t / 1e12 / peak, 4),
                       "attainable_TFLOP/s": round(attainable, 1),
                       "attainable_frac": round(alg_flop[c] / t / 1e12 / attainable, 4)})
+        k["in_step"] = c in CALLS
         kernels[c] = k
 
     dominant = max(CALLS, key=lambda c: per_call[c])
@@ -275,7 +289,7 @@ def main():
 
     q_im_bytes = sum(alg_bytes[c] for c in ("quantize_xw", "quantize_dy", "cbf_im2col"))
     q_im_ms = sum(per_call[c] for c in ("quantize_xw", "quantize_dy", "cbf_im2col"))
-    gemm_ms = sum(per_call[c] for c in alg_flop)
+    gemm_ms = sum(per_call[c] for c in step_gemms)
 
     # ---- naive comparison path (not part of the step) ------------------------
     naive = None

@@ -205,6 +205,18 @@ size_t mqconv_workspace_bytes(const mq_conv* cv, int op, mq_elem fa, mq_elem fb)
 int mqconv_forward(const mq_conv* cv, mq_mx xq, mq_mx wq, float* y, void* ws, size_t ws_bytes,
                    void* stream);
 
+/* mqconv_forward whose output is Y MX-quantized (the next layer's
+ * activation, quantized once: §III-A, §IV-B) instead of fp32: yq receives
+ * exactly the codes and scales that mqconv_quantize of mqconv_forward's
+ * fp32 Y would write, without the fp32 Y ever reaching memory.
+ *   yq: ACT (Ho, Wo, N, Cout), any format; bp 1, or bp 32 when N is a
+ *       multiple of 32 or divides 32 (otherwise MQ_ERR_UNSUPPORTED: a block
+ *       would straddle two of the kernel's 32-row output groups). Its code
+ *       and scale buffers are fully overwritten.
+ *   xq, wq, ws, ws_bytes, errors: as mqconv_forward. */
+int mqconv_forward_mx(const mq_conv* cv, mq_mx xq, mq_mx wq, mq_mx yq, void* ws, size_t ws_bytes,
+                      void* stream);
+
 /* Input-gradient GEMM G_X' = W_f^T . G_Yf (§IV-B) folded back to G_X
  * (Eq. 2: convolution of G_Y with the channel-transposed kernel).
  *   dyq: GRAD (Ho, Wo, N, Cout), any bp;  wq: WEIGHT, bp must be 32

@@ -66,6 +66,7 @@ def lib() -> ctypes.CDLL:
             "mqconv_cbf_im2col": (I, [CV, mq_mx, P, P, P]),
             "mqconv_workspace_bytes": (S, [CV, I, I, I]),
             "mqconv_forward": (I, [CV, mq_mx, mq_mx, P, P, S, P]),
+            "mqconv_forward_mx": (I, [CV, mq_mx, mq_mx, mq_mx, P, S, P]),
             "mqconv_backward_data": (I, [CV, mq_mx, mq_mx, P, P, S, P]),
             "mqconv_backward_weight": (I, [CV, mq_mx, mq_mx, P, P, S, P]),
             "mqconv_naive_workspace_bytes": (S, [CV, I, I, I]),
@@ -83,7 +84,7 @@ def lib() -> ctypes.CDLL:
 
 EXPORTED = ("mqconv_abi_version", "mqconv_status_string", "mqconv_codes_bytes", "mqconv_scales_bytes",
             "mqconv_im2col_codes_bytes", "mqconv_im2col_scales_bytes", "mqconv_quantize", "mqconv_quantize_group",
-            "mqconv_cbf_im2col", "mqconv_workspace_bytes", "mqconv_forward", "mqconv_backward_data",
+            "mqconv_cbf_im2col", "mqconv_workspace_bytes", "mqconv_forward", "mqconv_forward_mx", "mqconv_backward_data",
             "mqconv_backward_weight", "mqconv_naive_workspace_bytes", "mqconv_naive_forward",
             "mqconv_naive_backward_data", "mqconv_naive_backward_weight")
 
@@ -201,6 +202,12 @@ def mqconv_forward(shape, xq: MxTensor, wq: MxTensor, y, ws=None, stream=None) -
     p, n = _ws(ws)
     _check(lib().mqconv_forward(ctypes.byref(_conv(shape)), xq.c_struct(), wq.c_struct(), _ptr(y), p, n,
                                 _stream(stream)), "mqconv_forward")
+
+
+def mqconv_forward_mx(shape, xq: MxTensor, wq: MxTensor, yq: MxTensor, ws=None, stream=None) -> None:
+    p, n = _ws(ws)
+    _check(lib().mqconv_forward_mx(ctypes.byref(_conv(shape)), xq.c_struct(), wq.c_struct(), yq.c_struct(), p, n,
+                                   _stream(stream)), "mqconv_forward_mx")
 
 
 def mqconv_backward_data(shape, dyq: MxTensor, wq: MxTensor, dx, ws=None, stream=None) -> None:

@@ -3,7 +3,9 @@
 
 namespace mq {
 
-hipError_t launch_forward(const Conv& cv, MxView x, MxView w, float* y, void*, size_t, hipStream_t st) {
+// out != nullptr: only fill *out with the problem (no launch)
+hipError_t launch_forward(const Conv& cv, MxView x, MxView w, float* y, void*, size_t, hipStream_t st,
+                          FwdProb* out) {
   FwdProb p;
   p.xc = x.codes; p.xs = x.scales; p.wc = w.codes; p.ws = w.scales; p.y = y;
   p.N = cv.n; p.H = cv.h; p.W = cv.w; p.Cin = cv.cin; p.Cout = cv.cout; p.KW = cv.kw;
@@ -25,7 +27,15 @@ hipError_t launch_forward(const Conv& cv, MxView x, MxView w, float* y, void*, s
   p.khalf = cv.cin <= 16;
   p.ga = scale_group_rows(x.bp, cv.n);
   p.gb = w.bp == 32 ? 32 : 0;
+  if (out) {
+    *out = p;
+    return hipSuccess;
+  }
   return launch_tiled(x.fmt, w.fmt, p, p.M, cv.cout, 1, st);
+}
+
+hipError_t launch_forward(const Conv& cv, MxView x, MxView w, float* y, void* ws, size_t ws_bytes, hipStream_t st) {
+  return launch_forward(cv, x, w, y, ws, ws_bytes, st, nullptr);
 }
 
 

@@ -125,6 +125,22 @@ struct FwdProb {
   __device__ int row_run(const Ctx&, int) const { return 1 << 30; }
 };
 
+// Forward whose epilogue MX-quantizes Y (an activation [Ho][Wo][N][Cout],
+// quantized as a separate quantization of the fp32 Y would do it) instead of
+// writing fp32: blocks of 32 channels x (1 row: ymode 0; the 32 rows of a
+// 32-row group within one pixel: ymode 1, N % 32 == 0; each pixel's N rows:
+// ymode 2, N dividing 32), so every block lies inside one 32-row strip of a
+// tile and one 32-column block of it.
+struct FwdMxProb : FwdProb {
+  uint8_t *yc, *ys;
+  int yfmt, ymode, yrb, ynPB, ynCB;
+  static constexpr bool kMxOut = true;
+};
+template <class P, class = void>
+struct MxOut : std::false_type {};
+template <class P>
+struct MxOut<P, std::void_t<decltype(P::kMxOut)>> : std::bool_constant<P::kMxOut> {};
+
 // Backward-data: rows of parity class z are h = hq*sh + ph_c, w = wq*sw + pw_c
 // (and all n); the taps reaching them are kh = kh0 + sh*ih, kw = kw0 + sw*iw,
 // from output pixel (ho0 - ih, wo0 - iw). A step is Cout blocks (v, v+1) of
@@ -601,6 +617,99 @@ __device__ __forceinline__ void stage_barrier() {
 // NG times the K range with NG times the waves.
 // At least two waves per SIMD: the register budget (VGPRs + accumulation
 // registers) stays within 256, so two 256x128 workgroups share a CU.
+// Maximum over aligned groups of g lanes (g = 2, 4, ..., 64, uniform), every
+// lane of a group receiving it: swaps within quads, mirrors within 8 and 16
+// lanes (DPP), a swizzle across the two 16-lane rows of 32 lanes, and the two
+// wave halves.
+template <int CTRL>
+__device__ __forceinline__ uint32_t max_dpp(uint32_t a) {
+  return max(a, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ uint32_t group_max(uint32_t a, int g) {
+  a = max_dpp<0xB1>(a);                // quad_perm [1,0,3,2]: lane ^ 1
+  if (g >= 4) a = max_dpp<0x4E>(a);    // quad_perm [2,3,0,1]: lane ^ 2
+  if (g >= 8) a = max_dpp<0x141>(a);   // row_half_mirror: 7 - lane within 8
+  if (g >= 16) a = max_dpp<0x140>(a);  // row_mirror: 15 - lane within 16
+  if (g >= 32) a = max(a, (uint32_t)__builtin_amdgcn_ds_swizzle((int)a, 0x401F));  // lane ^ 16 within 32
+  if (g >= 64) a = max((uint32_t)__builtin_amdgcn_readlane((int)a, 0), (uint32_t)__builtin_amdgcn_readlane((int)a, 32));
+  return a;
+}
+
+// MX epilogue of one 32-row strip (rows ms.., columns c0.. of the wave, in
+// LDS with pitch EP floats): lane l takes row l/2 and the 16 channels
+// (l%2)*16.. of each 32-column block; the block maximum is a cross-lane
+// maximum over the lanes of the block's rows; codes and scale bytes follow
+// the element rule of the quantizer (scale_clamp16, convert_store_half_run).
+// The codes are packed in LDS (cst: 32 rows of TN runs) and leave as
+// consecutive dwords of each row segment (whole rows are one contiguous
+// stretch), not as scattered half runs.
+// LEAN (tiles whose accumulators already fill most registers): one block at
+// a time and one copy piece at a time, so the epilogue needs few registers.
+template <int F, int TN, bool LEAN>
+__device__ __forceinline__ void mx_store_strip(const FwdMxProb& p, const float* strip, int EP, int ms, int c0,
+                                               int lane, uint8_t* cst) {
+  constexpr int RB = run_bytes_of(F), SEG = TN * RB;
+  const int r = lane >> 1, half = lane & 1;
+  const int m = ms + r;
+  const int cb0 = c0 >> 5;
+  const int nb = min(TN, p.ynCB - cb0);  // blocks of this wave inside the padded row (uniform)
+  const int glanes = p.ymode == 0 ? 2 : (p.ymode == 1 ? 64 : 2 * p.N);  // lanes of one block
+  typedef float v4f __attribute__((ext_vector_type(4)));
+#pragma unroll(LEAN ? 1 : TN)
+  for (int j = 0; j < TN; j++) {
+    if (j >= nb) break;  // uniform
+    float x[16];
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      const v4f t = *reinterpret_cast<const v4f*>(strip + r * EP + j * 32 + half * 16 + 4 * k);
+      x[4 * k] = t[0]; x[4 * k + 1] = t[1]; x[4 * k + 2] = t[2]; x[4 * k + 3] = t[3];
+    }
+    uint32_t a = 0;
+#pragma unroll
+    for (int i = 0; i < 16; i++) a = max(a, __float_as_uint(x[i]) & 0x7fffffffu);
+    a = group_max(a, glanes);
+    const uint32_t S = scale_byte_from_amax<F>(a);
+    float v[16];
+    scale_clamp16<F>(x, S, v);
+    convert_store_half_run<F>(cst + r * SEG + j * RB + half * (RB / 2), v);
+    const bool first = p.ymode == 0 ? half == 0 : (p.ymode == 1 ? lane == 0 : (lane & (2 * p.N - 1)) == 0);
+    if (first && m < p.M) {
+      const int pix = (int)fdiv((unsigned)m, p.dN), n = m - pix * p.N;
+      const long long blk = p.ymode == 0 ? (long long)m : (long long)pix * p.ynPB + (n >> 5);
+      p.ys[blk * p.ynCB + cb0 + j] = (uint8_t)S;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the packed codes are in LDS (same wave)
+  __builtin_amdgcn_wave_barrier();
+  // row segments: nb runs of each of the 32 rows, as VW-byte pieces (every
+  // run, row and segment start is a multiple of VW)
+  constexpr int VW = RB % 16 == 0 ? 16 : 8;
+  typedef uint32_t vw_t __attribute__((ext_vector_type(VW / 4)));
+  if (!LEAN && nb == TN) {  // the usual case: all reads first, then all stores
+    constexpr int PR = SEG / VW, IT = (32 * PR + 63) / 64;
+    vw_t val[IT];
+#pragma unroll
+    for (int it = 0; it < IT; it++) {
+      const int d = min(it * 64 + lane, 32 * PR - 1), row = d / PR, off = d - row * PR;
+      val[it] = *reinterpret_cast<const vw_t*>(cst + row * SEG + off * VW);
+    }
+#pragma unroll
+    for (int it = 0; it < IT; it++) {
+      const int d = it * 64 + lane, row = d / PR, off = d - row * PR;
+      if (d < 32 * PR && ms + row < p.M)
+        *reinterpret_cast<vw_t*>(p.yc + (long long)(ms + row) * p.yrb + cb0 * RB + off * VW) = val[it];
+    }
+  } else {
+    const int pr = nb * RB / VW;
+    for (int d = lane; d < 32 * pr; d += 64) {
+      const int row = d / pr, off = d - row * pr;
+      if (ms + row < p.M)
+        *reinterpret_cast<vw_t*>(p.yc + (long long)(ms + row) * p.yrb + cb0 * RB + off * VW) =
+            *reinterpret_cast<const vw_t*>(cst + row * SEG + off * VW);
+    }
+  }
+}
+
 template <int FA, int FB, class P, int WM, int WN, int TM, int TN, int NS, bool GS, bool KH, int KPS, int NG>
 __global__ __launch_bounds__(256 * NG) __attribute__((amdgpu_waves_per_eu(2))) void mx_gemm_kernel(P prob) {
   static_assert(!KH || (FA <= 1 && FB <= 1), "half K-blocks only for 8-bit codes");
@@ -629,7 +738,9 @@ __global__ __launch_bounds__(256 * NG) __attribute__((amdgpu_waves_per_eu(2))) v
   constexpr int ZERO = DUMMY + 1024;  // KH: 16 zero bytes for the empty upper pieces
   constexpr int STRIP = 32 * (TN * 32 + 8) * 4;  // one wave's epilogue strip (bytes)
   constexpr int XCH = NG > 1 ? 4 * TM * TN * 16 * 64 * 4 : 0;  // group 1's accumulators
-  constexpr int EPI = XCH > 4 * STRIP ? XCH : 4 * STRIP;
+  // MX output: each wave packs a strip's codes (32 rows x TN runs) after the strips
+  constexpr int CST = MxOut<P>::value ? 32 * TN * 32 : 0;
+  constexpr int EPI = XCH > 4 * (STRIP + CST) ? XCH : 4 * (STRIP + CST);
   constexpr int ARENA = (ZERO + 16) > EPI ? (ZERO + 16) : EPI;
   __shared__ __attribute__((aligned(16))) uint8_t arena[ARENA];
 
@@ -1008,6 +1119,20 @@ __global__ __launch_bounds__(256 * NG) __attribute__((amdgpu_waves_per_eu(2))) v
         strip[(8 * (e >> 2) + 4 * q + (e & 3)) * EP + j * 32 + r32] = acc[i][j][e];
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the strip is written (same wave)
     __builtin_amdgcn_wave_barrier();
+    if constexpr (MxOut<P>::value) {
+      const int ms = m0 + (wm * TM + i) * 32;
+      uint8_t* const cst = arena + 4 * STRIP + wave * CST;
+      constexpr bool LEAN = TM * TN >= 8;
+      switch (prob.yfmt) {
+        case 0: mx_store_strip<0, TN, LEAN>(prob, strip, EP, ms, c_wave, lane, cst); break;
+        case 1: mx_store_strip<1, TN, LEAN>(prob, strip, EP, ms, c_wave, lane, cst); break;
+        case 2: mx_store_strip<2, TN, LEAN>(prob, strip, EP, ms, c_wave, lane, cst); break;
+        case 3: mx_store_strip<3, TN, LEAN>(prob, strip, EP, ms, c_wave, lane, cst); break;
+        default: mx_store_strip<4, TN, LEAN>(prob, strip, EP, ms, c_wave, lane, cst); break;
+      }
+      __builtin_amdgcn_wave_barrier();
+      continue;
+    }
     constexpr int V = 32 * EW / 4;  // float4 pieces in the strip
     // the strip's first row and the run of rows that follow it at a fixed
     // stride: one address computation per strip instead of one per row

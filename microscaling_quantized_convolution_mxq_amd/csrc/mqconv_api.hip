@@ -185,6 +185,24 @@ int mqconv_forward(const mq_conv* cv, mq_mx xq, mq_mx wq, float* y, void* ws, si
   return hip_status(launch_forward(to_conv(cv), view(xq), view(wq), y, ws, ws_bytes, (hipStream_t)stream));
 }
 
+int mqconv_forward_mx(const mq_conv* cv, mq_mx xq, mq_mx wq, mq_mx yq, void* ws, size_t ws_bytes, void* stream) {
+  if (!cv) return MQ_ERR_NULL;
+  if (!conv_ok(cv)) return MQ_ERR_SHAPE;
+  const Conv c = to_conv(cv);
+  int s = check_mx(xq, MQ_ROLE_ACT, cv->h, cv->w, cv->n, cv->cin);
+  if (s != MQ_OK) return s;
+  s = check_mx(wq, MQ_ROLE_WEIGHT, cv->cout, cv->kh, cv->kw, cv->cin);
+  if (s != MQ_OK) return s;
+  s = check_mx(yq, MQ_ROLE_ACT, c.ho(), c.wo(), cv->n, cv->cout);
+  if (s != MQ_OK) return s;
+  // a block of 32 batch rows must not straddle two 32-row groups of output rows
+  if (yq.block_partner == 32 && cv->n % 32 != 0 && 32 % cv->n != 0) return MQ_ERR_UNSUPPORTED;
+  const size_t need = gemm_workspace_bytes(c, 0, xq.fmt, wq.fmt);
+  if (need > 0 && (!ws || ws_bytes < need)) return MQ_ERR_WORKSPACE;
+  MxOutView y{static_cast<uint8_t*>(yq.codes), yq.scales, yq.fmt, yq.block_partner};
+  return hip_status(launch_forward_mx(c, view(xq), view(wq), y, (hipStream_t)stream));
+}
+
 int mqconv_backward_data(const mq_conv* cv, mq_mx dyq, mq_mx wq, float* dx, void* ws, size_t ws_bytes,
                          void* stream) {
   if (!cv) return MQ_ERR_NULL;

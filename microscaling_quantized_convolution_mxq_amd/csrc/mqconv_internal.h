@@ -21,6 +21,13 @@ struct MxView {
   int fmt;
   int bp;
 };
+// an MX tensor a kernel writes
+struct MxOutView {
+  uint8_t* codes;
+  uint8_t* scales;
+  int fmt;
+  int bp;
+};
 
 inline int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 
@@ -74,6 +81,8 @@ inline size_t transposed_bytes(int fmt, long long A, long long P, long long B, l
 size_t gemm_workspace_bytes(const Conv& cv, int op, int fa, int fb);
 hipError_t launch_forward(const Conv& cv, MxView x, MxView w, float* y, void* ws, size_t ws_bytes,
                           hipStream_t st);
+// forward with Y MX-quantized in the epilogue (bp 1, or bp 32 with N % 32 == 0 or 32 % N == 0)
+hipError_t launch_forward_mx(const Conv& cv, MxView x, MxView w, MxOutView yq, hipStream_t st);
 hipError_t launch_backward_data(const Conv& cv, MxView dy, MxView w, float* dx, void* ws,
                                 size_t ws_bytes, hipStream_t st);
 hipError_t launch_backward_weight(const Conv& cv, MxView dy, MxView x, float* dw, void* ws,

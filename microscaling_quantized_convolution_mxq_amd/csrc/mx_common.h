@@ -70,6 +70,70 @@ __device__ __forceinline__ float inv_scale_from_byte(uint32_t S) {
   return __uint_as_float((254u - S) << 23);
 }
 
+// The 16 values of half a block run divided by the block's scale 2^(S-127)
+// and clamped to the format's largest finite value (saturation); a block
+// holding a NaN or an infinity (S = 0xFF) gets all-zero codes.
+template <int F>
+__device__ __forceinline__ void scale_clamp16(const float (&x)[16], uint32_t S, float (&v)[16]) {
+  constexpr float maxv = Fmt<F>::maxv;
+  const float inv = inv_scale_from_byte(S == 255u ? 127u : S);
+#pragma unroll
+  for (int i = 0; i < 16; i++) v[i] = S == 255u ? 0.0f : fminf(fmaxf(x[i] * inv, -maxv), maxv);
+}
+
+// Converts 16 scaled values (|v| <= max normal already) to codes and stores
+// them as half a packed run, with gfx950's conversion instructions: FP8 two
+// codes per instruction, FP4 two codes per byte, FP6 sixteen codes per
+// instruction (its output interleaves the two 16-value operands, so the even
+// values go in the first operand and the odd ones in the second). These
+// instructions round to nearest even, keep the sign of zero and produce the
+// element formats' subnormals.
+template <int F>
+__device__ __forceinline__ void convert_store_half_run(uint8_t* dst, const float (&v)[16]) {
+  constexpr int bits = Fmt<F>::bits;
+  if constexpr (bits == 8) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      uint32_t r;
+      if constexpr (F == 0) {
+        r = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * i], v[4 * i + 1], 0, false);
+        r = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * i + 2], v[4 * i + 3], r, true);
+      } else {
+        r = __builtin_amdgcn_cvt_pk_bf8_f32(v[4 * i], v[4 * i + 1], 0, false);
+        r = __builtin_amdgcn_cvt_pk_bf8_f32(v[4 * i + 2], v[4 * i + 3], r, true);
+      }
+      w[i] = r;
+    }
+    *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+  } else if constexpr (bits == 6) {
+    v16f even, odd;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      even[i] = v[2 * i]; odd[i] = v[2 * i + 1];
+      even[8 + i] = 0.0f; odd[8 + i] = 0.0f;
+    }
+    typedef int v6i __attribute__((ext_vector_type(6)));
+    v6i p;
+    if constexpr (F == 2) p = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(even, odd, 1.0f);
+    else p = __builtin_amdgcn_cvt_scalef32_2xpk16_bf6_f32(even, odd, 1.0f);
+    uint32_t* d = reinterpret_cast<uint32_t*>(dst);  // 4-byte aligned: offsets are multiples of 12
+    d[0] = p[0]; d[1] = p[1]; d[2] = p[2];
+  } else {
+    uint32_t w[2];
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+      uint32_t r = 0;
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * i], v[8 * i + 1], 1.0f, 0);
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * i + 2], v[8 * i + 3], 1.0f, 1);
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * i + 4], v[8 * i + 5], 1.0f, 2);
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * i + 6], v[8 * i + 7], 1.0f, 3);
+      w[i] = r;
+    }
+    *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+  }
+}
+
 // Block-scaled MFMA 32x32x64 with E8M0 scales (gfx950 v_mfma_scale_f32_32x32x64_f8f6f4).
 // Register images (lane l = row r + 32 q, rows of A and of B^T are "rows"):
 //   8-bit formats: bytes 0..15 = codes [16q, 16q+16) of K-block 0 of the pair,

@@ -26,7 +26,7 @@ def _declared():
 
 def test_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 17
+    assert len(names) == 18
     out = subprocess.run(["nm", "-D", "--defined-only", mq.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT\s+(mqconv_\w+)", out))
     assert set(names) <= exported
@@ -115,6 +115,16 @@ def test_validation_errors_without_gpu():
     assert _call(mq.mqconv_forward, s, x, w, 0) == -1
     assert _call(mq.mqconv_forward, s, w, x, FAKE) == -3
     assert _call(mq.mqconv_forward, s, x, _mx(mq.ROLE_WEIGHT, (s.cout, 1, 1, s.cin)), FAKE) == -2
+    # forward with MX output
+    yq = _mx(mq.ROLE_ACT, (s.ho, s.wo, s.n, s.cout))
+    assert _call(mq.mqconv_forward_mx, s, x, w, _mx(mq.ROLE_ACT, (s.ho, s.wo, s.n, s.cout), codes=0)) == -1
+    assert _call(mq.mqconv_forward_mx, s, x, w, _mx(mq.ROLE_GRAD, (s.ho, s.wo, s.n, s.cout))) == -3
+    assert _call(mq.mqconv_forward_mx, s, x, w, _mx(mq.ROLE_ACT, (s.ho, s.wo, s.n, s.cout + 1))) == -2
+    assert _call(mq.mqconv_forward_mx, s, w, x, yq) == -3
+    s24 = ConvShape(24, 64, 8, 8, 64, 3, 3, 1, 1)  # bp 32 with N = 24: blocks would straddle row groups
+    x24 = _mx(mq.ROLE_ACT, (8, 8, 24, 64))
+    w24 = _mx(mq.ROLE_WEIGHT, (64, 3, 3, 64))
+    assert _call(mq.mqconv_forward_mx, s24, x24, w24, _mx(mq.ROLE_ACT, (8, 8, 24, 64))) == -6
     # backward-data: needs bp 32 weights and a workspace
     assert _call(mq.mqconv_backward_data, s, dy, _mx(mq.ROLE_WEIGHT, (s.cout, s.kh, s.kw, s.cin), bp=1), FAKE) == -6
     assert _call(mq.mqconv_backward_data, s, dy, w, FAKE) == -5

@@ -188,3 +188,55 @@ def test_gemm_deterministic():
     b = run_gpu(shape, x, w, dy, wl.fx, wl.fw, wl.fdy, 32)
     for k in a:
         np.testing.assert_array_equal(a[k], b[k])
+
+
+# ---- forward with the MX-quantized output ---------------------------------------
+# mqconv_forward_mx must write exactly what quantizing mqconv_forward's own fp32
+# Y writes: the oracle quantizes the GPU's fp32 Y (a near-tie in Y could round
+# differently if the oracle's Y were used, so the GPU's Y is the common input).
+FWD_MX = [
+    ("n16_bp32", ConvShape(16, 64, 12, 12, 64), 0, 0, 32),
+    ("n16_bp1", ConvShape(16, 64, 12, 12, 64), 0, 0, 1),
+    ("n32_s2_cout72", ConvShape(32, 40, 9, 7, 72, 3, 3, 2, 1), 0, 1, 32),
+    ("n64_1x1", ConvShape(64, 96, 5, 6, 160, 1, 1, 1, 0), 1, 0, 32),
+    ("n4_bp32_fp4x", ConvShape(4, 48, 10, 9, 40), 4, 2, 32),
+    ("n5_bp1_fp6", ConvShape(5, 33, 7, 8, 45), 3, 4, 1),
+    ("n2_bp32", ConvShape(2, 32, 16, 16, 32), 2, 3, 32),
+    ("n8_cin16_half_blocks", ConvShape(8, 16, 9, 9, 24), 0, 1, 32),
+]
+
+
+def _fwd_mx(shape, x, w, fx, fw, fy, bp, label):
+    say(f"forward_mx {label} shape={shape.as_tuple()} fmts=({fx},{fw})->{fy} bp={bp}")
+    xq = gpu_quantize(x, mq.ROLE_ACT, fx, bp)
+    wq = gpu_quantize(w, mq.ROLE_WEIGHT, fw, 32)
+    y = torch.empty((shape.ho, shape.wo, shape.n, shape.cout), device="cuda")
+    mq.mqconv_forward(shape, xq, wq, y)
+    yq = mq.MxTensor.empty(mq.ROLE_ACT, fy, bp, (shape.ho, shape.wo, shape.n, shape.cout))
+    yq.codes.fill_(0xAB)  # poison: every byte must be written
+    yq.scales.fill_(0xAB)
+    mq.mqconv_forward_mx(shape, xq, wq, yq)
+    oc, os_ = oracle_packed_y(host(y), fy, bp)
+    np.testing.assert_array_equal(host(yq.scales), os_.reshape(-1), err_msg=f"scales {label}")
+    np.testing.assert_array_equal(host(yq.codes), oc.reshape(-1), err_msg=f"codes {label}")
+
+
+def oracle_packed_y(y, fy, bp):
+    codes, scales, _ = oracle.quantize(oracle.ROLE_ACT, fy, bp, y)
+    return oracle.pack(fy, codes), scales
+
+
+@pytest.mark.parametrize("fy", range(5))
+@pytest.mark.parametrize("case", FWD_MX, ids=[c[0] for c in FWD_MX])
+def test_forward_mx_equals_quantized_fp32_forward(case, fy):
+    label, shape, fx, fw, bp = case
+    rng = np.random.default_rng(900 + 10 * fy + FWD_MX.index(case))
+    x = (rng.standard_normal((shape.h, shape.w, shape.n, shape.cin)) * 2.0).astype(np.float32)
+    w = (rng.standard_normal((shape.cout, shape.kh, shape.kw, shape.cin)) * 0.1).astype(np.float32)
+    _fwd_mx(shape, x, w, fx, fw, fy, bp, f"{label} fy={fy}")
+
+
+def test_forward_mx_full_c2():
+    wl = WORKLOADS["c2"]
+    x, w, _ = draw_inputs(wl)
+    _fwd_mx(wl.shape, x, w, wl.fx, wl.fw, wl.fx, wl.bp, "c2")
