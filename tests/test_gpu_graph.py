@@ -37,14 +37,16 @@ def test_graph_replays_match_eager(name, shape):
     dw = torch.empty(w.shape, device="cuda")
     ws1 = workspace(mq.mqconv_workspace_bytes(s, 1, wl.fdy, wl.fw))
     ws2 = workspace(mq.mqconv_workspace_bytes(s, 2, wl.fdy, wl.fx))
-    outs = [xq.codes, xq.scales, wq.codes, wq.scales, gq.codes, gq.scales, cc, cs, y, dx, dw]
+    ybp = 32 if (s.n % 32 == 0 or 32 % s.n == 0) else 1
+    yq = mq.MxTensor.empty(mq.ROLE_ACT, wl.fx, ybp, (s.ho, s.wo, s.n, s.cout))
+    outs = [xq.codes, xq.scales, wq.codes, wq.scales, gq.codes, gq.scales, cc, cs, y, dx, dw, yq.codes, yq.scales]
 
     def path():
-        mq.mqconv_quantize(X, xq)
-        mq.mqconv_quantize(Wt, wq)
+        mq.mqconv_quantize_group([(X, xq), (Wt, wq)])
         mq.mqconv_quantize(DY, gq)
         mq.mqconv_cbf_im2col(s, xq, cc, cs)
         mq.mqconv_forward(s, xq, wq, y)
+        mq.mqconv_forward_mx(s, xq, wq, yq)
         mq.mqconv_backward_data(s, gq, wq, dx, ws1)
         mq.mqconv_backward_weight(s, gq, xq, dw, ws2)
 

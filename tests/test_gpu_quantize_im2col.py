@@ -131,6 +131,13 @@ def test_quantize_group_small_mixed():
     ]
     _check_group(items, "mixed")
     _check_group(items[:1], "single")
+    # the largest group: eight members of one format in one launch
+    eight = [(r(2, 2, 16, 64), mq.ROLE_ACT, 1, 32), (r(9, 3, 3, 40), mq.ROLE_WEIGHT, 1, 32),
+             (r(3, 1, 5, 70), mq.ROLE_GRAD, 1, 1), (r(1, 2, 64, 32), mq.ROLE_GRAD, 1, 32),
+             (r(33, 1, 1, 8), mq.ROLE_WEIGHT, 1, 1), (r(2, 5, 1, 96), mq.ROLE_ACT, 1, 32),
+             (r(4, 4, 8, 300), mq.ROLE_ACT, 1, 32), (r(70, 3, 3, 64), mq.ROLE_WEIGHT, 1, 32)]
+    assert len(eight) == mq.QUANTIZE_GROUP_MAX
+    _check_group(eight, "eight")
 
 
 @pytest.mark.parametrize("key", ["c2", "c4", "c5"])
