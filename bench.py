@@ -15,8 +15,9 @@ time). Every entry point is also timed on its own (a graph of repeated
 calls on rotating buffer sets, HIP events on the stream the kernels run
 on); `roofline` covers the entry point that takes the most time per step,
 with its algorithmic bytes or FLOPs per call. The forward whose epilogue
-writes Y as MX codes (`mqconv_forward_mx`) is timed the same way and listed
-with `in_step: false`. `cpu_baseline` times the CPU
+writes Y as MX codes (`mqconv_forward_mx`) and the backward-data whose
+epilogue writes dX as MX codes (`mqconv_backward_data_mx`) are timed the same
+way and listed with `in_step: false`. `cpu_baseline` times the CPU
 oracle on a bounded sample of the same workload.
 
 Prints one JSON line.
@@ -41,14 +42,17 @@ MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "fp6fp4": 10100.0}
 CSRC = os.path.join(ROOT, "microscaling_quantized_convolution_mxq_amd", "csrc")
 CALLS = ["quantize_xw", "quantize_dy", "cbf_im2col", "forward", "backward_data", "backward_weight"]
 # timed on their own too, but not part of the step: the forward whose epilogue
-# writes Y as MX codes and scales (the next layer's activation) instead of fp32
-EXTRA = ["forward_mx"]
+# writes Y as MX codes and scales (the next layer's activation) instead of fp32,
+# and the backward-data that writes dX the same way (the previous layer's gradient)
+EXTRA = ["forward_mx", "backward_data_mx"]
 # kernels each entry point launches (see the launchers in csrc/)
 CALL_KERNELS = {
     # X and W share one launch when their formats match, else one launch each
     "quantize_xw": ["mxq_quantize_group_kernel (same format; else 2 x mxq_quantize_kernel)"],
     "quantize_dy": ["mxq_quantize_kernel"], "cbf_im2col": ["cbf_im2col_kernel"],
     "forward": ["mx_gemm_kernel<FwdProb>"], "forward_mx": ["mx_gemm_kernel<FwdMxProb>"],
+    "backward_data_mx": ["mx_gemm_kernel<MxOutProb<DgradNatProb>> (8-bit W; else transpose_codes_kernel + "
+                         "mx_gemm_kernel<MxOutProb<DgradProb>>)"],
     # 8-bit codes are read in place; other formats are first re-laid by transpose_codes_kernel
     "backward_data": ["mx_gemm_kernel<DgradNatProb> (8-bit W; else transpose_codes_kernel + mx_gemm_kernel<DgradProb>)"],
     "backward_weight": ["mx_gemm_kernel<WgradNatProb> (8-bit dY and X; 8-bit dY only: transpose_codes_kernel (X) + "
@@ -110,6 +114,7 @@ def main():
         d["y"] = torch.empty((s.ho, s.wo, s.n, s.cout), device="cuda")
         d["yq"] = mq.MxTensor.empty(mq.ROLE_ACT, wl.fx, bp, (s.ho, s.wo, s.n, s.cout))
         d["dx"] = torch.empty(x.shape, device="cuda")
+        d["dxq"] = mq.MxTensor.empty(mq.ROLE_GRAD, wl.fdy, bp, x.shape)
         d["dw"] = torch.empty(w.shape, device="cuda")
         d["ws1"] = torch.empty(max(1, mq.mqconv_workspace_bytes(s, 1, wl.fdy, wl.fw)), dtype=torch.uint8, device="cuda")
         d["ws2"] = torch.empty(max(1, mq.mqconv_workspace_bytes(s, 2, wl.fdy, wl.fx)), dtype=torch.uint8, device="cuda")
@@ -134,6 +139,8 @@ def main():
             mq.mqconv_forward_mx(s, d["xq"], d["wq"], d["yq"])
         elif name == "backward_data":
             mq.mqconv_backward_data(s, d["gq"], d["wq"], d["dx"], d["ws1"])
+        elif name == "backward_data_mx":
+            mq.mqconv_backward_data_mx(s, d["gq"], d["wq"], d["dxq"], d["ws1"])
         elif name == "backward_weight":
             mq.mqconv_backward_weight(s, d["gq"], d["xq"], d["dw"], d["ws2"])
 
@@ -198,7 +205,8 @@ def main():
     # Infinity Cache as the step's sets do (no call reads cache-resident inputs).
     NEED = {"quantize_xw": ("x", "xq", "w", "wq"), "quantize_dy": ("dy", "gq"),
             "cbf_im2col": ("xq", "cc", "cs"), "forward": ("xq", "wq", "y"), "forward_mx": ("xq", "wq", "yq"),
-            "backward_data": ("gq", "wq", "dx", "ws1"), "backward_weight": ("gq", "xq", "dw", "ws2")}
+            "backward_data": ("gq", "wq", "dx", "ws1"), "backward_data_mx": ("gq", "wq", "dxq", "ws1"),
+            "backward_weight": ("gq", "xq", "dw", "ws2")}
 
     def nbytes(v):
         return (v.codes.numel() + v.scales.numel()) if isinstance(v, mq.MxTensor) else v.numel() * v.element_size()
@@ -237,21 +245,23 @@ def main():
     col_b = mq.mqconv_im2col_codes_bytes(s, wl.fx) + mq.mqconv_im2col_scales_bytes(s, bp)
     yq_dims = (s.ho, s.wo, s.n, s.cout)
     yq_b = mq.mqconv_codes_bytes(mq.ROLE_ACT, wl.fx, *yq_dims) + mq.mqconv_scales_bytes(mq.ROLE_ACT, bp, *yq_dims)
+    dxq_b = mq.mqconv_codes_bytes(mq.ROLE_GRAD, wl.fdy, *x.shape) + mq.mqconv_scales_bytes(mq.ROLE_GRAD, bp, *x.shape)
     # bytes each call must move at least once (inputs read, outputs written)
     alg_bytes = {
         "quantize_xw": 4 * nx + xq_b + 4 * nw + wq_b, "quantize_dy": 4 * ng + gq_b,
         "cbf_im2col": xq_b + col_b,
         "forward": xq_b + wq_b + 4 * ng, "backward_data": gq_b + wq_b + 4 * nx, "backward_weight": gq_b + xq_b + 4 * nw,
-        "forward_mx": xq_b + wq_b + yq_b,
+        "forward_mx": xq_b + wq_b + yq_b, "backward_data_mx": gq_b + wq_b + dxq_b,
     }
-    alg_flop = {"forward": flop, "backward_data": flop, "backward_weight": flop, "forward_mx": flop}
+    alg_flop = {"forward": flop, "backward_data": flop, "backward_weight": flop, "forward_mx": flop,
+                "backward_data_mx": flop}
     step_gemms = ("forward", "backward_data", "backward_weight")
 
     def mfma_peak(fa, fb):
         return MFMA_PEAK_TFLOPS["fp6fp4"] if (fa >= 2 and fb >= 2) else MFMA_PEAK_TFLOPS["fp8"]
 
     call_peak = {"forward": mfma_peak(wl.fx, wl.fw), "forward_mx": mfma_peak(wl.fx, wl.fw),
-                 "backward_data": mfma_peak(wl.fdy, wl.fw),
+                 "backward_data": mfma_peak(wl.fdy, wl.fw), "backward_data_mx": mfma_peak(wl.fdy, wl.fw),
                  "backward_weight": mfma_peak(wl.fdy, wl.fx)}
     kernels = {}
     for c in CALLS + EXTRA:

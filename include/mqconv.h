@@ -226,6 +226,18 @@ int mqconv_forward_mx(const mq_conv* cv, mq_mx xq, mq_mx wq, mq_mx yq, void* ws,
 int mqconv_backward_data(const mq_conv* cv, mq_mx dyq, mq_mx wq, float* dx, void* ws,
                          size_t ws_bytes, void* stream);
 
+/* mqconv_backward_data whose output is G_X MX-quantized (the gradient the
+ * previous layer consumes, quantized once: §III-A, §IV-B) instead of fp32:
+ * dxq receives exactly the codes and scales that mqconv_quantize of
+ * mqconv_backward_data's fp32 G_X would write; the fp32 G_X never reaches
+ * memory.
+ *   dxq: GRAD (H, W, N, Cin), any format; bp 1, or bp 32 when N is a
+ *        multiple of 32 or divides 32 (otherwise MQ_ERR_UNSUPPORTED). Its
+ *        code and scale buffers are fully overwritten.
+ *   dyq, wq, ws, ws_bytes, errors: as mqconv_backward_data. */
+int mqconv_backward_data_mx(const mq_conv* cv, mq_mx dyq, mq_mx wq, mq_mx dxq, void* ws,
+                            size_t ws_bytes, void* stream);
+
 /* Weight-gradient GEMM G_Wf = G_Yf . X'^T (§IV-B; Eq. 3).
  *   dyq: GRAD (Ho, Wo, N, Cout) and xq: ACT (H, W, N, Cin), both bp 32
  *        (the contraction runs along N, the partner dimension; bp 1 returns

@@ -68,6 +68,7 @@ def lib() -> ctypes.CDLL:
             "mqconv_forward": (I, [CV, mq_mx, mq_mx, P, P, S, P]),
             "mqconv_forward_mx": (I, [CV, mq_mx, mq_mx, mq_mx, P, S, P]),
             "mqconv_backward_data": (I, [CV, mq_mx, mq_mx, P, P, S, P]),
+            "mqconv_backward_data_mx": (I, [CV, mq_mx, mq_mx, mq_mx, P, S, P]),
             "mqconv_backward_weight": (I, [CV, mq_mx, mq_mx, P, P, S, P]),
             "mqconv_naive_workspace_bytes": (S, [CV, I, I, I]),
             "mqconv_naive_forward": (I, [CV, P, P, I, I, P, P, S, P]),
@@ -85,7 +86,7 @@ def lib() -> ctypes.CDLL:
 EXPORTED = ("mqconv_abi_version", "mqconv_status_string", "mqconv_codes_bytes", "mqconv_scales_bytes",
             "mqconv_im2col_codes_bytes", "mqconv_im2col_scales_bytes", "mqconv_quantize", "mqconv_quantize_group",
             "mqconv_cbf_im2col", "mqconv_workspace_bytes", "mqconv_forward", "mqconv_forward_mx", "mqconv_backward_data",
-            "mqconv_backward_weight", "mqconv_naive_workspace_bytes", "mqconv_naive_forward",
+            "mqconv_backward_data_mx", "mqconv_backward_weight", "mqconv_naive_workspace_bytes", "mqconv_naive_forward",
             "mqconv_naive_backward_data", "mqconv_naive_backward_weight")
 
 
@@ -214,6 +215,12 @@ def mqconv_backward_data(shape, dyq: MxTensor, wq: MxTensor, dx, ws=None, stream
     p, n = _ws(ws)
     _check(lib().mqconv_backward_data(ctypes.byref(_conv(shape)), dyq.c_struct(), wq.c_struct(), _ptr(dx), p,
                                       n, _stream(stream)), "mqconv_backward_data")
+
+
+def mqconv_backward_data_mx(shape, dyq: MxTensor, wq: MxTensor, dxq: MxTensor, ws=None, stream=None) -> None:
+    p, n = _ws(ws)
+    _check(lib().mqconv_backward_data_mx(ctypes.byref(_conv(shape)), dyq.c_struct(), wq.c_struct(), dxq.c_struct(),
+                                         p, n, _stream(stream)), "mqconv_backward_data_mx")
 
 
 def mqconv_backward_weight(shape, dyq: MxTensor, xq: MxTensor, dw, ws=None, stream=None) -> None:

@@ -3,8 +3,11 @@
 
 namespace mq {
 
-hipError_t launch_backward_data(const Conv& cv, MxView dy, MxView w, float* dx, void* ws, size_t,
-                                hipStream_t st) {
+// Fills the problem (in *nat when the weight codes are read in place, else
+// in *gen, *natural telling which) and launches the re-laying of 6/4-bit
+// weight codes into the workspace; the caller launches the GEMM.
+hipError_t prepare_backward_data(const Conv& cv, MxView dy, MxView w, float* dx, void* ws, hipStream_t st,
+                                 DgradNatProb* nat, DgradProb* gen, bool* natural_out) {
   uint8_t* wt = static_cast<uint8_t*>(ws);
   DgradProb p;
   // rows of A are (pixel, n); rows of B are Cin, 32 to a block
@@ -42,15 +45,29 @@ hipError_t launch_backward_data(const Conv& cv, MxView dy, MxView w, float* dx, 
     const int nkw = kw0 < cv.kw ? (cv.kw - kw0 + cv.sw - 1) / cv.sw : 0;
     p.dNkw[c] = make_fastdiv((unsigned)(nkw > 0 ? nkw : 1));
   }
-  const int maxHc = ceil_div(cv.h, cv.sh), maxWc = ceil_div(cv.w, cv.sw);
+  *natural_out = natural;
   if (natural) {
-    DgradNatProb q;
-    static_cast<DgradProb&>(q) = p;
-    q.T = (int)T; q.wrb = (int)row_bytes(w.fmt, cv.cin);
-    q.wtc = w.codes; q.wtc_bytes = (long long)cv.cout * T * q.wrb;
-    return launch_tiled(dy.fmt, w.fmt, q, maxHc * maxWc * cv.n, cv.cin, cv.sh * cv.sw, st);
+    static_cast<DgradProb&>(*nat) = p;
+    nat->T = (int)T; nat->wrb = (int)row_bytes(w.fmt, cv.cin);
+    nat->wtc = w.codes; nat->wtc_bytes = (long long)cv.cout * T * nat->wrb;
+  } else {
+    *gen = p;
   }
-  return launch_tiled(dy.fmt, w.fmt, p, maxHc * maxWc * cv.n, cv.cin, cv.sh * cv.sw, st);
+  return hipSuccess;
+}
+
+// rows of the problem: every parity class spans at most maxHc x maxWc pixels
+int dgrad_rows(const Conv& cv) { return ceil_div(cv.h, cv.sh) * ceil_div(cv.w, cv.sw) * cv.n; }
+
+hipError_t launch_backward_data(const Conv& cv, MxView dy, MxView w, float* dx, void* ws, size_t,
+                                hipStream_t st) {
+  DgradNatProb q;
+  DgradProb p;
+  bool natural = false;
+  const hipError_t e = prepare_backward_data(cv, dy, w, dx, ws, st, &q, &p, &natural);
+  if (e != hipSuccess) return e;
+  if (natural) return launch_tiled(dy.fmt, w.fmt, q, dgrad_rows(cv), cv.cin, cv.sh * cv.sw, st);
+  return launch_tiled(dy.fmt, w.fmt, p, dgrad_rows(cv), cv.cin, cv.sh * cv.sw, st);
 }
 
 

@@ -123,19 +123,23 @@ struct FwdProb {
   __device__ float* out_row(const Ctx&, int, int m) const { return m < M ? y + (long long)m * Cout : nullptr; }
   // rows m .. m + run - 1 lie at out_row(m) + j * ncols()
   __device__ int row_run(const Ctx&, int) const { return 1 << 30; }
+  // row of the [pixel][N] output that row m of the problem is
+  __device__ long long out_index(const Ctx&, int m) const { return m; }
 };
 
-// Forward whose epilogue MX-quantizes Y (an activation [Ho][Wo][N][Cout],
-// quantized as a separate quantization of the fp32 Y would do it) instead of
-// writing fp32: blocks of 32 channels x (1 row: ymode 0; the 32 rows of a
-// 32-row group within one pixel: ymode 1, N % 32 == 0; each pixel's N rows:
-// ymode 2, N dividing 32), so every block lies inside one 32-row strip of a
-// tile and one 32-column block of it.
-struct FwdMxProb : FwdProb {
+// A problem whose epilogue MX-quantizes its output (an activation or a
+// gradient [pixel][N][C], quantized as a separate quantization of the fp32
+// output would do it) instead of writing fp32: blocks of 32 channels x (1
+// row: ymode 0; the 32 rows of a 32-row group within one pixel: ymode 1,
+// N % 32 == 0; each pixel's N rows: ymode 2, N dividing 32), so every block
+// lies inside one 32-row strip of a tile and one 32-column block of it.
+template <class Base>
+struct MxOutProb : Base {
   uint8_t *yc, *ys;
   int yfmt, ymode, yrb, ynPB, ynCB;
   static constexpr bool kMxOut = true;
 };
+using FwdMxProb = MxOutProb<FwdProb>;
 template <class P, class = void>
 struct MxOut : std::false_type {};
 template <class P>
@@ -228,11 +232,15 @@ struct DgradProb {
   }
   __device__ float* out_row(const Ctx& c, int, int m) const {
     if (m >= c.M) return nullptr;
-    if (sh == 1 && sw == 1) return dx + (long long)m * Cin;  // one class: rows in dX order
+    return dx + out_index(c, m) * Cin;
+  }
+  // row of dX [H][W][N] that row m of class c is
+  __device__ long long out_index(const Ctx& c, int m) const {
+    if (sh == 1 && sw == 1) return m;  // one class: rows in dX order
     const int pix = (int)fdiv((unsigned)m, dN), n = m - pix * N;
     const int hq = (int)fdiv((unsigned)pix, c.dwc), wq = pix - hq * c.Wc;
     const int h = hq * sh + c.ph_c, w = wq * sw + c.pw_c;
-    return dx + (((long long)h * W + w) * N + n) * Cin;
+    return ((long long)h * W + w) * N + n;
   }
 };
 
@@ -645,12 +653,13 @@ __device__ __forceinline__ uint32_t group_max(uint32_t a, int g) {
 // stretch), not as scattered half runs.
 // LEAN (tiles whose accumulators already fill most registers): one block at
 // a time and one copy piece at a time, so the epilogue needs few registers.
-template <int F, int TN, bool LEAN>
-__device__ __forceinline__ void mx_store_strip(const FwdMxProb& p, const float* strip, int EP, int ms, int c0,
-                                               int lane, uint8_t* cst) {
+template <int F, int TN, bool LEAN, class P>
+__device__ __forceinline__ void mx_store_strip(const P& p, const typename P::Ctx& cx, const float* strip, int EP,
+                                               int ms, int c0, int lane, uint8_t* cst) {
   constexpr int RB = run_bytes_of(F), SEG = TN * RB;
   const int r = lane >> 1, half = lane & 1;
   const int m = ms + r;
+  const int M = p.rows_a(cx);
   const int cb0 = c0 >> 5;
   const int nb = min(TN, p.ynCB - cb0);  // blocks of this wave inside the padded row (uniform)
   const int glanes = p.ymode == 0 ? 2 : (p.ymode == 1 ? 64 : 2 * p.N);  // lanes of one block
@@ -673,9 +682,10 @@ __device__ __forceinline__ void mx_store_strip(const FwdMxProb& p, const float* 
     scale_clamp16<F>(x, S, v);
     convert_store_half_run<F>(cst + r * SEG + j * RB + half * (RB / 2), v);
     const bool first = p.ymode == 0 ? half == 0 : (p.ymode == 1 ? lane == 0 : (lane & (2 * p.N - 1)) == 0);
-    if (first && m < p.M) {
-      const int pix = (int)fdiv((unsigned)m, p.dN), n = m - pix * p.N;
-      const long long blk = p.ymode == 0 ? (long long)m : (long long)pix * p.ynPB + (n >> 5);
+    if (first && m < M) {
+      const long long gm = p.out_index(cx, m);
+      const long long pix = gm / p.N, n = gm - pix * p.N;
+      const long long blk = p.ymode == 0 ? gm : pix * p.ynPB + (n >> 5);
       p.ys[blk * p.ynCB + cb0 + j] = (uint8_t)S;
     }
   }
@@ -696,15 +706,15 @@ __device__ __forceinline__ void mx_store_strip(const FwdMxProb& p, const float* 
 #pragma unroll
     for (int it = 0; it < IT; it++) {
       const int d = it * 64 + lane, row = d / PR, off = d - row * PR;
-      if (d < 32 * PR && ms + row < p.M)
-        *reinterpret_cast<vw_t*>(p.yc + (long long)(ms + row) * p.yrb + cb0 * RB + off * VW) = val[it];
+      if (d < 32 * PR && ms + row < M)
+        *reinterpret_cast<vw_t*>(p.yc + p.out_index(cx, ms + row) * p.yrb + cb0 * RB + off * VW) = val[it];
     }
   } else {
     const int pr = nb * RB / VW;
     for (int d = lane; d < 32 * pr; d += 64) {
       const int row = d / pr, off = d - row * pr;
-      if (ms + row < p.M)
-        *reinterpret_cast<vw_t*>(p.yc + (long long)(ms + row) * p.yrb + cb0 * RB + off * VW) =
+      if (ms + row < M)
+        *reinterpret_cast<vw_t*>(p.yc + p.out_index(cx, ms + row) * p.yrb + cb0 * RB + off * VW) =
             *reinterpret_cast<const vw_t*>(cst + row * SEG + off * VW);
     }
   }
@@ -1124,11 +1134,11 @@ __global__ __launch_bounds__(256 * NG) __attribute__((amdgpu_waves_per_eu(2))) v
       uint8_t* const cst = arena + 4 * STRIP + wave * CST;
       constexpr bool LEAN = TM * TN >= 8;
       switch (prob.yfmt) {
-        case 0: mx_store_strip<0, TN, LEAN>(prob, strip, EP, ms, c_wave, lane, cst); break;
-        case 1: mx_store_strip<1, TN, LEAN>(prob, strip, EP, ms, c_wave, lane, cst); break;
-        case 2: mx_store_strip<2, TN, LEAN>(prob, strip, EP, ms, c_wave, lane, cst); break;
-        case 3: mx_store_strip<3, TN, LEAN>(prob, strip, EP, ms, c_wave, lane, cst); break;
-        default: mx_store_strip<4, TN, LEAN>(prob, strip, EP, ms, c_wave, lane, cst); break;
+        case 0: mx_store_strip<0, TN, LEAN>(prob, cx, strip, EP, ms, c_wave, lane, cst); break;
+        case 1: mx_store_strip<1, TN, LEAN>(prob, cx, strip, EP, ms, c_wave, lane, cst); break;
+        case 2: mx_store_strip<2, TN, LEAN>(prob, cx, strip, EP, ms, c_wave, lane, cst); break;
+        case 3: mx_store_strip<3, TN, LEAN>(prob, cx, strip, EP, ms, c_wave, lane, cst); break;
+        default: mx_store_strip<4, TN, LEAN>(prob, cx, strip, EP, ms, c_wave, lane, cst); break;
       }
       __builtin_amdgcn_wave_barrier();
       continue;

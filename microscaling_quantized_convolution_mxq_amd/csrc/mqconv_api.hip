@@ -221,6 +221,27 @@ int mqconv_backward_data(const mq_conv* cv, mq_mx dyq, mq_mx wq, float* dx, void
   return hip_status(launch_backward_data(c, view(dyq), view(wq), dx, ws, ws_bytes, (hipStream_t)stream));
 }
 
+int mqconv_backward_data_mx(const mq_conv* cv, mq_mx dyq, mq_mx wq, mq_mx dxq, void* ws, size_t ws_bytes,
+                            void* stream) {
+  if (!cv) return MQ_ERR_NULL;
+  if (!conv_ok(cv)) return MQ_ERR_SHAPE;
+  const Conv c = to_conv(cv);
+  int s = check_mx(dyq, MQ_ROLE_GRAD, c.ho(), c.wo(), cv->n, cv->cout);
+  if (s != MQ_OK) return s;
+  s = check_mx(wq, MQ_ROLE_WEIGHT, cv->cout, cv->kh, cv->kw, cv->cin);
+  if (s != MQ_OK) return s;
+  s = check_mx(dxq, MQ_ROLE_GRAD, cv->h, cv->w, cv->n, cv->cin);
+  if (s != MQ_OK) return s;
+  if (wq.block_partner != 32) return MQ_ERR_UNSUPPORTED;
+  // a block of 32 batch rows must not straddle two 32-row groups of output rows
+  if (dxq.block_partner == 32 && cv->n % 32 != 0 && 32 % cv->n != 0) return MQ_ERR_UNSUPPORTED;
+  const size_t need = gemm_workspace_bytes(c, 1, dyq.fmt, wq.fmt);
+  if (need > 0 && (!ws || ws_bytes < need)) return MQ_ERR_WORKSPACE;
+  if (ws && !aligned16(ws)) return MQ_ERR_ALIGN;
+  MxOutView dx{static_cast<uint8_t*>(dxq.codes), dxq.scales, dxq.fmt, dxq.block_partner};
+  return hip_status(launch_backward_data_mx(c, view(dyq), view(wq), dx, ws, ws_bytes, (hipStream_t)stream));
+}
+
 int mqconv_backward_weight(const mq_conv* cv, mq_mx dyq, mq_mx xq, float* dw, void* ws, size_t ws_bytes,
                            void* stream) {
   if (!cv) return MQ_ERR_NULL;

@@ -85,6 +85,9 @@ hipError_t launch_forward(const Conv& cv, MxView x, MxView w, float* y, void* ws
 hipError_t launch_forward_mx(const Conv& cv, MxView x, MxView w, MxOutView yq, hipStream_t st);
 hipError_t launch_backward_data(const Conv& cv, MxView dy, MxView w, float* dx, void* ws,
                                 size_t ws_bytes, hipStream_t st);
+// backward-data with dX MX-quantized in the epilogue (same block rules as the forward's Y)
+hipError_t launch_backward_data_mx(const Conv& cv, MxView dy, MxView w, MxOutView dxq, void* ws,
+                                   size_t ws_bytes, hipStream_t st);
 hipError_t launch_backward_weight(const Conv& cv, MxView dy, MxView x, float* dw, void* ws,
                                   size_t ws_bytes, hipStream_t st);
 

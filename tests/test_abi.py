@@ -26,7 +26,7 @@ def _declared():
 
 def test_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 18
+    assert len(names) == 19
     out = subprocess.run(["nm", "-D", "--defined-only", mq.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT\s+(mqconv_\w+)", out))
     assert set(names) <= exported
@@ -129,6 +129,16 @@ def test_validation_errors_without_gpu():
     assert _call(mq.mqconv_backward_data, s, dy, _mx(mq.ROLE_WEIGHT, (s.cout, s.kh, s.kw, s.cin), bp=1), FAKE) == -6
     assert _call(mq.mqconv_backward_data, s, dy, w, FAKE) == -5
     assert _call(mq.mqconv_backward_data, s, x, w, FAKE) == -3
+    # backward-data with MX output
+    dxq = _mx(mq.ROLE_GRAD, (s.h, s.w, s.n, s.cin))
+    assert _call(mq.mqconv_backward_data_mx, s, dy, w, _mx(mq.ROLE_GRAD, (s.h, s.w, s.n, s.cin), codes=0)) == -1
+    assert _call(mq.mqconv_backward_data_mx, s, dy, w, _mx(mq.ROLE_ACT, (s.h, s.w, s.n, s.cin))) == -3
+    assert _call(mq.mqconv_backward_data_mx, s, dy, w, _mx(mq.ROLE_GRAD, (s.h, s.w, s.n, s.cin + 1))) == -2
+    assert _call(mq.mqconv_backward_data_mx, s, dy, _mx(mq.ROLE_WEIGHT, (s.cout, s.kh, s.kw, s.cin), bp=1),
+                 dxq) == -6
+    assert _call(mq.mqconv_backward_data_mx, s, dy, w, dxq) == -5
+    dy24 = _mx(mq.ROLE_GRAD, (8, 8, 24, 64), fmt=1)
+    assert _call(mq.mqconv_backward_data_mx, s24, dy24, w24, _mx(mq.ROLE_GRAD, (8, 8, 24, 64))) == -6
     # backward-weight: needs bp 32 on both operands
     assert _call(mq.mqconv_backward_weight, s, dy, _mx(mq.ROLE_ACT, (s.h, s.w, s.n, s.cin), bp=1), FAKE) == -6
     assert _call(mq.mqconv_backward_weight, s, _mx(mq.ROLE_GRAD, (s.ho, s.wo, s.n, s.cout), bp=1), x, FAKE) == -6

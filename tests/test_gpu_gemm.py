@@ -240,3 +240,56 @@ def test_forward_mx_full_c2():
     wl = WORKLOADS["c2"]
     x, w, _ = draw_inputs(wl)
     _fwd_mx(wl.shape, x, w, wl.fx, wl.fw, wl.fx, wl.bp, "c2")
+
+
+# ---- backward-data with the MX-quantized output ---------------------------------
+# mqconv_backward_data_mx must write exactly what quantizing (role GRAD)
+# mqconv_backward_data's own fp32 dX writes; the GPU's dX is the common input
+# for the same reason as above. Cases span both weight paths (8-bit codes read
+# in place; 6/4-bit codes re-laid first), stride-2 parity classes, a 1x1
+# stride-2 conv whose odd pixels receive no tap (all-zero blocks), Cin not a
+# multiple of 32 and the three block modes (bp 1; bp 32 with N % 32 == 0;
+# bp 32 with N dividing 32).
+DGRAD_MX = [
+    ("n16_bp32", ConvShape(16, 64, 12, 12, 64), 1, 0, 32),
+    ("n16_bp1", ConvShape(16, 64, 12, 12, 64), 1, 0, 1),
+    ("n32_s2_cin72", ConvShape(32, 72, 9, 7, 40, 3, 3, 2, 1), 1, 1, 32),
+    ("n8_1x1_s2_zero_pixels", ConvShape(8, 40, 9, 8, 48, 1, 1, 2, 0), 0, 0, 32),
+    ("n4_w_fp4", ConvShape(4, 48, 10, 9, 40), 1, 4, 32),
+    ("n5_bp1_w_fp6", ConvShape(5, 33, 7, 8, 45), 0, 3, 1),
+    ("n64_1x1", ConvShape(64, 160, 5, 6, 96, 1, 1, 1, 0), 1, 0, 32),
+    ("n8_cout16_half_blocks", ConvShape(8, 24, 9, 9, 16), 0, 1, 32),
+]
+
+
+def _dgrad_mx(shape, w, dy, fdy, fw, fx, bp, label):
+    say(f"backward_data_mx {label} shape={shape.as_tuple()} fmts=({fdy},{fw})->{fx} bp={bp}")
+    gq = gpu_quantize(dy, mq.ROLE_GRAD, fdy, bp)
+    wq = gpu_quantize(w, mq.ROLE_WEIGHT, fw, 32)
+    ws = workspace(mq.mqconv_workspace_bytes(shape, 1, fdy, fw))
+    dx = torch.empty((shape.h, shape.w, shape.n, shape.cin), device="cuda")
+    mq.mqconv_backward_data(shape, gq, wq, dx, ws)
+    dxq = mq.MxTensor.empty(mq.ROLE_GRAD, fx, bp, (shape.h, shape.w, shape.n, shape.cin))
+    dxq.codes.fill_(0xAB)  # poison: every byte must be written
+    dxq.scales.fill_(0xAB)
+    mq.mqconv_backward_data_mx(shape, gq, wq, dxq, ws)
+    codes, scales, _ = oracle.quantize(oracle.ROLE_GRAD, fx, bp, host(dx))
+    np.testing.assert_array_equal(host(dxq.scales), scales.reshape(-1), err_msg=f"scales {label}")
+    np.testing.assert_array_equal(host(dxq.codes), oracle.pack(fx, codes).reshape(-1), err_msg=f"codes {label}")
+
+
+@pytest.mark.parametrize("fx", range(5))
+@pytest.mark.parametrize("case", DGRAD_MX, ids=[c[0] for c in DGRAD_MX])
+def test_backward_data_mx_equals_quantized_fp32_dgrad(case, fx):
+    label, shape, fdy, fw, bp = case
+    rng = np.random.default_rng(1900 + 10 * fx + DGRAD_MX.index(case))
+    w = (rng.standard_normal((shape.cout, shape.kh, shape.kw, shape.cin)) * 0.1).astype(np.float32)
+    dy = (rng.standard_normal((shape.ho, shape.wo, shape.n, shape.cout)) * 1e-3).astype(np.float32)
+    _dgrad_mx(shape, w, dy, fdy, fw, fx, bp, f"{label} fx={fx}")
+
+
+@pytest.mark.parametrize("name", ["c2", "c5"])
+def test_backward_data_mx_full(name):
+    wl = WORKLOADS[name]
+    _, w, dy = draw_inputs(wl)
+    _dgrad_mx(wl.shape, w, dy, wl.fdy, wl.fw, wl.fdy, wl.bp, name)
