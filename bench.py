@@ -50,7 +50,7 @@ CALL_KERNELS = {
     # X and W share one launch when their formats match, else one launch each
     "quantize_xw": ["mxq_quantize_group_kernel (same format; else 2 x mxq_quantize_kernel)"],
     "quantize_dy": ["mxq_quantize_kernel"], "cbf_im2col": ["cbf_im2col_kernel"],
-    "forward": ["mx_gemm_kernel<FwdProb>"], "forward_mx": ["mx_gemm_kernel<FwdMxProb>"],
+    "forward": ["mx_gemm_kernel<FwdProb>"], "forward_mx": ["mx_gemm_kernel<MxOutProb<FwdProb>>"],
     "backward_data_mx": ["mx_gemm_kernel<MxOutProb<DgradNatProb>> (8-bit W; else transpose_codes_kernel + "
                          "mx_gemm_kernel<MxOutProb<DgradProb>>)"],
     # 8-bit codes are read in place; other formats are first re-laid by transpose_codes_kernel

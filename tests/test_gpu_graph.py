@@ -39,7 +39,9 @@ def test_graph_replays_match_eager(name, shape):
     ws2 = workspace(mq.mqconv_workspace_bytes(s, 2, wl.fdy, wl.fx))
     ybp = 32 if (s.n % 32 == 0 or 32 % s.n == 0) else 1
     yq = mq.MxTensor.empty(mq.ROLE_ACT, wl.fx, ybp, (s.ho, s.wo, s.n, s.cout))
-    outs = [xq.codes, xq.scales, wq.codes, wq.scales, gq.codes, gq.scales, cc, cs, y, dx, dw, yq.codes, yq.scales]
+    dxq = mq.MxTensor.empty(mq.ROLE_GRAD, wl.fdy, ybp, x.shape)
+    outs = [xq.codes, xq.scales, wq.codes, wq.scales, gq.codes, gq.scales, cc, cs, y, dx, dw, yq.codes, yq.scales,
+            dxq.codes, dxq.scales]
 
     def path():
         mq.mqconv_quantize_group([(X, xq), (Wt, wq)])
@@ -48,6 +50,7 @@ def test_graph_replays_match_eager(name, shape):
         mq.mqconv_forward(s, xq, wq, y)
         mq.mqconv_forward_mx(s, xq, wq, yq)
         mq.mqconv_backward_data(s, gq, wq, dx, ws1)
+        mq.mqconv_backward_data_mx(s, gq, wq, dxq, ws1)
         mq.mqconv_backward_weight(s, gq, xq, dw, ws2)
 
     stream = torch.cuda.Stream()
