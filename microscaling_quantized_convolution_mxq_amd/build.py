@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmqconv.so")
-SOURCES = ["quantize.hip", "layout.hip", "gemm_fwd.hip", "gemm_fwd_mx.hip", "gemm_dgrad.hip", "gemm_dgrad_mx.hip", "gemm_wgrad.hip", "gemm_plain.hip",
+SOURCES = ["quantize.hip", "layout.hip", "gemm_fwd.hip", "gemm_fwd_mx.hip", "gemm_dgrad.hip", "gemm_dgrad_mx.hip", "gemm_dgrad_mx_relaid.hip", "gemm_wgrad.hip", "gemm_plain.hip",
            "naive.hip", "mqconv_api.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -18,10 +18,6 @@ hipError_t prepare_backward_data(const Conv& cv, MxView dy, MxView w, float* dx,
   // staging); other formats are first re-laid with runs along Cout
   const bool natural = w.fmt <= 1;
   const bool half = !natural && half_k_blocks(p.ga, p.gb, p.khalf, dy.fmt, w.fmt);
-  if (!natural) {
-    hipError_t e = launch_transpose_codes(w.codes, wt, w.fmt, half, 1, cv.cout, cv.kh * cv.kw, cv.cin, st);
-    if (e != hipSuccess) return e;
-  }
   p.dyc = dy.codes; p.dys = dy.scales; p.wtc = wt; p.ws = w.scales; p.dx = dx;
   p.N = cv.n; p.H = cv.h; p.W = cv.w; p.Cin = cv.cin; p.Cout = cv.cout; p.KH = cv.kh; p.KW = cv.kw;
   p.sh = cv.sh; p.sw = cv.sw; p.ph = cv.ph; p.pw = cv.pw; p.Ho = cv.ho(); p.Wo = cv.wo();
@@ -44,6 +40,11 @@ hipError_t prepare_backward_data(const Conv& cv, MxView dy, MxView w, float* dx,
     const int kw0 = c < cv.sw ? (c + cv.pw) % cv.sw : 0;
     const int nkw = kw0 < cv.kw ? (cv.kw - kw0 + cv.sw - 1) / cv.sw : 0;
     p.dNkw[c] = make_fastdiv((unsigned)(nkw > 0 ? nkw : 1));
+  }
+  // every check has passed: only now is anything enqueued
+  if (!natural) {
+    const hipError_t e = launch_transpose_codes(w.codes, wt, w.fmt, half, 1, cv.cout, cv.kh * cv.kw, cv.cin, st);
+    if (e != hipSuccess) return e;
   }
   *natural_out = natural;
   if (natural) {

@@ -133,15 +133,6 @@ hipError_t launch_backward_weight(const Conv& cv, MxView dy, MxView x, float* dw
   const bool natural = dy.fmt <= 1 && x.fmt <= 1 && cv.cin % 16 == 0 && kext_ok;
   const bool mixed = !natural && dy.fmt <= 1 && kext_ok;
   const bool half = !natural && half_k_blocks(p.ga, p.gb, p.khalf, dy.fmt, x.fmt);
-  hipError_t e = hipSuccess;
-  if (!natural && !mixed) {
-    e = launch_transpose_codes(dy.codes, dyt, dy.fmt, half, (int)npix_o, cv.n, 1, cv.cout, st);
-    if (e != hipSuccess) return e;
-  }
-  if (!natural) {
-    e = launch_transpose_codes(x.codes, xt, x.fmt, half, cv.h * cv.w, cv.n, 1, cv.cin, st);
-    if (e != hipSuccess) return e;
-  }
   // as the kernel choice below: half K-blocks take four K-blocks per step and
   // two wave groups per workgroup, so half as many slices cover the K range
   p.kps = half_k_blocks(p.ga, p.gb, p.khalf, dy.fmt, x.fmt) ? 4 : 2;
@@ -160,6 +151,17 @@ hipError_t launch_backward_weight(const Conv& cv, MxView dy, MxView x, float* dw
   const long long lead = (long long)cv.ph * cv.w + cv.pw;
   p.xtcb = (int)(lead * cv.cin * p.nNB * p.xRB); p.xsb = (int)(lead * p.nNB * p.ncbi);
   if (!offsets_fit(p.xtc_bytes, p.xtcb) || !offsets_fit(p.xs_bytes, p.xsb)) return hipErrorInvalidValue;
+  // every check of the re-laid path has passed: only now is anything enqueued
+  // (the in-place path re-lays nothing; its own check follows)
+  hipError_t e = hipSuccess;
+  if (!natural && !mixed) {
+    e = launch_transpose_codes(dy.codes, dyt, dy.fmt, half, (int)npix_o, cv.n, 1, cv.cout, st);
+    if (e != hipSuccess) return e;
+  }
+  if (!natural) {
+    e = launch_transpose_codes(x.codes, xt, x.fmt, half, cv.h * cv.w, cv.n, 1, cv.cin, st);
+    if (e != hipSuccess) return e;
+  }
   p.dCin = make_fastdiv(cv.cin); p.dKW = make_fastdiv(cv.kw);
   p.dnsub = make_fastdiv(ks.nsub); p.dWo = make_fastdiv(p.Wo);
   const long long nj = (long long)p.T * cv.cin;
