@@ -190,3 +190,132 @@ def test_paths_on_random_inputs_are_close_to_exact_conv():
     for got in (out["y"], naive):
         err = np.abs(got - exact).max() / np.abs(exact).max()
         assert 1e-4 < err < 0.05
+
+
+# ---- channel-batch-first im2col pinned to torch's unfold (§IV-A) ------------------
+CBF_CASES = [
+    ConvShape(2, 3, 6, 5, 4, 3, 3, 1, 1),
+    ConvShape(3, 4, 7, 6, 2, 3, 3, 2, 1),
+    ConvShape(2, 5, 6, 7, 2, 3, 1, 1, 0),
+    ConvShape(1, 2, 5, 6, 2, 5, 3, 2, 2),
+    ConvShape(4, 3, 4, 4, 2, 1, 1, 2, 0),
+    ConvShape(33, 40, 5, 4, 2, 3, 3, 2, 1),
+]
+
+
+def _unfold_cbf(shape, t):
+    """torch's unfold of a CBF tensor [H][W][N][C], returned in the CBF im2col
+    order [Ho][Wo][N][Kh][Kw][C] (unfold's rows are (c, kh, kw), its columns
+    the output pixels in row-major order)."""
+    u = F.unfold(_nchw(t), (shape.kh, shape.kw), padding=shape.pad, stride=shape.stride).numpy()
+    u = u.reshape(shape.n, t.shape[3], shape.kh, shape.kw, shape.ho, shape.wo)
+    return np.ascontiguousarray(np.transpose(u, (4, 5, 0, 2, 3, 1)))
+
+
+@pytest.mark.parametrize("shape", CBF_CASES)
+def test_cbf_im2col_f32_matches_torch_unfold(shape):
+    """X'[ho,wo,n,kh,kw,c] = X[ho*s+kh-p, wo*s+kw-p, n, c], zero outside the
+    image: the same patches as §II-C1's im2col, in the CBF order."""
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((shape.h, shape.w, shape.n, shape.cin)).astype(np.float32)
+    got = oracle.cbf_im2col_f32(shape, x)
+    np.testing.assert_array_equal(got, _unfold_cbf(shape, x).astype(np.float32))
+    # the explicit CBF X' times the (kh, kw, c)-flattened kernel is Eq. (1)
+    w = rng.standard_normal((shape.cout, shape.kh, shape.kw, shape.cin))
+    y = got.reshape(shape.ho * shape.wo * shape.n, -1).astype(np.float64) @ w.reshape(shape.cout, -1).T
+    np.testing.assert_allclose(y.reshape(shape.ho, shape.wo, shape.n, shape.cout),
+                               oracle.conv_fwd(shape, x.astype(np.float64), w), rtol=1e-10, atol=1e-10)
+
+
+@pytest.mark.parametrize("bp", [1, 32])
+@pytest.mark.parametrize("shape", CBF_CASES)
+def test_cbf_im2col_codes_and_scales_match_torch_unfold(shape, bp):
+    """The quantized CBF im2col moves codes and block scales unchanged: codes
+    are unfolded like values, and every (ho, wo, kh, kw) slice takes the scale
+    row of its source pixel, with scale byte 0 at padding. Both are checked
+    against torch's unfold of the code and scale arrays (integers up to 255
+    are exact in float64)."""
+    rng = np.random.default_rng(22)
+    x = (rng.standard_normal((shape.h, shape.w, shape.n, shape.cin))
+         * np.exp(rng.uniform(-4, 4, (shape.h, shape.w, 1, 1)))).astype(np.float32)
+    xc, xs, _ = oracle.quantize(oracle.ROLE_ACT, 0, bp, x)
+    oc, os_ = oracle.cbf_im2col_codes(shape, bp, xc, xs)
+    np.testing.assert_array_equal(oc, _unfold_cbf(shape, xc.astype(np.float64)).astype(np.uint8))
+    nb, ncb = xs.shape[2], xs.shape[3]
+    # scales [H][W][nb][ncb] unfolded as a one-sample image of nb*ncb channels
+    su = F.unfold(torch.from_numpy(np.transpose(xs.reshape(shape.h, shape.w, nb * ncb), (2, 0, 1))[None].astype(np.float64)),
+                  (shape.kh, shape.kw), padding=shape.pad, stride=shape.stride).numpy()
+    su = su.reshape(nb, ncb, shape.kh, shape.kw, shape.ho, shape.wo)
+    np.testing.assert_array_equal(os_, np.transpose(su, (4, 5, 2, 3, 0, 1)).astype(np.uint8))
+    assert (os_ == 0).any() == (shape.pad > 0)
+
+
+# ---- the naive path's block directions (§III-C, Table I "Dacapo") ----------------
+# Hand-worked cases on a 1x1 convolution (H = 1, W = 32, N = 1, Cin = Cout = 32, so
+# classic im2col is the identity map X'[m][k] = x[0][m][0][k] and M = K = Cout = 32:
+# one block of 32 along each GEMM direction). One operand holds the value 256 at
+# [0][0] and a = 1.5 * 2^-12 elsewhere; the other is all ones. In E4M3, the block
+# holding 256 gets the shared exponent 8 - 8 = 0, and a / 2^0 lies below half of the
+# smallest subnormal 2^-9, so every a in that block becomes 0; a block without the
+# 256 has exponent -12 - 8 = -20 and a * 2^20 = 384 is exact, so it keeps a; ones are
+# exact. Quantizing along the documented direction keeps 256 on one line and a
+# everywhere else; quantizing along the transposed direction instead zeroes the a of
+# the line/column through [0][0] and gives the other results listed.
+A_SMALL = 1.5 * 2.0 ** -12
+
+
+def _naive_case(outlier_first):
+    t = np.full((32, 32), A_SMALL)
+    t[0, 0] = 256.0
+    ones = np.ones((32, 32))
+    return (t, ones) if outlier_first else (ones, t)
+
+
+def _line_and_rest(v, first_axis):
+    """Expected [32][32] result: 256 on line 0 of the given axis, 32a elsewhere."""
+    e = np.full((32, 32), 32 * A_SMALL)
+    if first_axis == 0:
+        e[0, :] = 256.0
+    else:
+        e[:, 0] = 256.0
+    return e
+
+
+NAIVE_SHAPE = ConvShape(1, 32, 1, 32, 32, 1, 1, 1, 0)
+
+
+@pytest.mark.parametrize("outlier_in", ["x", "w"])
+def test_naive_forward_quantizes_both_operands_along_k(outlier_in):
+    """Y[m][co] = sum_k Q_k(X')[m][k] Q_k(W_f)[co][k]. Along k: Y = 256 on the
+    line through the outlier, 32a elsewhere (along m or co instead, the other
+    lines would get 31a and the outlier's line 256 + 31a)."""
+    xm, wm = _naive_case(outlier_in == "x")
+    x = xm.reshape(1, 32, 1, 32).astype(np.float32)
+    w = wm.reshape(32, 1, 1, 32).astype(np.float32)
+    y, counts = oracle.naive_fwd(NAIVE_SHAPE, x, w, 0, 0)
+    y = y.reshape(32, 32)  # [m][co]
+    np.testing.assert_array_equal(y, _line_and_rest(None, 0 if outlier_in == "x" else 1))
+
+
+@pytest.mark.parametrize("outlier_in", ["dy", "w"])
+def test_naive_backward_data_quantizes_along_cout(outlier_in):
+    """G_X'[m][k] = sum_co Q_co(G_Y)[m][co] Q_co(W_f)[co][k], then col2im (the
+    identity here). With the outlier in G_Y[0][0] the m = 0 line is 256, with
+    it in W_f[0][0] the k = 0 line is; 32a elsewhere."""
+    dym, wm = _naive_case(outlier_in == "dy")
+    dy = dym.reshape(1, 32, 1, 32).astype(np.float32)
+    w = wm.reshape(32, 1, 1, 32).astype(np.float32)
+    dx, _ = oracle.naive_dgrad(NAIVE_SHAPE, dy, w, 0, 0)
+    np.testing.assert_array_equal(dx.reshape(32, 32), _line_and_rest(None, 0 if outlier_in == "dy" else 1))
+
+
+@pytest.mark.parametrize("outlier_in", ["dy", "x"])
+def test_naive_backward_weight_quantizes_along_m(outlier_in):
+    """G_W[co][k] = sum_m Q_m(G_Y)[m][co] Q_m(X')[m][k]. With the outlier in
+    G_Y[0][0] the co = 0 line is 256, with it in X'[0][0] the k = 0 line is;
+    32a elsewhere."""
+    dym, xm = _naive_case(outlier_in == "dy")
+    dy = dym.reshape(1, 32, 1, 32).astype(np.float32)
+    x = xm.reshape(1, 32, 1, 32).astype(np.float32)
+    dw, _ = oracle.naive_wgrad(NAIVE_SHAPE, dy, x, 0, 0)
+    np.testing.assert_array_equal(dw.reshape(32, 32), _line_and_rest(None, 0 if outlier_in == "dy" else 1))
