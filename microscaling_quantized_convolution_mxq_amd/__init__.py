@@ -17,6 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmqconv.so")
 
 MQ_OK = 0
+MQ_ERR_SHAPE = -2
 STATUS_NAMES = {0: "MQ_OK", -1: "MQ_ERR_NULL", -2: "MQ_ERR_SHAPE", -3: "MQ_ERR_FORMAT",
                 -4: "MQ_ERR_ALIGN", -5: "MQ_ERR_WORKSPACE", -6: "MQ_ERR_UNSUPPORTED", -7: "MQ_ERR_HIP"}
 E4M3, E5M2, E2M3, E3M2, E2M1 = 0, 1, 2, 3, 4
@@ -25,9 +26,10 @@ OP_FWD, OP_DGRAD, OP_WGRAD = 0, 1, 2
 
 
 class MqConvError(RuntimeError):
-    def __init__(self, status: int, where: str):
+    def __init__(self, status: int, where: str, detail: str = ""):
         self.status = status
-        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} ({_status_string(status)})")
+        msg = f"{where}: {STATUS_NAMES.get(status, status)}"
+        super().__init__(msg + (f" ({detail})" if detail else f" ({_status_string(status)})"))
 
 
 class mq_conv(ctypes.Structure):
@@ -113,6 +115,54 @@ def _ptr(t) -> Optional[int]:
     return t.data_ptr() if hasattr(t, "data_ptr") else int(t)
 
 
+def _buf(t, nbytes: int, dtype: Optional[str], what: str) -> Optional[int]:
+    """Device address of a buffer handed to the library. A torch tensor must
+    be contiguous, of the expected dtype (None: any), hold at least `nbytes`
+    bytes and live on the GPU, else MqConvError(MQ_ERR_SHAPE) is raised before
+    the C call: the C side sees raw pointers and cannot check any of this. A
+    plain integer address is passed through unchecked (the caller vouches for
+    it)."""
+    if t is None or not hasattr(t, "data_ptr"):
+        return _ptr(t)
+    if dtype is not None and str(t.dtype) != "torch." + dtype:
+        raise MqConvError(MQ_ERR_SHAPE, what, f"dtype {t.dtype}, expected torch.{dtype}")
+    if not t.is_contiguous():
+        raise MqConvError(MQ_ERR_SHAPE, what, "tensor is not contiguous")
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise MqConvError(MQ_ERR_SHAPE, what, f"{have} bytes, needs {nbytes}")
+    if not t.is_cuda:
+        raise MqConvError(MQ_ERR_SHAPE, what, "not a GPU tensor")
+    return t.data_ptr()
+
+
+def _f32(t, count: int, what: str) -> Optional[int]:
+    return _buf(t, 4 * count, "float32", what)
+
+
+def _dims(shape):
+    """(n, cin, h, w, cout, kh, kw, ho, wo) of a convolution."""
+    c = _conv(shape)
+    ho = (c.h + 2 * c.pad_h - c.kh) // c.stride_h + 1 if c.stride_h > 0 else 0
+    wo = (c.w + 2 * c.pad_w - c.kw) // c.stride_w + 1 if c.stride_w > 0 else 0
+    return c.n, c.cin, c.h, c.w, c.cout, c.kh, c.kw, max(ho, 0), max(wo, 0)
+
+
+def _nx(shape):
+    n, cin, h, w, *_ = _dims(shape)
+    return h * w * n * cin
+
+
+def _nw(shape):
+    _, cin, _, _, cout, kh, kw, _, _ = _dims(shape)
+    return cout * kh * kw * cin
+
+
+def _ny(shape):
+    n, _, _, _, cout, _, _, ho, wo = _dims(shape)
+    return ho * wo * n * cout
+
+
 def _stream(stream) -> Optional[int]:
     if stream is None:
         import torch
@@ -140,8 +190,14 @@ class MxTensor:
         return MxTensor(torch.empty(nc, dtype=torch.uint8, device=device),
                         torch.empty(ns, dtype=torch.uint8, device=device), fmt, bp, role, tuple(dims))
 
-    def c_struct(self) -> mq_mx:
-        return mq_mx(_ptr(self.codes), _ptr(self.scales), self.fmt, self.bp, self.role, *self.dims)
+    def c_struct(self, what: str = "MxTensor") -> mq_mx:
+        """The C view; tensor buffers are checked against the sizes the
+        layout needs (invalid role/format/dims are left to the C call, which
+        reports them with its own status)."""
+        nc = mqconv_codes_bytes(self.role, self.fmt, *self.dims)
+        ns = mqconv_scales_bytes(self.role, self.bp, *self.dims)
+        return mq_mx(_buf(self.codes, nc, "uint8", what + ".codes"), _buf(self.scales, ns, "uint8", what + ".scales"),
+                     self.fmt, self.bp, self.role, *self.dims)
 
 
 def mqconv_abi_version() -> int:
@@ -168,8 +224,16 @@ def mqconv_im2col_scales_bytes(shape, bp: int) -> int:
     return lib().mqconv_im2col_scales_bytes(ctypes.byref(_conv(shape)), bp)
 
 
+def _prod(d):
+    r = 1
+    for v in d:
+        r *= int(v)
+    return r
+
+
 def mqconv_quantize(src, dst: MxTensor, stream=None) -> None:
-    _check(lib().mqconv_quantize(_ptr(src), dst.c_struct(), _stream(stream)), "mqconv_quantize")
+    _check(lib().mqconv_quantize(_f32(src, _prod(dst.dims), "src"), dst.c_struct("dst"), _stream(stream)),
+           "mqconv_quantize")
 
 
 QUANTIZE_GROUP_MAX = 8
@@ -179,14 +243,16 @@ def mqconv_quantize_group(pairs, stream=None) -> None:
     """mqconv_quantize of several (src, dst MxTensor) pairs in one call."""
     pairs = list(pairs)
     n = len(pairs)
-    srcs = (ctypes.c_void_p * max(1, n))(*[_ptr(p[0]) for p in pairs])
-    dsts = (mq_mx * max(1, n))(*[p[1].c_struct() for p in pairs])
+    srcs = (ctypes.c_void_p * max(1, n))(*[_f32(p[0], _prod(p[1].dims), f"src[{i}]") for i, p in enumerate(pairs)])
+    dsts = (mq_mx * max(1, n))(*[p[1].c_struct(f"dst[{i}]") for i, p in enumerate(pairs)])
     _check(lib().mqconv_quantize_group(n, srcs, dsts, _stream(stream)), "mqconv_quantize_group")
 
 
 def mqconv_cbf_im2col(shape, xq: MxTensor, col_codes, col_scales, stream=None) -> None:
-    _check(lib().mqconv_cbf_im2col(ctypes.byref(_conv(shape)), xq.c_struct(), _ptr(col_codes),
-                                   _ptr(col_scales), _stream(stream)), "mqconv_cbf_im2col")
+    cc = _buf(col_codes, mqconv_im2col_codes_bytes(shape, xq.fmt), "uint8", "col_codes")
+    cs = _buf(col_scales, mqconv_im2col_scales_bytes(shape, xq.bp), "uint8", "col_scales")
+    _check(lib().mqconv_cbf_im2col(ctypes.byref(_conv(shape)), xq.c_struct("xq"), cc, cs, _stream(stream)),
+           "mqconv_cbf_im2col")
 
 
 def mqconv_workspace_bytes(shape, op: int, fa: int, fb: int) -> int:
@@ -194,39 +260,42 @@ def mqconv_workspace_bytes(shape, op: int, fa: int, fb: int) -> int:
 
 
 def _ws(ws):
+    """(address, bytes) of a workspace; its size is checked by the C call."""
     if ws is None:
         return None, 0
-    return _ptr(ws), ws.numel() * ws.element_size()
+    if not hasattr(ws, "data_ptr"):
+        raise MqConvError(MQ_ERR_SHAPE, "ws", "a workspace must be a tensor (its size is passed on)")
+    return _buf(ws, 0, None, "ws"), ws.numel() * ws.element_size()
 
 
 def mqconv_forward(shape, xq: MxTensor, wq: MxTensor, y, ws=None, stream=None) -> None:
     p, n = _ws(ws)
-    _check(lib().mqconv_forward(ctypes.byref(_conv(shape)), xq.c_struct(), wq.c_struct(), _ptr(y), p, n,
-                                _stream(stream)), "mqconv_forward")
+    _check(lib().mqconv_forward(ctypes.byref(_conv(shape)), xq.c_struct("xq"), wq.c_struct("wq"),
+                                _f32(y, _ny(shape), "y"), p, n, _stream(stream)), "mqconv_forward")
 
 
 def mqconv_forward_mx(shape, xq: MxTensor, wq: MxTensor, yq: MxTensor, ws=None, stream=None) -> None:
     p, n = _ws(ws)
-    _check(lib().mqconv_forward_mx(ctypes.byref(_conv(shape)), xq.c_struct(), wq.c_struct(), yq.c_struct(), p, n,
-                                   _stream(stream)), "mqconv_forward_mx")
+    _check(lib().mqconv_forward_mx(ctypes.byref(_conv(shape)), xq.c_struct("xq"), wq.c_struct("wq"),
+                                   yq.c_struct("yq"), p, n, _stream(stream)), "mqconv_forward_mx")
 
 
 def mqconv_backward_data(shape, dyq: MxTensor, wq: MxTensor, dx, ws=None, stream=None) -> None:
     p, n = _ws(ws)
-    _check(lib().mqconv_backward_data(ctypes.byref(_conv(shape)), dyq.c_struct(), wq.c_struct(), _ptr(dx), p,
-                                      n, _stream(stream)), "mqconv_backward_data")
+    _check(lib().mqconv_backward_data(ctypes.byref(_conv(shape)), dyq.c_struct("dyq"), wq.c_struct("wq"),
+                                      _f32(dx, _nx(shape), "dx"), p, n, _stream(stream)), "mqconv_backward_data")
 
 
 def mqconv_backward_data_mx(shape, dyq: MxTensor, wq: MxTensor, dxq: MxTensor, ws=None, stream=None) -> None:
     p, n = _ws(ws)
-    _check(lib().mqconv_backward_data_mx(ctypes.byref(_conv(shape)), dyq.c_struct(), wq.c_struct(), dxq.c_struct(),
-                                         p, n, _stream(stream)), "mqconv_backward_data_mx")
+    _check(lib().mqconv_backward_data_mx(ctypes.byref(_conv(shape)), dyq.c_struct("dyq"), wq.c_struct("wq"),
+                                         dxq.c_struct("dxq"), p, n, _stream(stream)), "mqconv_backward_data_mx")
 
 
 def mqconv_backward_weight(shape, dyq: MxTensor, xq: MxTensor, dw, ws=None, stream=None) -> None:
     p, n = _ws(ws)
-    _check(lib().mqconv_backward_weight(ctypes.byref(_conv(shape)), dyq.c_struct(), xq.c_struct(), _ptr(dw),
-                                        p, n, _stream(stream)), "mqconv_backward_weight")
+    _check(lib().mqconv_backward_weight(ctypes.byref(_conv(shape)), dyq.c_struct("dyq"), xq.c_struct("xq"),
+                                        _f32(dw, _nw(shape), "dw"), p, n, _stream(stream)), "mqconv_backward_weight")
 
 
 def mqconv_naive_workspace_bytes(shape, op: int, fa: int, fb: int) -> int:
@@ -235,17 +304,20 @@ def mqconv_naive_workspace_bytes(shape, op: int, fa: int, fb: int) -> int:
 
 def mqconv_naive_forward(shape, x, w, fx: int, fw: int, y, ws, stream=None) -> None:
     p, n = _ws(ws)
-    _check(lib().mqconv_naive_forward(ctypes.byref(_conv(shape)), _ptr(x), _ptr(w), fx, fw, _ptr(y), p, n,
-                                      _stream(stream)), "mqconv_naive_forward")
+    _check(lib().mqconv_naive_forward(ctypes.byref(_conv(shape)), _f32(x, _nx(shape), "x"), _f32(w, _nw(shape), "w"),
+                                      fx, fw, _f32(y, _ny(shape), "y"), p, n, _stream(stream)),
+           "mqconv_naive_forward")
 
 
 def mqconv_naive_backward_data(shape, dy, w, fdy: int, fw: int, dx, ws, stream=None) -> None:
     p, n = _ws(ws)
-    _check(lib().mqconv_naive_backward_data(ctypes.byref(_conv(shape)), _ptr(dy), _ptr(w), fdy, fw, _ptr(dx),
-                                            p, n, _stream(stream)), "mqconv_naive_backward_data")
+    _check(lib().mqconv_naive_backward_data(ctypes.byref(_conv(shape)), _f32(dy, _ny(shape), "dy"),
+                                            _f32(w, _nw(shape), "w"), fdy, fw, _f32(dx, _nx(shape), "dx"), p, n,
+                                            _stream(stream)), "mqconv_naive_backward_data")
 
 
 def mqconv_naive_backward_weight(shape, dy, x, fdy: int, fx: int, dw, ws, stream=None) -> None:
     p, n = _ws(ws)
-    _check(lib().mqconv_naive_backward_weight(ctypes.byref(_conv(shape)), _ptr(dy), _ptr(x), fdy, fx,
-                                              _ptr(dw), p, n, _stream(stream)), "mqconv_naive_backward_weight")
+    _check(lib().mqconv_naive_backward_weight(ctypes.byref(_conv(shape)), _f32(dy, _ny(shape), "dy"),
+                                              _f32(x, _nx(shape), "x"), fdy, fx, _f32(dw, _nw(shape), "dw"), p, n,
+                                              _stream(stream)), "mqconv_naive_backward_weight")

@@ -156,3 +156,53 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(mq, "_lib", None)
     with pytest.raises(ImportError):
         mq.lib()
+
+
+def test_binding_checks_tensor_buffers_before_the_call():
+    """Device, dtype, contiguity and byte size of every torch buffer are
+    checked by the binding (the C side only sees raw pointers). CPU tensors
+    stand in here: each malformed buffer is rejected with MQ_ERR_SHAPE for its
+    own reason before the device check, a well-formed one for being on the
+    CPU."""
+    import torch
+    s = ConvShape(4, 40, 6, 5, 36, 3, 3, 2, 1)
+    nc = mq.mqconv_codes_bytes(mq.ROLE_ACT, 0, s.h, s.w, s.n, s.cin)
+    ns = mq.mqconv_scales_bytes(mq.ROLE_ACT, 32, s.h, s.w, s.n, s.cin)
+
+    def act(codes=None, scales=None):
+        return mq.MxTensor(torch.zeros(nc, dtype=torch.uint8) if codes is None else codes,
+                           torch.zeros(ns, dtype=torch.uint8) if scales is None else scales,
+                           0, 32, mq.ROLE_ACT, (s.h, s.w, s.n, s.cin))
+
+    def reason(fn, *args):
+        with pytest.raises(mq.MqConvError) as e:
+            fn(*args, stream=0)
+        assert e.value.status == -2
+        return str(e.value)
+
+    src = torch.zeros(s.h * s.w * s.n * s.cin)
+    assert "dtype" in reason(mq.mqconv_quantize, src.double(), act())
+    assert "contiguous" in reason(mq.mqconv_quantize, torch.zeros(2 * src.numel())[::2], act())
+    assert "needs" in reason(mq.mqconv_quantize, src[:-1], act())
+    assert "needs" in reason(mq.mqconv_quantize, FAKE, act(codes=torch.zeros(nc - 1, dtype=torch.uint8)))
+    assert "dtype" in reason(mq.mqconv_quantize, FAKE, act(codes=FAKE, scales=torch.zeros(ns, dtype=torch.int8)))
+    assert "GPU" in reason(mq.mqconv_quantize, src, act())
+    assert "src[1]" in reason(mq.mqconv_quantize_group, [(FAKE, _mx(mq.ROLE_ACT, (s.h, s.w, s.n, s.cin))),
+                                                         (src[:5], act())])
+    x = _mx(mq.ROLE_ACT, (s.h, s.w, s.n, s.cin))
+    w = _mx(mq.ROLE_WEIGHT, (s.cout, s.kh, s.kw, s.cin))
+    dy = _mx(mq.ROLE_GRAD, (s.ho, s.wo, s.n, s.cout), fmt=1)
+    ny, nxe, nwe = s.ho * s.wo * s.n * s.cout, s.h * s.w * s.n * s.cin, s.cout * s.kh * s.kw * s.cin
+    ccb = mq.mqconv_im2col_codes_bytes(s, 0)
+    assert "col_codes" in reason(mq.mqconv_cbf_im2col, s, x, torch.zeros(ccb - 16, dtype=torch.uint8), FAKE)
+    assert "y: MQ_ERR_SHAPE" in reason(mq.mqconv_forward, s, x, w, torch.zeros(ny - 1))
+    assert "needs" in reason(mq.mqconv_forward, s, x, w, torch.zeros(ny - 1))
+    assert "GPU" in reason(mq.mqconv_forward, s, x, w, torch.zeros(ny))
+    assert "needs" in reason(mq.mqconv_backward_data, s, dy, w, torch.zeros(nxe - 1))
+    assert "needs" in reason(mq.mqconv_backward_weight, s, dy, x, torch.zeros(nwe - 1))
+    assert "dtype" in reason(mq.mqconv_backward_weight, s, dy, x, torch.zeros(nwe, dtype=torch.float16))
+    assert "GPU" in reason(mq.mqconv_backward_weight, s, dy, x, FAKE, torch.zeros(16, dtype=torch.uint8))
+    assert "workspace" in reason(mq.mqconv_backward_weight, s, dy, x, FAKE, FAKE)
+    assert "needs" in reason(mq.mqconv_naive_forward, s, torch.zeros(nxe - 1), FAKE, 0, 0, FAKE, None)
+    assert "needs" in reason(mq.mqconv_naive_backward_data, s, FAKE, torch.zeros(nwe - 1), 1, 0, FAKE, None)
+    assert "needs" in reason(mq.mqconv_naive_backward_weight, s, FAKE, FAKE, 1, 0, torch.zeros(nwe - 1), None)
