@@ -88,7 +88,8 @@ def lib() -> ctypes.CDLL:
 EXPORTED = ("mqconv_abi_version", "mqconv_status_string", "mqconv_codes_bytes", "mqconv_scales_bytes",
             "mqconv_im2col_codes_bytes", "mqconv_im2col_scales_bytes", "mqconv_quantize", "mqconv_quantize_group",
             "mqconv_cbf_im2col", "mqconv_workspace_bytes", "mqconv_forward", "mqconv_forward_mx", "mqconv_backward_data",
-            "mqconv_backward_data_mx", "mqconv_backward_weight", "mqconv_naive_workspace_bytes", "mqconv_naive_forward",
+            "mqconv_backward_data_mx", "mqconv_backward_weight",
+            "mqconv_naive_workspace_bytes", "mqconv_naive_forward",
             "mqconv_naive_backward_data", "mqconv_naive_backward_weight")
 
 

@@ -86,8 +86,7 @@ static int wgrad_splits(const Conv& cv, int fdy, int fx) {
   const long long npix = (long long)cv.ho() * cv.wo();
   const long long nNB = ceil_div(cv.n, 32);
   const long long ops = npix * cv.cout * nNB * run_bytes(fdy) + (long long)cv.h * cv.w * cv.cin * nNB * run_bytes(fx);
-  // the same count for either step size (the workspace size depends on it):
-  // capped by the number of four-block steps
+  // the same count for either step size: capped by the number of four-block steps
   const WgradSteps ks = wgrad_steps(cv, 4);
   const long long nkb = (long long)cv.ho() * cv.wo() * ceil_div(cv.n, 32);
   int s = splitk_slices(cv.cout, (long long)cv.kh * cv.kw * cv.cin, nkb, ops);
@@ -96,48 +95,95 @@ static int wgrad_splits(const Conv& cv, int fdy, int fx) {
   return s;
 }
 
+// How the backward-weight GEMM reads its operands and how much workspace it
+// uses: 8-bit codes are read where quantization left them (K-major staging)
+// when a 16-channel chunk of B stays in one tap and a K-block's lines are
+// the N values of one pixel (natural); otherwise both are first re-laid with
+// runs along N; with 8-bit gradient codes and other activation codes
+// (mixed) only the activation is re-laid. Workspace: [re-laid dY][re-laid
+// X][fp32 partial sums of the S slices], each part present only when used.
+struct WgradPlan {
+  bool natural, mixed, half;
+  int kps, S;
+  size_t dyt_b, xt_b, part_b;
+};
+static WgradPlan wgrad_plan(const Conv& cv, int fdy, int fx) {
+  WgradPlan w;
+  const int ga = 32, gb = cv.cin % 32 == 0 ? 32 : 0, khalf = cv.n <= 16;
+  const bool kext_ok = cv.n <= 32 || cv.n % 32 == 0;
+  w.natural = fdy <= 1 && fx <= 1 && cv.cin % 16 == 0 && kext_ok;
+  w.mixed = !w.natural && fdy <= 1 && kext_ok;
+  w.half = !w.natural && half_k_blocks(ga, gb, khalf, fdy, fx);
+  // half K-blocks take four K-blocks per step and two wave groups per
+  // workgroup, so half as many slices cover the K range
+  w.kps = half_k_blocks(ga, gb, khalf, fdy, fx) ? 4 : 2;
+  const int S0 = wgrad_splits(cv, fdy, fx);
+  w.S = w.kps == 4 ? ceil_div(S0, 2) : S0;
+  const long long npix_o = (long long)cv.ho() * cv.wo();
+  w.dyt_b = (!w.natural && !w.mixed) ? align256(transposed_bytes(fdy, npix_o, cv.n, 1, cv.cout)) : 0;
+  w.xt_b = !w.natural ? align256(transposed_bytes(fx, (long long)cv.h * cv.w, cv.n, 1, cv.cin)) : 0;
+  w.part_b = w.S > 1 ? align256((size_t)w.S * cv.cout * cv.kh * cv.kw * cv.cin * 4) : 0;
+  return w;
+}
+
 size_t gemm_workspace_bytes(const Conv& cv, int op, int fa, int fb) {
   if (op == 0) return 0;
-  if (op == 1) {  // W re-laid with runs along Cout
-    return align256(transposed_bytes(fb, 1, cv.cout, (long long)cv.kh * cv.kw, cv.cin));
+  if (op == 1) {  // 6/4-bit W re-laid with runs along Cout (8-bit W is read in place)
+    return fb <= 1 ? 0 : align256(transposed_bytes(fb, 1, cv.cout, (long long)cv.kh * cv.kw, cv.cin));
   }
   // op 2: fa = gradient format, fb = activation format
-  const size_t dyt = align256(transposed_bytes(fa, (long long)cv.ho() * cv.wo(), cv.n, 1, cv.cout));
-  const size_t xt = align256(transposed_bytes(fb, (long long)cv.h * cv.w, cv.n, 1, cv.cin));
-  const int S = wgrad_splits(cv, fa, fb);
-  const size_t part = S > 1 ? align256((size_t)S * cv.cout * cv.kh * cv.kw * cv.cin * 4) : 0;
-  return dyt + xt + part;
+  const WgradPlan w = wgrad_plan(cv, fa, fb);
+  return w.dyt_b + w.xt_b + w.part_b;
+}
+
+// Offsets of the kernels' buffer loads are 32-bit: every operand buffer plus
+// the bias in front of it (padding, backward taps) must stay below the
+// offset that marks invalid blocks. The same quantities as the launchers.
+bool gemm_offsets_ok(const Conv& cv, int op, int fa, int fb, int bpa) {
+  if (op == 0) {  // forward: fa = X format, bpa = X bp
+    const long long ncb = ceil_div(cv.cin, 32), xrb = ncb * run_bytes(fa), xnPB = ceil_div(cv.n, bpa);
+    const long long lead = (long long)cv.ph * cv.w + cv.pw;
+    return offsets_fit((long long)cv.h * cv.w * cv.n * xrb, lead * cv.n * xrb) &&
+           offsets_fit((long long)cv.h * cv.w * xnPB * ncb, lead * xnPB * ncb);
+  }
+  if (op == 1) {  // backward-data: fa = dY format, bpa = dY bp
+    const long long ncob = ceil_div(cv.cout, 32), dyrb = ncob * run_bytes(fa), dynPB = ceil_div(cv.n, bpa);
+    const long long dmax = (long long)(ceil_div(cv.kh, cv.sh) - 1) * cv.wo() + (ceil_div(cv.kw, cv.sw) - 1);
+    return offsets_fit((long long)cv.ho() * cv.wo() * cv.n * dyrb, dmax * cv.n * dyrb) &&
+           offsets_fit((long long)cv.ho() * cv.wo() * dynPB * ncob, dmax * dynPB * ncob);
+  }
+  // backward-weight: fa = dY format, fb = X format
+  const WgradPlan w = wgrad_plan(cv, fa, fb);
+  const long long nNB = ceil_div(cv.n, 32), ncbi = ceil_div(cv.cin, 32);
+  const long long xRB = w.half ? 16 : run_bytes(fb);
+  const long long lead = (long long)cv.ph * cv.w + cv.pw;
+  bool ok = offsets_fit((long long)cv.h * cv.w * nNB * ncbi, lead * nNB * ncbi);
+  if (w.natural) {
+    const long long xrb = row_bytes(fb, cv.cin);
+    ok = ok && offsets_fit((long long)cv.h * cv.w * cv.n * xrb, lead * cv.n * xrb);
+  } else {
+    ok = ok && offsets_fit((long long)cv.h * cv.w * cv.cin * nNB * xRB, lead * cv.cin * nNB * xRB);
+  }
+  return ok;
 }
 
 hipError_t launch_backward_weight(const Conv& cv, MxView dy, MxView x, float* dw, void* ws, size_t,
                                   hipStream_t st) {
+  const WgradPlan plan = wgrad_plan(cv, dy.fmt, x.fmt);
   uint8_t* base = static_cast<uint8_t*>(ws);
   const long long npix_o = (long long)cv.ho() * cv.wo();
   uint8_t* dyt = base;
-  const size_t dyt_b = align256(transposed_bytes(dy.fmt, npix_o, cv.n, 1, cv.cout));
-  uint8_t* xt = base + dyt_b;
-  const size_t xt_b = align256(transposed_bytes(x.fmt, (long long)cv.h * cv.w, cv.n, 1, cv.cin));
-  float* part = reinterpret_cast<float*>(base + dyt_b + xt_b);
+  uint8_t* xt = base + plan.dyt_b;
+  float* part = reinterpret_cast<float*>(base + plan.dyt_b + plan.xt_b);
+  const bool natural = plan.natural, mixed = plan.mixed, half = plan.half;
+  const int S = plan.S;
   WgradProb p;
   // rows of A are Cout (32 to a block); rows of B are (tap, Cin), whose
   // 32-channel blocks line up with 32-row groups when Cin is a multiple of 32
   p.khalf = cv.n <= 16;
   p.ga = 32;
   p.gb = cv.cin % 32 == 0 ? 32 : 0;
-  // 8-bit codes are read where quantization left them (K-major staging)
-  // when a 16-channel chunk of B stays in one tap and a K-block's lines are
-  // the N values of one pixel; otherwise both are first re-laid with runs
-  // along N; with 8-bit gradient codes and other activation codes (mixed)
-  // only the activation is re-laid
-  const bool kext_ok = cv.n <= 32 || cv.n % 32 == 0;
-  const bool natural = dy.fmt <= 1 && x.fmt <= 1 && cv.cin % 16 == 0 && kext_ok;
-  const bool mixed = !natural && dy.fmt <= 1 && kext_ok;
-  const bool half = !natural && half_k_blocks(p.ga, p.gb, p.khalf, dy.fmt, x.fmt);
-  // as the kernel choice below: half K-blocks take four K-blocks per step and
-  // two wave groups per workgroup, so half as many slices cover the K range
-  p.kps = half_k_blocks(p.ga, p.gb, p.khalf, dy.fmt, x.fmt) ? 4 : 2;
-  const int S0 = wgrad_splits(cv, dy.fmt, x.fmt);  // the workspace holds S0 slices
-  const int S = p.kps == 4 ? ceil_div(S0, 2) : S0;
+  p.kps = plan.kps;
   p.dytc = dyt; p.dys = dy.scales; p.xtc = xt; p.xs = x.scales; p.part = S > 1 ? part : dw;
   p.N = cv.n; p.H = cv.h; p.W = cv.w; p.Cin = cv.cin; p.Cout = cv.cout; p.KW = cv.kw;
   p.T = cv.kh * cv.kw; p.sh = cv.sh; p.sw = cv.sw; p.ph = cv.ph; p.pw = cv.pw; p.Ho = cv.ho(); p.Wo = cv.wo();
@@ -150,9 +196,21 @@ hipError_t launch_backward_weight(const Conv& cv, MxView dy, MxView x, float* dw
   // padding moves the taps of the first output pixels before the buffer
   const long long lead = (long long)cv.ph * cv.w + cv.pw;
   p.xtcb = (int)(lead * cv.cin * p.nNB * p.xRB); p.xsb = (int)(lead * p.nNB * p.ncbi);
+  // (gemm_offsets_ok has been checked by the caller; these never fail then)
   if (!offsets_fit(p.xtc_bytes, p.xtcb) || !offsets_fit(p.xs_bytes, p.xsb)) return hipErrorInvalidValue;
-  // every check of the re-laid path has passed: only now is anything enqueued
-  // (the in-place path re-lays nothing; its own check follows)
+  p.dCin = make_fastdiv(cv.cin); p.dKW = make_fastdiv(cv.kw);
+  p.dnsub = make_fastdiv(ks.nsub); p.dWo = make_fastdiv(p.Wo);
+  const long long nj = (long long)p.T * cv.cin;
+  WgradNatProb q;
+  if (natural) {
+    static_cast<WgradProb&>(q) = p;
+    q.dyrb = (int)row_bytes(dy.fmt, cv.cout); q.xrb = (int)row_bytes(x.fmt, cv.cin);
+    q.dytc = dy.codes; q.dytc_bytes = npix_o * cv.n * q.dyrb;
+    q.xtc = x.codes; q.xtc_bytes = (long long)cv.h * cv.w * cv.n * q.xrb;
+    q.xtcb = (int)(lead * cv.n * q.xrb);
+    if (!offsets_fit(q.xtc_bytes, q.xtcb)) return hipErrorInvalidValue;
+  }
+  // every check has passed: only now is anything enqueued
   hipError_t e = hipSuccess;
   if (!natural && !mixed) {
     e = launch_transpose_codes(dy.codes, dyt, dy.fmt, half, (int)npix_o, cv.n, 1, cv.cout, st);
@@ -162,24 +220,14 @@ hipError_t launch_backward_weight(const Conv& cv, MxView dy, MxView x, float* dw
     e = launch_transpose_codes(x.codes, xt, x.fmt, half, cv.h * cv.w, cv.n, 1, cv.cin, st);
     if (e != hipSuccess) return e;
   }
-  p.dCin = make_fastdiv(cv.cin); p.dKW = make_fastdiv(cv.kw);
-  p.dnsub = make_fastdiv(ks.nsub); p.dWo = make_fastdiv(p.Wo);
-  const long long nj = (long long)p.T * cv.cin;
   if (natural) {
-    WgradNatProb q;
-    static_cast<WgradProb&>(q) = p;
-    q.dyrb = (int)row_bytes(dy.fmt, cv.cout); q.xrb = (int)row_bytes(x.fmt, cv.cin);
-    q.dytc = dy.codes; q.dytc_bytes = npix_o * cv.n * q.dyrb;
-    q.xtc = x.codes; q.xtc_bytes = (long long)cv.h * cv.w * cv.n * q.xrb;
-    q.xtcb = (int)(lead * cv.n * q.xrb);
-    if (!offsets_fit(q.xtc_bytes, q.xtcb)) return hipErrorInvalidValue;
     e = launch_tiled(dy.fmt, x.fmt, q, cv.cout, (int)nj, S, st);
   } else if (mixed) {  // (half K-blocks need 8-bit activation codes: never here)
-    WgradMixProb q;
-    static_cast<WgradProb&>(q) = p;
-    q.dyrb = (int)row_bytes(dy.fmt, cv.cout);
-    q.dytc = dy.codes; q.dytc_bytes = npix_o * cv.n * q.dyrb;
-    e = launch_tiled(dy.fmt, x.fmt, q, cv.cout, (int)nj, S, st);
+    WgradMixProb r;
+    static_cast<WgradProb&>(r) = p;
+    r.dyrb = (int)row_bytes(dy.fmt, cv.cout);
+    r.dytc = dy.codes; r.dytc_bytes = npix_o * cv.n * r.dyrb;
+    e = launch_tiled(dy.fmt, x.fmt, r, cv.cout, (int)nj, S, st);
   } else {
     e = launch_tiled(dy.fmt, x.fmt, p, cv.cout, (int)nj, S, st);
   }

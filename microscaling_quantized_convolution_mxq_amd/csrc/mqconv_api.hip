@@ -180,6 +180,7 @@ int mqconv_forward(const mq_conv* cv, mq_mx xq, mq_mx wq, float* y, void* ws, si
   if (s != MQ_OK) return s;
   if (!y) return MQ_ERR_NULL;
   if ((uintptr_t)y & 3u) return MQ_ERR_ALIGN;
+  if (!gemm_offsets_ok(to_conv(cv), 0, xq.fmt, wq.fmt, xq.block_partner)) return MQ_ERR_SHAPE;
   const size_t need = gemm_workspace_bytes(to_conv(cv), 0, xq.fmt, wq.fmt);
   if (need > 0 && (!ws || ws_bytes < need)) return MQ_ERR_WORKSPACE;
   return hip_status(launch_forward(to_conv(cv), view(xq), view(wq), y, ws, ws_bytes, (hipStream_t)stream));
@@ -197,6 +198,7 @@ int mqconv_forward_mx(const mq_conv* cv, mq_mx xq, mq_mx wq, mq_mx yq, void* ws,
   if (s != MQ_OK) return s;
   // a block of 32 batch rows must not straddle two 32-row groups of output rows
   if (yq.block_partner == 32 && cv->n % 32 != 0 && 32 % cv->n != 0) return MQ_ERR_UNSUPPORTED;
+  if (!gemm_offsets_ok(c, 0, xq.fmt, wq.fmt, xq.block_partner)) return MQ_ERR_SHAPE;
   const size_t need = gemm_workspace_bytes(c, 0, xq.fmt, wq.fmt);
   if (need > 0 && (!ws || ws_bytes < need)) return MQ_ERR_WORKSPACE;
   MxOutView y{static_cast<uint8_t*>(yq.codes), yq.scales, yq.fmt, yq.block_partner};
@@ -215,6 +217,7 @@ int mqconv_backward_data(const mq_conv* cv, mq_mx dyq, mq_mx wq, float* dx, void
   if (wq.block_partner != 32) return MQ_ERR_UNSUPPORTED;
   if (!dx) return MQ_ERR_NULL;
   if ((uintptr_t)dx & 3u) return MQ_ERR_ALIGN;
+  if (!gemm_offsets_ok(c, 1, dyq.fmt, wq.fmt, dyq.block_partner)) return MQ_ERR_SHAPE;
   const size_t need = gemm_workspace_bytes(c, 1, dyq.fmt, wq.fmt);
   if (need > 0 && (!ws || ws_bytes < need)) return MQ_ERR_WORKSPACE;
   if (ws && !aligned16(ws)) return MQ_ERR_ALIGN;
@@ -235,6 +238,7 @@ int mqconv_backward_data_mx(const mq_conv* cv, mq_mx dyq, mq_mx wq, mq_mx dxq, v
   if (wq.block_partner != 32) return MQ_ERR_UNSUPPORTED;
   // a block of 32 batch rows must not straddle two 32-row groups of output rows
   if (dxq.block_partner == 32 && cv->n % 32 != 0 && 32 % cv->n != 0) return MQ_ERR_UNSUPPORTED;
+  if (!gemm_offsets_ok(c, 1, dyq.fmt, wq.fmt, dyq.block_partner)) return MQ_ERR_SHAPE;
   const size_t need = gemm_workspace_bytes(c, 1, dyq.fmt, wq.fmt);
   if (need > 0 && (!ws || ws_bytes < need)) return MQ_ERR_WORKSPACE;
   if (ws && !aligned16(ws)) return MQ_ERR_ALIGN;
@@ -242,11 +246,11 @@ int mqconv_backward_data_mx(const mq_conv* cv, mq_mx dyq, mq_mx wq, mq_mx dxq, v
   return hip_status(launch_backward_data_mx(c, view(dyq), view(wq), dx, ws, ws_bytes, (hipStream_t)stream));
 }
 
-int mqconv_backward_weight(const mq_conv* cv, mq_mx dyq, mq_mx xq, float* dw, void* ws, size_t ws_bytes,
-                           void* stream) {
+// Checks of the backward-weight call that need no workspace argument.
+static int check_backward_weight(const mq_conv* cv, const mq_mx& dyq, const mq_mx& xq, const float* dw) {
   if (!cv) return MQ_ERR_NULL;
   if (!conv_ok(cv)) return MQ_ERR_SHAPE;
-  Conv c = to_conv(cv);
+  const Conv c = to_conv(cv);
   int s = check_mx(dyq, MQ_ROLE_GRAD, c.ho(), c.wo(), cv->n, cv->cout);
   if (s != MQ_OK) return s;
   s = check_mx(xq, MQ_ROLE_ACT, cv->h, cv->w, cv->n, cv->cin);
@@ -254,6 +258,15 @@ int mqconv_backward_weight(const mq_conv* cv, mq_mx dyq, mq_mx xq, float* dw, vo
   if (dyq.block_partner != 32 || xq.block_partner != 32) return MQ_ERR_UNSUPPORTED;
   if (!dw) return MQ_ERR_NULL;
   if ((uintptr_t)dw & 3u) return MQ_ERR_ALIGN;
+  if (!gemm_offsets_ok(c, 2, dyq.fmt, xq.fmt, 32)) return MQ_ERR_SHAPE;
+  return MQ_OK;
+}
+
+int mqconv_backward_weight(const mq_conv* cv, mq_mx dyq, mq_mx xq, float* dw, void* ws, size_t ws_bytes,
+                           void* stream) {
+  const int s = check_backward_weight(cv, dyq, xq, dw);
+  if (s != MQ_OK) return s;
+  const Conv c = to_conv(cv);
   const size_t need = gemm_workspace_bytes(c, 2, dyq.fmt, xq.fmt);
   if (need > 0 && (!ws || ws_bytes < need)) return MQ_ERR_WORKSPACE;
   if (ws && !aligned16(ws)) return MQ_ERR_ALIGN;

@@ -79,6 +79,10 @@ inline size_t transposed_bytes(int fmt, long long A, long long P, long long B, l
 }
 
 size_t gemm_workspace_bytes(const Conv& cv, int op, int fa, int fb);
+// whether the 32-bit buffer offsets of a GEMM's operands fit (op 0 forward:
+// fa = X format, bpa = X bp; op 1 backward-data: fa = dY format, bpa = dY bp;
+// op 2 backward-weight: fa = dY format, fb = X format)
+bool gemm_offsets_ok(const Conv& cv, int op, int fa, int fb, int bpa);
 hipError_t launch_forward(const Conv& cv, MxView x, MxView w, float* y, void* ws, size_t ws_bytes,
                           hipStream_t st);
 // forward with Y MX-quantized in the epilogue (bp 1, or bp 32 with N % 32 == 0 or 32 % N == 0)

@@ -64,7 +64,9 @@ def test_workspace_queries():
     for wl in WORKLOADS.values():
         s = wl.shape
         assert mq.mqconv_workspace_bytes(s, mq.OP_FWD, wl.fx, wl.fw) == 0
-        assert mq.mqconv_workspace_bytes(s, mq.OP_DGRAD, wl.fdy, wl.fw) > 0
+        # 8-bit weight codes are read in place; 6/4-bit ones are re-laid first
+        assert mq.mqconv_workspace_bytes(s, mq.OP_DGRAD, wl.fdy, 0) == 0
+        assert mq.mqconv_workspace_bytes(s, mq.OP_DGRAD, wl.fdy, 4) > 0
         assert mq.mqconv_workspace_bytes(s, mq.OP_WGRAD, wl.fdy, wl.fx) > 0
         for op in range(3):
             assert mq.mqconv_naive_workspace_bytes(s, op, wl.fx, wl.fw) > 0
@@ -127,7 +129,8 @@ def test_validation_errors_without_gpu():
     assert _call(mq.mqconv_forward_mx, s24, x24, w24, _mx(mq.ROLE_ACT, (8, 8, 24, 64))) == -6
     # backward-data: needs bp 32 weights and a workspace
     assert _call(mq.mqconv_backward_data, s, dy, _mx(mq.ROLE_WEIGHT, (s.cout, s.kh, s.kw, s.cin), bp=1), FAKE) == -6
-    assert _call(mq.mqconv_backward_data, s, dy, w, FAKE) == -5
+    w4 = _mx(mq.ROLE_WEIGHT, (s.cout, s.kh, s.kw, s.cin), fmt=4)  # 4-bit codes are re-laid in the workspace
+    assert _call(mq.mqconv_backward_data, s, dy, w4, FAKE) == -5
     assert _call(mq.mqconv_backward_data, s, x, w, FAKE) == -3
     # backward-data with MX output
     dxq = _mx(mq.ROLE_GRAD, (s.h, s.w, s.n, s.cin))
@@ -136,7 +139,7 @@ def test_validation_errors_without_gpu():
     assert _call(mq.mqconv_backward_data_mx, s, dy, w, _mx(mq.ROLE_GRAD, (s.h, s.w, s.n, s.cin + 1))) == -2
     assert _call(mq.mqconv_backward_data_mx, s, dy, _mx(mq.ROLE_WEIGHT, (s.cout, s.kh, s.kw, s.cin), bp=1),
                  dxq) == -6
-    assert _call(mq.mqconv_backward_data_mx, s, dy, w, dxq) == -5
+    assert _call(mq.mqconv_backward_data_mx, s, dy, w4, dxq) == -5
     dy24 = _mx(mq.ROLE_GRAD, (8, 8, 24, 64), fmt=1)
     assert _call(mq.mqconv_backward_data_mx, s24, dy24, w24, _mx(mq.ROLE_GRAD, (8, 8, 24, 64))) == -6
     # backward-weight: needs bp 32 on both operands
@@ -206,3 +209,4 @@ def test_binding_checks_tensor_buffers_before_the_call():
     assert "needs" in reason(mq.mqconv_naive_forward, s, torch.zeros(nxe - 1), FAKE, 0, 0, FAKE, None)
     assert "needs" in reason(mq.mqconv_naive_backward_data, s, FAKE, torch.zeros(nwe - 1), 1, 0, FAKE, None)
     assert "needs" in reason(mq.mqconv_naive_backward_weight, s, FAKE, FAKE, 1, 0, torch.zeros(nwe - 1), None)
+
