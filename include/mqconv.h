@@ -21,8 +21,9 @@
  * ---------------------------------------------------------------------------
  * Pointers.   Every tensor pointer is a DEVICE pointer allocated and owned by
  *             the caller. The library never allocates, frees or retains
- *             memory. `mq_conv` descriptors are HOST pointers, read during
- *             the call only.
+ *             memory, apart from the fixed scratch array of
+ *             mqconv_backward_weight_noalloc (see there). `mq_conv`
+ *             descriptors are HOST pointers, read during the call only.
  * Streams.    `stream` is a hipStream_t passed as void*; NULL means the
  *             default stream. Every call only enqueues work and returns.
  * Errors.     The return value is an mq_status. All argument validation
@@ -245,6 +246,23 @@ int mqconv_backward_data_mx(const mq_conv* cv, mq_mx dyq, mq_mx wq, mq_mx dxq, v
  *   dw: fp32 [Cout][Kh][Kw][Cin], fully overwritten. */
 int mqconv_backward_weight(const mq_conv* cv, mq_mx dyq, mq_mx xq, float* dw, void* ws,
                            size_t ws_bytes, void* stream);
+
+/* mqconv_backward_weight for callers that cannot allocate (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation and result, bit for bit, with no workspace argument. Its
+ * scratch space (re-laid codes and split-K partial sums) is a fixed array of
+ * MQ_NOALLOC_SCRATCH_BYTES in device memory that this library holds on every
+ * device it runs on until the process ends; the call itself allocates and
+ * frees nothing.
+ *   Arguments and errors: as mqconv_backward_weight, and MQ_ERR_WORKSPACE
+ *   when the problem needs more scratch than MQ_NOALLOC_SCRATCH_BYTES
+ *   (mqconv_workspace_bytes(cv, 2, dyq.fmt, xq.fmt) tells how much it
+ *   needs); MQ_ERR_HIP if the scratch array's address cannot be taken.
+ *   Every call on one device uses that device's one array: calls that
+ *   overlap in time on one device (two streams, two host threads) race and
+ *   give undefined results; calls ordered on one stream are safe. */
+#define MQ_NOALLOC_SCRATCH_BYTES (128u << 20)
+int mqconv_backward_weight_noalloc(const mq_conv* cv, mq_mx dyq, mq_mx xq, float* dw, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Naive comparison path (kept only to measure bytes moved; §III-C, Table I

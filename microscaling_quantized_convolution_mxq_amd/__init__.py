@@ -72,6 +72,7 @@ def lib() -> ctypes.CDLL:
             "mqconv_backward_data": (I, [CV, mq_mx, mq_mx, P, P, S, P]),
             "mqconv_backward_data_mx": (I, [CV, mq_mx, mq_mx, mq_mx, P, S, P]),
             "mqconv_backward_weight": (I, [CV, mq_mx, mq_mx, P, P, S, P]),
+            "mqconv_backward_weight_noalloc": (I, [CV, mq_mx, mq_mx, P, P]),
             "mqconv_naive_workspace_bytes": (S, [CV, I, I, I]),
             "mqconv_naive_forward": (I, [CV, P, P, I, I, P, P, S, P]),
             "mqconv_naive_backward_data": (I, [CV, P, P, I, I, P, P, S, P]),
@@ -88,7 +89,7 @@ def lib() -> ctypes.CDLL:
 EXPORTED = ("mqconv_abi_version", "mqconv_status_string", "mqconv_codes_bytes", "mqconv_scales_bytes",
             "mqconv_im2col_codes_bytes", "mqconv_im2col_scales_bytes", "mqconv_quantize", "mqconv_quantize_group",
             "mqconv_cbf_im2col", "mqconv_workspace_bytes", "mqconv_forward", "mqconv_forward_mx", "mqconv_backward_data",
-            "mqconv_backward_data_mx", "mqconv_backward_weight",
+            "mqconv_backward_data_mx", "mqconv_backward_weight", "mqconv_backward_weight_noalloc",
             "mqconv_naive_workspace_bytes", "mqconv_naive_forward",
             "mqconv_naive_backward_data", "mqconv_naive_backward_weight")
 
@@ -297,6 +298,18 @@ def mqconv_backward_weight(shape, dyq: MxTensor, xq: MxTensor, dw, ws=None, stre
     p, n = _ws(ws)
     _check(lib().mqconv_backward_weight(ctypes.byref(_conv(shape)), dyq.c_struct("dyq"), xq.c_struct("xq"),
                                         _f32(dw, _nw(shape), "dw"), p, n, _stream(stream)), "mqconv_backward_weight")
+
+
+# scratch bytes the library holds per device for mqconv_backward_weight_noalloc
+NOALLOC_SCRATCH_BYTES = 128 << 20
+
+
+def mqconv_backward_weight_noalloc(shape, dyq: MxTensor, xq: MxTensor, dw, stream=None) -> None:
+    """mqconv_backward_weight with the library's own per-device scratch array
+    instead of a workspace (no allocation anywhere in the call)."""
+    _check(lib().mqconv_backward_weight_noalloc(ctypes.byref(_conv(shape)), dyq.c_struct("dyq"), xq.c_struct("xq"),
+                                                _f32(dw, _nw(shape), "dw"), _stream(stream)),
+           "mqconv_backward_weight_noalloc")
 
 
 def mqconv_naive_workspace_bytes(shape, op: int, fa: int, fb: int) -> int:

@@ -6,6 +6,8 @@
 
 #include <limits.h>
 
+#include <mutex>
+
 using namespace mq;
 
 namespace {
@@ -74,6 +76,34 @@ MxView view(const mq_mx& t) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MQ_OK : MQ_ERR_HIP; }
 
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Backward-weight without any allocation: the scratch space (re-laid codes,
+// split-K partial sums) is a fixed array of this library's code object in
+// device memory. Every device the library runs on holds its own copy, at its
+// own address, until the process ends; host code reaches it only through
+// that per-device address, taken once per device with that device current.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[MQ_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // per-device address of `scratch` (nullptr: not taken yet)
+
+// Address of the current device's copy of `scratch` (nullptr on failure).
+void* scratch_for_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
 }  // namespace
 
 extern "C" {
@@ -271,6 +301,18 @@ int mqconv_backward_weight(const mq_conv* cv, mq_mx dyq, mq_mx xq, float* dw, vo
   if (need > 0 && (!ws || ws_bytes < need)) return MQ_ERR_WORKSPACE;
   if (ws && !aligned16(ws)) return MQ_ERR_ALIGN;
   return hip_status(launch_backward_weight(c, view(dyq), view(xq), dw, ws, ws_bytes, (hipStream_t)stream));
+}
+
+int mqconv_backward_weight_noalloc(const mq_conv* cv, mq_mx dyq, mq_mx xq, float* dw, void* stream) {
+  const int s = check_backward_weight(cv, dyq, xq, dw);
+  if (s != MQ_OK) return s;
+  const Conv c = to_conv(cv);
+  const size_t need = gemm_workspace_bytes(c, 2, dyq.fmt, xq.fmt);
+  if (need > (size_t)MQ_NOALLOC_SCRATCH_BYTES) return MQ_ERR_WORKSPACE;
+  void* ws = need > 0 ? scratch_for_current_device() : nullptr;
+  if (need > 0 && !ws) return MQ_ERR_HIP;
+  return hip_status(launch_backward_weight(c, view(dyq), view(xq), dw, ws, MQ_NOALLOC_SCRATCH_BYTES,
+                                           (hipStream_t)stream));
 }
 
 size_t mqconv_naive_workspace_bytes(const mq_conv* cv, int op, mq_elem fa, mq_elem fb) {

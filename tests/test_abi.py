@@ -26,7 +26,7 @@ def _declared():
 
 def test_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 19
+    assert len(names) == 20
     out = subprocess.run(["nm", "-D", "--defined-only", mq.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT\s+(mqconv_\w+)", out))
     assert set(names) <= exported
@@ -210,3 +210,24 @@ def test_binding_checks_tensor_buffers_before_the_call():
     assert "needs" in reason(mq.mqconv_naive_backward_data, s, FAKE, torch.zeros(nwe - 1), 1, 0, FAKE, None)
     assert "needs" in reason(mq.mqconv_naive_backward_weight, s, FAKE, FAKE, 1, 0, torch.zeros(nwe - 1), None)
 
+
+def test_noalloc_validation_without_gpu():
+    """The no-allocation backward-weight call checks its arguments like
+    mqconv_backward_weight and rejects a problem whose scratch need exceeds
+    the fixed array (MQ_ERR_WORKSPACE) before any HIP call."""
+    s = WORKLOADS["c5"].shape
+    x = _mx(mq.ROLE_ACT, (s.h, s.w, s.n, s.cin), fmt=3)
+    dy = _mx(mq.ROLE_GRAD, (s.ho, s.wo, s.n, s.cout), fmt=1)
+    assert _call(mq.mqconv_backward_weight_noalloc, s, dy, x, 0) == -1
+    assert _call(mq.mqconv_backward_weight_noalloc, s, dy, _mx(mq.ROLE_ACT, (s.h, s.w, s.n, s.cin), bp=1), FAKE) == -6
+    assert _call(mq.mqconv_backward_weight_noalloc, s, x, x, FAKE) == -3
+    big = ConvShape(64, 128, 160, 160, 256, 3, 3, 2, 1)
+    assert mq.mqconv_workspace_bytes(big, 2, 1, 3) > mq.NOALLOC_SCRATCH_BYTES
+    xb = _mx(mq.ROLE_ACT, (big.h, big.w, big.n, big.cin), fmt=3)
+    dyb = _mx(mq.ROLE_GRAD, (big.ho, big.wo, big.n, big.cout), fmt=1)
+    assert _call(mq.mqconv_backward_weight_noalloc, big, dyb, xb, FAKE) == -5
+
+
+def test_noalloc_scratch_size_matches_header():
+    m = re.search(r"#define MQ_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == mq.NOALLOC_SCRATCH_BYTES
