@@ -8,6 +8,8 @@ order. Source: "MicroQonv: Reshaping Convolution Tensors for Efficient
 Microscaling in Training and Inference":
   quantize ........ §II-D, §III-A (E8M0 power-of-two block scale), §IV-B
                     (square blocks along both GEMM directions)
+  quantize_sr ..... §III-A (stochastic rounding of the gradient), with the
+                    Philox4x32-10 counter-based generator
   cbf_im2col ...... §IV-A, Fig. 3
   conv_* .......... §II-A Eqs. (1)-(3)
   naive_* ......... §II-C (classic im2col, kernel flattening, the three GEMMs
@@ -61,6 +63,10 @@ def lib():
             "mqref_encode": (I, [I, D]),
             "mqref_encode_array": (None, [I, P, LL, P]),
             "mqref_quantize_view": (LL, [I, I, P, LL, LL, LL, LL, P, P]),
+            "mqref_philox4x32_10": (None, [P, P, P]),
+            "mqref_sr_word": (ctypes.c_uint32, [ctypes.c_uint64, LL, LL]),
+            "mqref_encode_sr": (I, [I, D, ctypes.c_uint32]),
+            "mqref_quantize_view_sr": (LL, [I, I, P, LL, LL, LL, LL, ctypes.c_uint64, P, P]),
             "mqref_dequant_view": (None, [I, I, P, P, LL, LL, LL, LL, P]),
             "mqref_row_bytes": (LL, [I, LL]),
             "mqref_pack_rows": (None, [I, P, LL, LL, P]),
@@ -146,6 +152,34 @@ def quantize_view(fmt: int, bp: int, src: np.ndarray, A: int, P: int, B: int, C:
     return codes, scales.reshape(A, B, -(-P // bp), -(-C // 32)), int(n)
 
 
+def philox4x32_10(ctr, key):
+    """Philox4x32-10 (Salmon et al., SC'11) of a 4-word counter and 2-word key."""
+    c = np.ascontiguousarray(np.asarray(ctr, np.uint32))
+    k = np.ascontiguousarray(np.asarray(key, np.uint32))
+    out = np.empty(4, np.uint32)
+    lib().mqref_philox4x32_10(_p(c), _p(k), _p(out))
+    return out
+
+
+def sr_word(seed: int, row: int, c: int) -> int:
+    return int(lib().mqref_sr_word(seed, row, c))
+
+
+def encode_sr(fmt: int, v: float, r: int) -> int:
+    """Code of an already-scaled value rounded stochastically with random word r."""
+    return lib().mqref_encode_sr(fmt, float(v), int(r))
+
+
+def quantize_view_sr(fmt: int, bp: int, src: np.ndarray, A: int, P: int, B: int, C: int, seed: int):
+    """quantize_view with stochastic rounding of the elements (§III-A)."""
+    src = np.ascontiguousarray(src, dtype=np.float32).reshape(-1)
+    assert src.size == A * P * B * C
+    codes = np.empty(src.size, np.uint8)
+    scales = np.empty(A * B * (-(-P // bp)) * (-(-C // 32)), np.uint8)
+    n = lib().mqref_quantize_view_sr(fmt, bp, _p(src), A, P, B, C, seed, _p(codes), _p(scales))
+    return codes, scales.reshape(A, B, -(-P // bp), -(-C // 32)), int(n)
+
+
 def dequant_view(fmt: int, bp: int, codes: np.ndarray, scales: np.ndarray, A, P, B, C):
     codes = np.ascontiguousarray(codes, dtype=np.uint8).reshape(-1)
     scales = np.ascontiguousarray(scales, dtype=np.uint8).reshape(-1)
@@ -167,6 +201,20 @@ def quantize(role: int, fmt: int, bp: int, x: np.ndarray):
     dims = x.shape
     A, P, B, C = _role_view(role, dims)
     codes, scales, n = quantize_view(fmt, bp, x, A, P, B, C)
+    if role in (ROLE_ACT, ROLE_GRAD):
+        scales = scales.reshape(dims[0], dims[1], -(-dims[2] // bp), -(-dims[3] // 32))
+    else:
+        scales = scales.reshape(dims[1], dims[2], -(-dims[0] // bp), -(-dims[3] // 32))
+    return codes.reshape(dims), scales, n
+
+
+def quantize_sr(role: int, fmt: int, bp: int, x: np.ndarray, seed: int):
+    """quantize() with stochastic rounding of the elements (the gradient's
+    rounding in §III-A); the random word of an element is that of its memory
+    row and channel (mqref.c, mqref_sr_word)."""
+    dims = x.shape
+    A, P, B, C = _role_view(role, dims)
+    codes, scales, n = quantize_view_sr(fmt, bp, x, A, P, B, C, seed)
     if role in (ROLE_ACT, ROLE_GRAD):
         scales = scales.reshape(dims[0], dims[1], -(-dims[2] // bp), -(-dims[3] // 32))
     else:

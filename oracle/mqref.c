@@ -189,6 +189,122 @@ long long mqref_quantize_view(int f, int bp, const float* src, long long A, long
   return count;
 }
 
+/* ------------------------------------------------------------------------
+ * Stochastic rounding of the gradient (§III-A: activations and weights round
+ * to nearest, "stochastic rounding is performed on the gradient").
+ * A scaled value between two neighbouring points lo < hi of the element grid
+ * rounds up with probability (v - lo) / (hi - lo): with the random word r
+ * (uniform 32-bit) and T = floor(2^32 (v - lo) / (hi - lo)), it takes hi when
+ * r < T, else lo; points of the grid stay; results above the largest normal
+ * saturate to it, as with round-to-nearest. The block scale follows the same
+ * rule as round-to-nearest (the scale is not rounded stochastically).
+ * ------------------------------------------------------------------------ */
+
+/* Philox4x32-10, the counter-based generator of Salmon, Moraes, Dror and
+ * Shaw ("Parallel random numbers: as easy as 1, 2, 3", SC'11): ten rounds of
+ * two 32x32->64-bit multiplications with the published multipliers and key
+ * increments, the first round with the original key. */
+void mqref_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+  uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3], k0 = key[0], k1 = key[1];
+  for (int r = 0; r < 10; r++) {
+    if (r > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0, p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0, n1 = (uint32_t)p1;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1, n3 = (uint32_t)p0;
+    c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+  }
+  out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/* The random word of element (memory row `row`, channel c) of a tensor
+ * quantized with `seed`: word c mod 4 of Philox4x32-10 at counter
+ * (row, floor(c / 4), 0, 0) with key (low, high 32 bits of seed). */
+uint32_t mqref_sr_word(uint64_t seed, long long row, long long c) {
+  const uint32_t ctr[4] = {(uint32_t)row, (uint32_t)(c >> 2), 0u, 0u};
+  const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+  uint32_t out[4];
+  mqref_philox4x32_10(ctr, key, out);
+  return out[c & 3];
+}
+
+/* Code of an already-scaled finite value, rounded stochastically with the
+ * random word r. */
+int mqref_encode_sr(int f, double v, uint32_t r) {
+  const mqref_fmt* F = &FMT[f];
+  const int emin = 1 - F->bias;
+  const double a = fabs(v);
+  double res = 0.0;
+  if (a != 0.0) {
+    int k;
+    frexp(a, &k);
+    int ex = k - 1;            /* floor(log2 a) */
+    if (ex < emin) ex = emin;  /* subnormals share the spacing of the first binade */
+    const double q = ldexp(1.0, ex - F->mbits); /* grid spacing around a */
+    const double t = a / q, lo = floor(t);
+    const double T = floor((t - lo) * 4294967296.0);
+    res = ((double)r < T ? lo + 1.0 : lo) * q;
+    if (res > F->maxnorm) res = F->maxnorm;
+  }
+  return mqref_encode(f, signbit(v) ? -res : res); /* res is a grid point: encoded exactly */
+}
+
+/* mqref_quantize_view with stochastic rounding of the elements; element
+ * (a, p, b, c) lies on memory row (a*P + p)*B + b, which with c picks its
+ * random word (mqref_sr_word). */
+long long mqref_quantize_view_sr(int f, int bp, const float* src, long long A, long long P, long long B,
+                                 long long C, uint64_t seed, uint8_t* codes, uint8_t* scales) {
+  const long long nPB = (P + bp - 1) / bp, nCB = (C + 31) / 32;
+  const int emax = mqref_elem_emax(f);
+  long long count = 0;
+#pragma omp parallel for collapse(2) reduction(+ : count) schedule(static)
+  for (long long a = 0; a < A; a++)
+    for (long long b = 0; b < B; b++)
+      for (long long pb = 0; pb < nPB; pb++)
+        for (long long cb = 0; cb < nCB; cb++) {
+          long long p0 = pb * bp, p1 = p0 + bp < P ? p0 + bp : P;
+          long long c0 = cb * 32, c1 = c0 + 32 < C ? c0 + 32 : C;
+          double amax = 0.0;
+          int nonfinite = 0;
+          for (long long p = p0; p < p1; p++)
+            for (long long c = c0; c < c1; c++) {
+              double x = src[((a * P + p) * B + b) * C + c];
+              if (!isfinite(x)) nonfinite = 1;
+              else if (fabs(x) > amax) amax = fabs(x);
+            }
+          int S;
+          if (nonfinite) {
+            S = 255;
+          } else {
+            int e;
+            if (amax == 0.0) {
+              e = -127;
+            } else {
+              int k;
+              frexp(amax, &k);
+              e = (k - 1) - emax;
+              if (e < -127) e = -127;
+              if (e > 127) e = 127;
+            }
+            S = e + 127;
+          }
+          scales[((a * B + b) * nPB + pb) * nCB + cb] = (uint8_t)S;
+          for (long long p = p0; p < p1; p++)
+            for (long long c = c0; c < c1; c++) {
+              const long long row = (a * P + p) * B + b, i = row * C + c;
+              if (S == 255)
+                codes[i] = 0;
+              else
+                codes[i] = (uint8_t)mqref_encode_sr(f, ldexp((double)src[i], 127 - S),
+                                                    mqref_sr_word(seed, row, c));
+            }
+          count += (p1 - p0) * (c1 - c0);
+        }
+  return count;
+}
+
 /* Dequantize (fake quantization): code value times 2^(S-127). Same view. */
 void mqref_dequant_view(int f, int bp, const uint8_t* codes, const uint8_t* scales, long long A,
                         long long P, long long B, long long C, double* out) {
