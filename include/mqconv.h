@@ -172,6 +172,21 @@ size_t mqconv_im2col_scales_bytes(const mq_conv* cv, int32_t bp);
  *      are fully overwritten (padding codes included). */
 int mqconv_quantize(const float* src, mq_mx dst, void* stream);
 
+/* mqconv_quantize with the elements rounded stochastically instead of to
+ * nearest: §III-A rounds activations and weights to nearest and the
+ * gradient stochastically. The block scale byte is the round-to-nearest
+ * one; each scaled element x * 2^-e between neighbouring grid points
+ * lo < hi becomes hi when its random word r satisfies
+ * r < floor(2^32 * (x * 2^-e - lo) / (hi - lo)), else lo (grid points stay,
+ * results above max normal saturate to it). The random word of the element
+ * on memory row `row` (the element index divided by C in the role's fp32
+ * order) and channel c is word (c mod 4) of Philox4x32-10 (Salmon et al.,
+ * "Parallel random numbers: as easy as 1, 2, 3", SC'11) at counter
+ * (row, c / 4, 0, 0) with key (seed & 0xffffffff, seed >> 32); equal
+ * (src, seed) give equal codes. Arguments, layouts and errors: as
+ * mqconv_quantize. */
+int mqconv_quantize_sr(const float* src, mq_mx dst, uint64_t seed, void* stream);
+
 /* mqconv_quantize of several tensors at once, e.g. a layer's activation and
  * weight before its forward pass (each still quantized once, §III-A, §IV-B):
  * src[i] -> dst[i] for i < count, every pair exactly as mqconv_quantize

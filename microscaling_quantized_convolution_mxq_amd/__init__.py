@@ -65,6 +65,7 @@ def lib() -> ctypes.CDLL:
             "mqconv_im2col_scales_bytes": (S, [CV, I32]),
             "mqconv_quantize": (I, [P, mq_mx, P]),
             "mqconv_quantize_group": (I, [I32, P, ctypes.POINTER(mq_mx), P]),
+            "mqconv_quantize_sr": (I, [P, mq_mx, ctypes.c_uint64, P]),
             "mqconv_cbf_im2col": (I, [CV, mq_mx, P, P, P]),
             "mqconv_workspace_bytes": (S, [CV, I, I, I]),
             "mqconv_forward": (I, [CV, mq_mx, mq_mx, P, P, S, P]),
@@ -88,6 +89,7 @@ def lib() -> ctypes.CDLL:
 
 EXPORTED = ("mqconv_abi_version", "mqconv_status_string", "mqconv_codes_bytes", "mqconv_scales_bytes",
             "mqconv_im2col_codes_bytes", "mqconv_im2col_scales_bytes", "mqconv_quantize", "mqconv_quantize_group",
+            "mqconv_quantize_sr",
             "mqconv_cbf_im2col", "mqconv_workspace_bytes", "mqconv_forward", "mqconv_forward_mx", "mqconv_backward_data",
             "mqconv_backward_data_mx", "mqconv_backward_weight", "mqconv_backward_weight_noalloc",
             "mqconv_naive_workspace_bytes", "mqconv_naive_forward",
@@ -236,6 +238,12 @@ def _prod(d):
 def mqconv_quantize(src, dst: MxTensor, stream=None) -> None:
     _check(lib().mqconv_quantize(_f32(src, _prod(dst.dims), "src"), dst.c_struct("dst"), _stream(stream)),
            "mqconv_quantize")
+
+
+def mqconv_quantize_sr(src, dst: MxTensor, seed: int, stream=None) -> None:
+    """mqconv_quantize with stochastically rounded elements (random words from seed)."""
+    _check(lib().mqconv_quantize_sr(_f32(src, _prod(dst.dims), "src"), dst.c_struct("dst"), int(seed) & (2**64 - 1),
+                                    _stream(stream)), "mqconv_quantize_sr")
 
 
 QUANTIZE_GROUP_MAX = 8

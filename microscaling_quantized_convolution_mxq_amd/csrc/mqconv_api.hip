@@ -174,6 +174,14 @@ int mqconv_quantize(const float* src, mq_mx dst, void* stream) {
   return hip_status(launch_quantize(r.src, r.codes, r.scales, r.fmt, r.bp, r.A, r.P, r.B, r.C, (hipStream_t)stream));
 }
 
+int mqconv_quantize_sr(const float* src, mq_mx dst, uint64_t seed, void* stream) {
+  QReq r;
+  const int e = quantize_req(src, dst, &r);
+  if (e != MQ_OK) return e;
+  return hip_status(launch_quantize_sr(r.src, r.codes, r.scales, r.fmt, r.bp, r.A, r.P, r.B, r.C, seed,
+                                       (hipStream_t)stream));
+}
+
 int mqconv_quantize_group(int32_t count, const float* const* src, const mq_mx* dst, void* stream) {
   if (!src || !dst) return MQ_ERR_NULL;
   if (count < 1 || count > MQ_QUANTIZE_GROUP_MAX) return MQ_ERR_SHAPE;

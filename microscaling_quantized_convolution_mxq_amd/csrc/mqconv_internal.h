@@ -55,6 +55,9 @@ inline long long row_bytes(int fmt, long long C) { return ((C + 31) / 32) * run_
 
 hipError_t launch_quantize(const float* src, uint8_t* codes, uint8_t* scales, int fmt, int bp, int A,
                            int P, int B, int C, hipStream_t st);
+// the same with the elements rounded stochastically (random words from seed)
+hipError_t launch_quantize_sr(const float* src, uint8_t* codes, uint8_t* scales, int fmt, int bp, int A,
+                              int P, int B, int C, uint64_t seed, hipStream_t st);
 // one tensor of a grouped quantization: [A][P][B] x C view as launch_quantize
 struct QReq {
   const float* src;

@@ -36,13 +36,74 @@ namespace mq {
 // A workgroup quantizes 4 tiles (one per wave), tiles 4 wg .. 4 wg + 3, and
 // of those the channel blocks cb0, cb0 + cbs, ...; `stage` is the wave's
 // packing buffer (ST).
+// ---------------------------------------------------------------------------
+// Stochastic rounding (§III-A: the gradient is rounded stochastically). A
+// scaled value between grid points lo < hi becomes hi when its random word r
+// is below floor(2^32 (v - lo) / (hi - lo)), else lo; grid points stay, and
+// results above the largest normal saturate. Element (memory row, channel c)
+// takes word c mod 4 of Philox4x32-10 at counter (row, c / 4, 0, 0) with the
+// seed's two halves as key (the generator of Salmon et al., SC'11: ten rounds
+// of two 32 x 32 -> 64-bit products and key increments).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                              uint32_t k1, uint32_t (&o)[4]) {
+#pragma unroll
+  for (int r = 0; r < 10; r++) {
+    if (r > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint32_t hi0 = __umulhi(0xD2511F53u, c0), lo0 = 0xD2511F53u * c0;
+    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c2), lo1 = 0xCD9E8D57u * c2;
+    c0 = hi1 ^ c1 ^ k0;
+    c1 = lo1;
+    c2 = hi0 ^ c3 ^ k1;
+    c3 = lo0;
+  }
+  o[0] = c0; o[1] = c1; o[2] = c2; o[3] = c3;
+}
+
+// The 16 values x of half a block run (channels c0 .. c0 + 15 of memory row
+// `row`, c0 a multiple of 16), divided by the block scale 2^(S - 127) and
+// rounded stochastically onto the element grid; the results are grid points
+// (or +-max), which the round-to-nearest conversions then encode exactly. A
+// block holding a NaN or an infinity (S = 0xFF) gets all-zero codes.
+template <int F>
+__device__ __forceinline__ void sr_scale16(const float (&x)[16], uint32_t S, uint32_t row, int c0, uint32_t k0,
+                                           uint32_t k1, float (&v)[16]) {
+  using T = Fmt<F>;
+  const float inv = inv_scale_from_byte(S == 255u ? 127u : S);
+  uint32_t rw[16];
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    uint32_t o[4];
+    philox4x32_10(row, (uint32_t)(c0 >> 2) + q, 0u, 0u, k0, k1, o);
+#pragma unroll
+    for (int i = 0; i < 4; i++) rw[4 * q + i] = o[i];
+  }
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    const float t = x[i] * inv;
+    const float a = fabsf(t);
+    // grid spacing 2^e around a: e = max(floor(log2 a), emin) - M
+    const int E = (int)(__float_as_uint(a) >> 23) - 127;
+    const int e = max(E, T::emin) - T::M;
+    const float u = a * __uint_as_float((uint32_t)(127 - e) << 23);  // a / 2^e, exact
+    const float fl = floorf(u);
+    const uint32_t thr = (uint32_t)floorf((u - fl) * 4294967296.0f);
+    float r = (fl + (rw[i] < thr ? 1.0f : 0.0f)) * __uint_as_float((uint32_t)(127 + e) << 23);
+    r = fminf(r, T::maxv);
+    v[i] = S == 255u ? 0.0f : copysignf(r, t);
+  }
+}
+
 constexpr int kStageCB = 8;
 constexpr int kStageBytes = 32 * kStageCB * 32;
-template <int F, int MODE, bool ST>
+template <int F, int MODE, bool ST, bool SR = false>
 __device__ __forceinline__ void quantize_tiles(const float* __restrict__ src, uint8_t* __restrict__ codes,
                                                uint8_t* __restrict__ scales, int A, int P, int B, int C,
                                                int bp, long long ntiles, long long wg, int cb0, int cbs,
-                                               uint8_t* stage) {
+                                               uint8_t* stage, uint32_t k0 = 0, uint32_t k1 = 0) {
   const int lane = threadIdx.x & 63;
   const long long tile = wg * 4 + (threadIdx.x >> 6);
   if (tile >= ntiles) return;
@@ -111,7 +172,8 @@ __device__ __forceinline__ void quantize_tiles(const float* __restrict__ src, ui
     }
     const uint32_t S = scale_byte_from_amax<F>(m);
     float v[16];
-    scale_clamp16<F>(x, S, v);
+    if constexpr (SR) sr_scale16<F>(x, S, (uint32_t)row, c0, k0, k1, v);
+    else scale_clamp16<F>(x, S, v);
     if constexpr (ST) {
       convert_store_half_run<F>(&stage[r * row_bytes + cb * RB + half * (RB / 2)], v);
       if (row_ok && writes_scale) scales[sidx + cb] = (uint8_t)S;
@@ -133,14 +195,15 @@ __device__ __forceinline__ void quantize_tiles(const float* __restrict__ src, ui
   }
 }
 
-template <int F, int MODE, bool ST>
+template <int F, int MODE, bool ST, bool SR>
 __global__ __launch_bounds__(256) void mxq_quantize_kernel(const float* __restrict__ src,
                                                           uint8_t* __restrict__ codes,
                                                           uint8_t* __restrict__ scales, int A, int P,
-                                                          int B, int C, int bp, long long ntiles) {
+                                                          int B, int C, int bp, long long ntiles, uint32_t k0,
+                                                          uint32_t k1) {
   __shared__ __attribute__((aligned(16))) uint8_t stage_buf[ST ? 4 : 1][ST ? kStageBytes : 16];
-  quantize_tiles<F, MODE, ST>(src, codes, scales, A, P, B, C, bp, ntiles, blockIdx.x, blockIdx.y, gridDim.y,
-                              stage_buf[ST ? threadIdx.x >> 6 : 0]);
+  quantize_tiles<F, MODE, ST, SR>(src, codes, scales, A, P, B, C, bp, ntiles, blockIdx.x, blockIdx.y, gridDim.y,
+                                  stage_buf[ST ? threadIdx.x >> 6 : 0], k0, k1);
 }
 
 // Several tensors of one element format in one launch (a small tensor, such
@@ -202,36 +265,46 @@ static QPlan quantize_plan(int A, int P, int B, int C, int bp) {
   return q;
 }
 
-template <int F, int MODE, bool ST>
-static void launch_one(const QReq& r, const QPlan& q, hipStream_t st) {
-  hipLaunchKernelGGL((mxq_quantize_kernel<F, MODE, ST>), dim3((unsigned)q.blocks, (unsigned)q.gy), dim3(256), 0,
-                     st, r.src, r.codes, r.scales, r.A, r.P, r.B, r.C, r.bp, q.ntiles);
+template <int F, int MODE, bool ST, bool SR>
+static void launch_one(const QReq& r, const QPlan& q, uint64_t seed, hipStream_t st) {
+  hipLaunchKernelGGL((mxq_quantize_kernel<F, MODE, ST, SR>), dim3((unsigned)q.blocks, (unsigned)q.gy), dim3(256), 0,
+                     st, r.src, r.codes, r.scales, r.A, r.P, r.B, r.C, r.bp, q.ntiles, (uint32_t)seed,
+                     (uint32_t)(seed >> 32));
 }
 
-template <int F>
-static hipError_t launch_f(const QReq& r, hipStream_t st) {
+template <int F, bool SR>
+static hipError_t launch_f(const QReq& r, uint64_t seed, hipStream_t st) {
   const QPlan q = quantize_plan(r.A, r.P, r.B, r.C, r.bp);
   switch (2 * q.mode + q.st) {
-    case 0: launch_one<F, 0, false>(r, q, st); break;
-    case 1: launch_one<F, 0, true>(r, q, st); break;
-    case 2: launch_one<F, 1, false>(r, q, st); break;
-    case 3: launch_one<F, 1, true>(r, q, st); break;
-    case 4: launch_one<F, 2, false>(r, q, st); break;
-    default: launch_one<F, 2, true>(r, q, st); break;
+    case 0: launch_one<F, 0, false, SR>(r, q, seed, st); break;
+    case 1: launch_one<F, 0, true, SR>(r, q, seed, st); break;
+    case 2: launch_one<F, 1, false, SR>(r, q, seed, st); break;
+    case 3: launch_one<F, 1, true, SR>(r, q, seed, st); break;
+    case 4: launch_one<F, 2, false, SR>(r, q, seed, st); break;
+    default: launch_one<F, 2, true, SR>(r, q, seed, st); break;
   }
   return hipGetLastError();
 }
 
+template <bool SR>
+static hipError_t launch_fmt(const QReq& r, uint64_t seed, hipStream_t st) {
+  switch (r.fmt) {
+    case 0: return launch_f<0, SR>(r, seed, st);
+    case 1: return launch_f<1, SR>(r, seed, st);
+    case 2: return launch_f<2, SR>(r, seed, st);
+    case 3: return launch_f<3, SR>(r, seed, st);
+    default: return launch_f<4, SR>(r, seed, st);
+  }
+}
+
 hipError_t launch_quantize(const float* src, uint8_t* codes, uint8_t* scales, int fmt, int bp, int A,
                            int P, int B, int C, hipStream_t st) {
-  const QReq r{src, codes, scales, fmt, bp, A, P, B, C};
-  switch (fmt) {
-    case 0: return launch_f<0>(r, st);
-    case 1: return launch_f<1>(r, st);
-    case 2: return launch_f<2>(r, st);
-    case 3: return launch_f<3>(r, st);
-    default: return launch_f<4>(r, st);
-  }
+  return launch_fmt<false>(QReq{src, codes, scales, fmt, bp, A, P, B, C}, 0, st);
+}
+
+hipError_t launch_quantize_sr(const float* src, uint8_t* codes, uint8_t* scales, int fmt, int bp, int A,
+                              int P, int B, int C, uint64_t seed, hipStream_t st) {
+  return launch_fmt<true>(QReq{src, codes, scales, fmt, bp, A, P, B, C}, seed, st);
 }
 
 // One grouped launch per element format present (and per kQGroupMax

@@ -11,6 +11,10 @@ Modes:
   summarize-call
              read the counter CSVs of a call run and write the HBM bytes of
              one call of that entry point (profiles/traffic_<workload>_<call>.json)
+  mfma       read the counter CSV of a step run with the matrix-core counters
+             and write, per GEMM kernel, the fraction of SIMD cycles the MFMA
+             unit was busy and the matrix operations it executed
+             (profiles/mfma_<workload>.txt)
 
 Counter passes (one counter group per run, as rocprofv3 requires), e.g. for
 the 3x3 YOLOv8n-style layer:
@@ -223,6 +227,55 @@ def summarize_call(d: str, workload: str, call: str, out_dir: str, command: str)
     return rec
 
 
+MFMA_COUNTERS = ("GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_F8",
+                 "SQ_INSTS_VALU_MFMA_MOPS_F6F4")
+N_XCC, N_SIMD = 8, 1024  # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
+
+
+def summarize_mfma(d: str, stem: str, workload: str, out_dir: str, command: str) -> str:
+    """Per GEMM dispatch of a step run (one counter pass with MFMA_COUNTERS):
+      MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES (summed over all SIMDs) divided by
+                  the kernel's cycles (GRBM_GUI_ACTIVE summed over the 8 XCDs,
+                  / 8) times the 1024 SIMDs;
+      executed  = (MOPS_F8 + MOPS_F6F4) x 512 matrix operations (adds and
+                  multiplies, zero padding of short K-blocks included), against
+                  the GEMM's algorithmic 2 N Ho Wo Cout Cin Kh Kw."""
+    files = glob.glob(os.path.join(d, "**", f"{stem}_counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no {stem}_counter_collection.csv under {d}")
+    per = {}
+    for r in csv.DictReader(open(files[0])):
+        key = (r.get("Dispatch_Id") or r.get("Correlation_Id"), r["Kernel_Name"])
+        per.setdefault(key, {})[r["Counter_Name"]] = per.get(key, {}).get(r["Counter_Name"], 0.0) + float(
+            r["Counter_Value"])
+    wls = _workloads(workload)
+    flops = sum(wl.shape.flops() for wl in wls)
+    lines = [f"MFMA counters of one training step, workload {workload} ({len(wls)} layer(s)); "
+             f"algorithmic FLOP per GEMM kind {flops / 1e9:.2f} G", "", "Command (run from the repository root on one MI355X):",
+             "  " + command, "",
+             f"{'kernel':74s} {'calls':>5s} {'cycles':>9s} {'MFMA busy':>9s} {'exec GFLOP':>10s}"]
+    agg = {}
+    for (_, name), c in per.items():
+        if "mx_gemm_kernel" not in name:
+            continue
+        k = name.split("(")[0].replace("void ", "")
+        a = agg.setdefault(k, [0, 0.0, 0.0, 0.0])
+        a[0] += 1
+        a[1] += c.get("GRBM_GUI_ACTIVE", 0.0) / N_XCC
+        a[2] += c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+        a[3] += (c.get("SQ_INSTS_VALU_MFMA_MOPS_F8", 0.0) + c.get("SQ_INSTS_VALU_MFMA_MOPS_F6F4", 0.0)) * 512
+    for k, (n, cyc, busy, ops) in sorted(agg.items(), key=lambda kv: -kv[1][1]):
+        frac = busy / (cyc * N_SIMD) if cyc else 0.0
+        lines.append(f"{k[:74]:74s} {n:5d} {cyc / n:9.0f} {frac:9.3f} {ops / n / 1e9:10.2f}")
+    text = "\n".join(lines) + "\n"
+    os.makedirs(out_dir, exist_ok=True)
+    wl_name = wls[0].name if len(wls) == 1 else "c3_yolov8n_backbone_27convs_n16"
+    with open(os.path.join(out_dir, f"mfma_{wl_name}.txt"), "w") as fh:
+        fh.write(text)
+    print(text)
+    return text
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="mode", required=True)
@@ -239,6 +292,12 @@ def main(argv=None):
     e.add_argument("--call", choices=CALL_NAMES, default="backward_weight")
     e.add_argument("--out", default=os.path.join(ROOT, "profiles"))
     e.add_argument("--command", default="")
+    f = sub.add_parser("mfma")
+    f.add_argument("--dir", required=True)
+    f.add_argument("--stem", default="mfma")
+    f.add_argument("--workload", default="c2")
+    f.add_argument("--out", default=os.path.join(ROOT, "profiles"))
+    f.add_argument("--command", default="")
     c = sub.add_parser("summarize")
     c.add_argument("--dir", required=True)
     c.add_argument("--workload", default="c2")
@@ -250,6 +309,8 @@ def main(argv=None):
         run_call(args.workload, args.call)
     elif args.mode == "copy":
         run_copy()
+    elif args.mode == "mfma":
+        summarize_mfma(args.dir, args.stem, args.workload, args.out, args.command)
     elif args.mode == "summarize-call":
         summarize_call(args.dir, args.workload, args.call, args.out, args.command)
     else:
