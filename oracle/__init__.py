@@ -15,6 +15,11 @@ Microscaling in Training and Inference":
   naive_* ......... §II-C (classic im2col, kernel flattening, the three GEMMs
                     G_W = G_Y . X'^T, G_X' = W^T . G_Y) and §III-C (quantize
                     the im2col-expanded tensor along each GEMM direction)
+  cuyckens_* ...... §III-C (the square-block method of [25] extended to
+                    convolution: the im2col-expanded X' quantized once in
+                    square blocks and saved for the backward pass)
+  activation_mse .. §IV-D, Table II (per-element quantization error of the
+                    activation under each method)
 """
 from __future__ import annotations
 
@@ -451,3 +456,88 @@ def naive_wgrad(shape, dy, x, fdy, fx):
     dwf = gtq @ xtq.T  # [co][k], k = (ci, kh, kw)
     dw = dwf.reshape(shape.cout, shape.cin, shape.kh, shape.kw)
     return np.ascontiguousarray(np.transpose(dw, (0, 2, 3, 1))), {"G": n1, "A": n2}
+
+
+# --------------------------------------------------------------------------
+# Square-block comparator (§III-C): the method of [25], written for fully
+# connected layers, extended to convolution by quantizing the im2col-expanded
+# X' once in square blocks (32 rows x 32 columns here, the block the MFMA
+# scale granularity allows), W_f and G_Y once in square blocks too; the same
+# codes serve the GEMM along either direction, so nothing is quantized twice,
+# but X' is stored expanded.
+# --------------------------------------------------------------------------
+def quantize_squares(fmt: int, mat: np.ndarray):
+    """Quantize a matrix [R][L] in 32 x 32 square blocks (32 consecutive rows x
+    32 consecutive columns, truncated at the edges). Returns (logical codes
+    [R][L], scales [ceil(R/32)][ceil(L/32)], count)."""
+    R, L = mat.shape
+    codes, scales, n = quantize_view(fmt, 32, mat, 1, R, 1, L)
+    return codes.reshape(R, L), scales.reshape(-(-R // 32), -(-L // 32)), n
+
+
+def dequant_squares(fmt: int, codes: np.ndarray, scales: np.ndarray):
+    R, L = codes.shape
+    return dequant_view(fmt, 32, codes, scales, 1, R, 1, L).reshape(R, L)
+
+
+def cuyckens_im2col_quantize(shape, x, fx):
+    """X' = classic im2col of x [M][K] (k = (ci, kh, kw)), quantized once in
+    square blocks: (codes [M][K], scales [M/32][K/32], count = |X'|)."""
+    return quantize_squares(fx, classic_im2col(shape, x))
+
+
+def cuyckens_fwd(shape, xcodes, xscales, w, fx, fw):
+    """Y[m][co] = sum_k X'q[m][k] W_fq[co][k] on the saved X'q; W_f in squares."""
+    Ho, Wo = out_hw(shape)
+    xq = dequant_squares(fx, xcodes, xscales)
+    wc, ws_, n = quantize_squares(fw, flatten_kernel(w))
+    y = xq @ dequant_squares(fw, wc, ws_).T
+    return y.reshape(Ho, Wo, shape.n, shape.cout), {"W": n}
+
+
+def cuyckens_dgrad(shape, dy, w, fdy, fw):
+    """G_X' = G_Yq . W_fq (both square-quantized once), then col2im."""
+    M = dy.shape[0] * dy.shape[1] * dy.shape[2]
+    gc, gs, n1 = quantize_squares(fdy, dy.reshape(M, -1))
+    wc, ws_, n2 = quantize_squares(fw, flatten_kernel(w))
+    gcol = dequant_squares(fdy, gc, gs) @ dequant_squares(fw, wc, ws_)  # [m][k]
+    return col2im(shape, gcol), {"G": n1, "W": n2}
+
+
+def cuyckens_wgrad(shape, dy, xcodes, xscales, fdy, fx):
+    """G_W = G_Yq^T . X'q on the saved X'q; returns [Cout][Kh][Kw][Cin]."""
+    M = dy.shape[0] * dy.shape[1] * dy.shape[2]
+    gc, gs, n = quantize_squares(fdy, dy.reshape(M, -1))
+    dwf = dequant_squares(fdy, gc, gs).T @ dequant_squares(fx, xcodes, xscales)  # [co][k]
+    dwr = dwf.reshape(shape.cout, shape.cin, shape.kh, shape.kw)
+    return np.ascontiguousarray(np.transpose(dwr, (0, 2, 3, 1))), {"G": n}
+
+
+def activation_mse(shape, x, fmt, method, bp=32):
+    """Mean squared error per element between every activation value a GEMM
+    consumes and its fp32 value (Table II's per-element quantization MSE),
+    over the values the forward and the weight-gradient GEMMs read:
+      "microqonv": X quantized once (32 channels x bp samples per pixel); each
+                   value of X' is a copy of one of them;
+      "naive":     X' quantized in lines of 32 along k (forward) and along m
+                   (weight gradient), both uses counted;
+      "cuyckens":  X' quantized once in 32 x 32 squares.
+    Padding positions of X' (zeros, exact in every method) are left out."""
+    xf = np.asarray(x, np.float32)
+    xcol = classic_im2col(shape, xf).astype(np.float64)
+    ids = classic_im2col(shape, (np.arange(xf.size, dtype=np.float64).reshape(xf.shape) + 1).astype(np.float32))
+    inside = ids > 0
+    if method == "microqonv":
+        c, s, _ = quantize(ROLE_ACT, fmt, bp, xf)
+        xq = dequantize(ROLE_ACT, fmt, bp, c, s).astype(np.float32)
+        err = (classic_im2col(shape, xq).astype(np.float64) - xcol)[inside]
+        return float(np.mean(err ** 2))
+    if method == "cuyckens":
+        c, s, _ = quantize_squares(fmt, xcol.astype(np.float32))
+        err = (dequant_squares(fmt, c, s) - xcol)[inside]
+        return float(np.mean(err ** 2))
+    fq, _ = quantize_lines(fmt, xcol.astype(np.float32))
+    bq, _ = quantize_lines(fmt, np.ascontiguousarray(xcol.T).astype(np.float32))
+    e1 = (fq - xcol)[inside]
+    e2 = (bq.T - xcol)[inside]
+    return float((np.sum(e1 ** 2) + np.sum(e2 ** 2)) / (e1.size + e2.size))
