@@ -43,13 +43,17 @@ CSRC = os.path.join(ROOT, "microscaling_quantized_convolution_mxq_amd", "csrc")
 CALLS = ["quantize_xw", "quantize_dy", "cbf_im2col", "forward", "backward_data", "backward_weight"]
 # timed on their own too, but not part of the step: the forward whose epilogue
 # writes Y as MX codes and scales (the next layer's activation) instead of fp32,
-# and the backward-data that writes dX the same way (the previous layer's gradient)
-EXTRA = ["forward_mx", "backward_data_mx"]
+# the backward-data that writes dX the same way (the previous layer's gradient),
+# the gradient quantized with stochastic rounding, and the backward-weight
+# variant that takes its scratch from the library's fixed array
+EXTRA = ["forward_mx", "backward_data_mx", "quantize_dy_sr", "backward_weight_noalloc"]
 # kernels each entry point launches (see the launchers in csrc/)
 CALL_KERNELS = {
     # X and W share one launch when their formats match, else one launch each
     "quantize_xw": ["mxq_quantize_group_kernel (same format; else 2 x mxq_quantize_kernel)"],
     "quantize_dy": ["mxq_quantize_kernel"], "cbf_im2col": ["cbf_im2col_kernel"],
+    "quantize_dy_sr": ["mxq_quantize_kernel (stochastic rounding)"],
+    "backward_weight_noalloc": ["as backward_weight, scratch in the library's fixed array"],
     "forward": ["mx_gemm_kernel<FwdProb>"], "forward_mx": ["mx_gemm_kernel<MxOutProb<FwdProb>>"],
     "backward_data_mx": ["mx_gemm_kernel<MxOutProb<DgradNatProb>> (8-bit W; else transpose_codes_kernel + "
                          "mx_gemm_kernel<MxOutProb<DgradProb>>)"],
@@ -74,7 +78,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="c2")
+    ap.add_argument("--workload", default="c5")
     ap.add_argument("--rotate-mb", type=float, default=640.0, help="minimum live set across rotated buffers")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-naive", action="store_true")
@@ -131,6 +135,8 @@ def main():
             mq.mqconv_quantize_group([(d["x"], d["xq"]), (d["w"], d["wq"])])
         elif name == "quantize_dy":
             mq.mqconv_quantize(d["dy"], d["gq"])
+        elif name == "quantize_dy_sr":
+            mq.mqconv_quantize_sr(d["dy"], d["gq"], 0x5EED)
         elif name == "cbf_im2col":
             mq.mqconv_cbf_im2col(s, d["xq"], d["cc"], d["cs"])
         elif name == "forward":
@@ -143,6 +149,8 @@ def main():
             mq.mqconv_backward_data_mx(s, d["gq"], d["wq"], d["dxq"], d["ws1"])
         elif name == "backward_weight":
             mq.mqconv_backward_weight(s, d["gq"], d["xq"], d["dw"], d["ws2"])
+        elif name == "backward_weight_noalloc":
+            mq.mqconv_backward_weight_noalloc(s, d["gq"], d["xq"], d["dw"])
 
     def step(d):
         for c in CALLS:
@@ -203,7 +211,8 @@ def main():
     # A graph of 2 x Rc calls rotating over Rc copies of just the buffers the
     # call touches, with Rc chosen so that those copies exceed the 256 MB
     # Infinity Cache as the step's sets do (no call reads cache-resident inputs).
-    NEED = {"quantize_xw": ("x", "xq", "w", "wq"), "quantize_dy": ("dy", "gq"),
+    NEED = {"quantize_xw": ("x", "xq", "w", "wq"), "quantize_dy": ("dy", "gq"), "quantize_dy_sr": ("dy", "gq"),
+            "backward_weight_noalloc": ("gq", "xq", "dw"),
             "cbf_im2col": ("xq", "cc", "cs"), "forward": ("xq", "wq", "y"), "forward_mx": ("xq", "wq", "yq"),
             "backward_data": ("gq", "wq", "dx", "ws1"), "backward_data_mx": ("gq", "wq", "dxq", "ws1"),
             "backward_weight": ("gq", "xq", "dw", "ws2")}
@@ -248,13 +257,14 @@ def main():
     dxq_b = mq.mqconv_codes_bytes(mq.ROLE_GRAD, wl.fdy, *x.shape) + mq.mqconv_scales_bytes(mq.ROLE_GRAD, bp, *x.shape)
     # bytes each call must move at least once (inputs read, outputs written)
     alg_bytes = {
-        "quantize_xw": 4 * nx + xq_b + 4 * nw + wq_b, "quantize_dy": 4 * ng + gq_b,
+        "quantize_xw": 4 * nx + xq_b + 4 * nw + wq_b, "quantize_dy": 4 * ng + gq_b, "quantize_dy_sr": 4 * ng + gq_b,
+        "backward_weight_noalloc": gq_b + xq_b + 4 * nw,
         "cbf_im2col": xq_b + col_b,
         "forward": xq_b + wq_b + 4 * ng, "backward_data": gq_b + wq_b + 4 * nx, "backward_weight": gq_b + xq_b + 4 * nw,
         "forward_mx": xq_b + wq_b + yq_b, "backward_data_mx": gq_b + wq_b + dxq_b,
     }
     alg_flop = {"forward": flop, "backward_data": flop, "backward_weight": flop, "forward_mx": flop,
-                "backward_data_mx": flop}
+                "backward_data_mx": flop, "backward_weight_noalloc": flop}
     step_gemms = ("forward", "backward_data", "backward_weight")
 
     def mfma_peak(fa, fb):
@@ -262,7 +272,7 @@ def main():
 
     call_peak = {"forward": mfma_peak(wl.fx, wl.fw), "forward_mx": mfma_peak(wl.fx, wl.fw),
                  "backward_data": mfma_peak(wl.fdy, wl.fw), "backward_data_mx": mfma_peak(wl.fdy, wl.fw),
-                 "backward_weight": mfma_peak(wl.fdy, wl.fx)}
+                 "backward_weight": mfma_peak(wl.fdy, wl.fx), "backward_weight_noalloc": mfma_peak(wl.fdy, wl.fx)}
     kernels = {}
     for c in CALLS + EXTRA:
         t = per_call[c] * 1e-3

@@ -276,7 +276,7 @@ int mqconv_backward_weight(const mq_conv* cv, mq_mx dyq, mq_mx xq, float* dw, vo
  *   Every call on one device uses that device's one array: calls that
  *   overlap in time on one device (two streams, two host threads) race and
  *   give undefined results; calls ordered on one stream are safe. */
-#define MQ_NOALLOC_SCRATCH_BYTES (128u << 20)
+#define MQ_NOALLOC_SCRATCH_BYTES (160u << 20)
 int mqconv_backward_weight_noalloc(const mq_conv* cv, mq_mx dyq, mq_mx xq, float* dw, void* stream);
 
 /* ---------------------------------------------------------------------------
@@ -303,6 +303,40 @@ int mqconv_naive_backward_data(const mq_conv* cv, const float* dy, const float* 
 int mqconv_naive_backward_weight(const mq_conv* cv, const float* dy, const float* x,
                                  mq_elem fdy, mq_elem fx, float* dw, void* ws, size_t ws_bytes,
                                  void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Square-block comparator (§III-C: the method of ref. [25], square blocks on
+ * the im2col-expanded activation of a fully connected layer, extended to
+ * convolution), kept to compare bytes moved and quantization error:
+ *   X'  = classic im2col of X as in the naive path (rows m = (ho, wo, n),
+ *         columns k = (ci, kh, kw)), quantized ONCE in 32 x 32 squares (32
+ *         consecutive m x 32 consecutive k, truncated at the edges) and kept
+ *         for the backward pass (the saved, expanded activation);
+ *   W_f [Cout][k] and G_Y [m][Cout] quantized once in squares as well;
+ *   forward:         Y    = X'q . W_fq^T
+ *   backward-data:   G_X' = G_Yq . W_fq, then col2im into G_X
+ *   backward-weight: G_W  = G_Yq^T . X'q (the saved X'q)
+ * A square's codes serve the contraction along either of its sides: where a
+ * GEMM contracts across the codes' runs it reads a copy re-laid in the
+ * workspace (codes move, no value is quantized again).
+ * Saved X'q: codes [M][ceil(K/32)] runs of 32 k (layout of packed rows as
+ * above), scales [ceil(M/32)][ceil(K/32)] E8M0 bytes, M = Ho*Wo*N,
+ * K = Cin*Kh*Kw. fp32 tensors x, dy, dx, w, dw as in the naive path.
+ * op of the workspace query: 0 forward (fa = X format, fb = W format),
+ * 1 backward-data (fa = dY, fb = W), 2 backward-weight (fa = dY, fb = X).
+ * --------------------------------------------------------------------------- */
+size_t mqconv_cuyckens_col_codes_bytes(const mq_conv* cv, mq_elem fx);
+size_t mqconv_cuyckens_col_scales_bytes(const mq_conv* cv);
+size_t mqconv_cuyckens_workspace_bytes(const mq_conv* cv, int op, mq_elem fa, mq_elem fb);
+int mqconv_cuyckens_im2col_quantize(const mq_conv* cv, const float* x, mq_elem fx, void* col_codes,
+                                    uint8_t* col_scales, void* stream);
+int mqconv_cuyckens_forward(const mq_conv* cv, const void* col_codes, const uint8_t* col_scales, mq_elem fx,
+                            const float* w, mq_elem fw, float* y, void* ws, size_t ws_bytes, void* stream);
+int mqconv_cuyckens_backward_data(const mq_conv* cv, const float* dy, const float* w, mq_elem fdy, mq_elem fw,
+                                  float* dx, void* ws, size_t ws_bytes, void* stream);
+int mqconv_cuyckens_backward_weight(const mq_conv* cv, const float* dy, const void* col_codes,
+                                    const uint8_t* col_scales, mq_elem fdy, mq_elem fx, float* dw, void* ws,
+                                    size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -75,6 +75,13 @@ def lib() -> ctypes.CDLL:
             "mqconv_backward_weight": (I, [CV, mq_mx, mq_mx, P, P, S, P]),
             "mqconv_backward_weight_noalloc": (I, [CV, mq_mx, mq_mx, P, P]),
             "mqconv_naive_workspace_bytes": (S, [CV, I, I, I]),
+            "mqconv_cuyckens_col_codes_bytes": (S, [CV, I]),
+            "mqconv_cuyckens_col_scales_bytes": (S, [CV]),
+            "mqconv_cuyckens_workspace_bytes": (S, [CV, I, I, I]),
+            "mqconv_cuyckens_im2col_quantize": (I, [CV, P, I, P, P, P]),
+            "mqconv_cuyckens_forward": (I, [CV, P, P, I, P, I, P, P, S, P]),
+            "mqconv_cuyckens_backward_data": (I, [CV, P, P, I, I, P, P, S, P]),
+            "mqconv_cuyckens_backward_weight": (I, [CV, P, P, P, I, I, P, P, S, P]),
             "mqconv_naive_forward": (I, [CV, P, P, I, I, P, P, S, P]),
             "mqconv_naive_backward_data": (I, [CV, P, P, I, I, P, P, S, P]),
             "mqconv_naive_backward_weight": (I, [CV, P, P, I, I, P, P, S, P]),
@@ -93,7 +100,9 @@ EXPORTED = ("mqconv_abi_version", "mqconv_status_string", "mqconv_codes_bytes", 
             "mqconv_cbf_im2col", "mqconv_workspace_bytes", "mqconv_forward", "mqconv_forward_mx", "mqconv_backward_data",
             "mqconv_backward_data_mx", "mqconv_backward_weight", "mqconv_backward_weight_noalloc",
             "mqconv_naive_workspace_bytes", "mqconv_naive_forward",
-            "mqconv_naive_backward_data", "mqconv_naive_backward_weight")
+            "mqconv_naive_backward_data", "mqconv_naive_backward_weight", "mqconv_cuyckens_col_codes_bytes",
+            "mqconv_cuyckens_col_scales_bytes", "mqconv_cuyckens_workspace_bytes", "mqconv_cuyckens_im2col_quantize",
+            "mqconv_cuyckens_forward", "mqconv_cuyckens_backward_data", "mqconv_cuyckens_backward_weight")
 
 
 def _status_string(status: int) -> str:
@@ -309,7 +318,7 @@ def mqconv_backward_weight(shape, dyq: MxTensor, xq: MxTensor, dw, ws=None, stre
 
 
 # scratch bytes the library holds per device for mqconv_backward_weight_noalloc
-NOALLOC_SCRATCH_BYTES = 128 << 20
+NOALLOC_SCRATCH_BYTES = 160 << 20
 
 
 def mqconv_backward_weight_noalloc(shape, dyq: MxTensor, xq: MxTensor, dw, stream=None) -> None:
@@ -343,3 +352,47 @@ def mqconv_naive_backward_weight(shape, dy, x, fdy: int, fx: int, dw, ws, stream
     _check(lib().mqconv_naive_backward_weight(ctypes.byref(_conv(shape)), _f32(dy, _ny(shape), "dy"),
                                               _f32(x, _nx(shape), "x"), fdy, fx, _f32(dw, _nw(shape), "dw"), p, n,
                                               _stream(stream)), "mqconv_naive_backward_weight")
+
+
+# ---- square-block comparator (include/mqconv.h) ----------------------------------
+def mqconv_cuyckens_col_codes_bytes(shape, fx: int) -> int:
+    return lib().mqconv_cuyckens_col_codes_bytes(ctypes.byref(_conv(shape)), fx)
+
+
+def mqconv_cuyckens_col_scales_bytes(shape) -> int:
+    return lib().mqconv_cuyckens_col_scales_bytes(ctypes.byref(_conv(shape)))
+
+
+def mqconv_cuyckens_workspace_bytes(shape, op: int, fa: int, fb: int) -> int:
+    return lib().mqconv_cuyckens_workspace_bytes(ctypes.byref(_conv(shape)), op, fa, fb)
+
+
+def mqconv_cuyckens_im2col_quantize(shape, x, fx: int, col_codes, col_scales, stream=None) -> None:
+    cc = _buf(col_codes, mqconv_cuyckens_col_codes_bytes(shape, fx), "uint8", "col_codes")
+    cs = _buf(col_scales, mqconv_cuyckens_col_scales_bytes(shape), "uint8", "col_scales")
+    _check(lib().mqconv_cuyckens_im2col_quantize(ctypes.byref(_conv(shape)), _f32(x, _nx(shape), "x"), fx, cc, cs,
+                                                 _stream(stream)), "mqconv_cuyckens_im2col_quantize")
+
+
+def mqconv_cuyckens_forward(shape, col_codes, col_scales, fx: int, w, fw: int, y, ws, stream=None) -> None:
+    p, n = _ws(ws)
+    cc = _buf(col_codes, mqconv_cuyckens_col_codes_bytes(shape, fx), "uint8", "col_codes")
+    cs = _buf(col_scales, mqconv_cuyckens_col_scales_bytes(shape), "uint8", "col_scales")
+    _check(lib().mqconv_cuyckens_forward(ctypes.byref(_conv(shape)), cc, cs, fx, _f32(w, _nw(shape), "w"), fw,
+                                         _f32(y, _ny(shape), "y"), p, n, _stream(stream)), "mqconv_cuyckens_forward")
+
+
+def mqconv_cuyckens_backward_data(shape, dy, w, fdy: int, fw: int, dx, ws, stream=None) -> None:
+    p, n = _ws(ws)
+    _check(lib().mqconv_cuyckens_backward_data(ctypes.byref(_conv(shape)), _f32(dy, _ny(shape), "dy"),
+                                               _f32(w, _nw(shape), "w"), fdy, fw, _f32(dx, _nx(shape), "dx"), p, n,
+                                               _stream(stream)), "mqconv_cuyckens_backward_data")
+
+
+def mqconv_cuyckens_backward_weight(shape, dy, col_codes, col_scales, fdy: int, fx: int, dw, ws, stream=None) -> None:
+    p, n = _ws(ws)
+    cc = _buf(col_codes, mqconv_cuyckens_col_codes_bytes(shape, fx), "uint8", "col_codes")
+    cs = _buf(col_scales, mqconv_cuyckens_col_scales_bytes(shape), "uint8", "col_scales")
+    _check(lib().mqconv_cuyckens_backward_weight(ctypes.byref(_conv(shape)), _f32(dy, _ny(shape), "dy"), cc, cs, fdy,
+                                                 fx, _f32(dw, _nw(shape), "dw"), p, n, _stream(stream)),
+           "mqconv_cuyckens_backward_weight")

@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmqconv.so")
 SOURCES = ["quantize.hip", "layout.hip", "gemm_fwd.hip", "gemm_fwd_mx.hip", "gemm_dgrad.hip", "gemm_dgrad_mx.hip", "gemm_dgrad_mx_relaid.hip", "gemm_wgrad.hip", "gemm_plain.hip",
-           "naive.hip", "mqconv_api.hip"]
+           "naive.hip", "cuyckens.hip", "mqconv_api.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -28,13 +28,24 @@ FLAGS = [
 ]
 
 
+def _includes(path: str, seen: set) -> set:
+    """Local headers a source includes, transitively (#include "...")."""
+    import re
+    for name in re.findall(r'^#include "([^"]+)"', open(path).read(), flags=re.M):
+        for d in (CSRC, os.path.join(ROOT, "include")):
+            h = os.path.join(d, name)
+            if os.path.exists(h) and h not in seen:
+                seen.add(h)
+                _includes(h, seen)
+    return seen
+
+
 def _stale(src: str, obj: str) -> bool:
-    """An object is stale when older than its source or any header."""
+    """An object is stale when older than its source or a header it includes."""
     if not os.path.exists(obj):
         return True
-    deps = [os.path.join(CSRC, src)] + [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".h")]
-    if src == "mqconv_api.hip":
-        deps.append(os.path.join(ROOT, "include", "mqconv.h"))
+    path = os.path.join(CSRC, src)
+    deps = [path, *_includes(path, set())]
     t = os.path.getmtime(obj)
     return any(os.path.getmtime(d) > t for d in deps)
 

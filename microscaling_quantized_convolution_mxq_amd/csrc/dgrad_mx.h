@@ -9,6 +9,7 @@ namespace mq {
 hipError_t prepare_backward_data(const Conv& cv, MxView dy, MxView w, float* dx, void* ws, hipStream_t st,
                                  DgradNatProb* nat, DgradProb* gen, bool* natural_out);
 int dgrad_rows(const Conv& cv);
+int dgrad_ksteps(const Conv& cv);
 // the GEMM launch of the re-laid weight path (6/4-bit weight codes)
 hipError_t launch_dgrad_mx_relaid(const Conv& cv, int fa, int fb, const DgradProb& p, MxOutView yq, hipStream_t st);
 
@@ -25,7 +26,7 @@ static hipError_t launch_dgrad_mx(const Conv& cv, int fa, int fb, const Q& q, Mx
   else if (cv.n % 32 == 0) o.ymode = 1;
   else if (32 % cv.n == 0) o.ymode = 2;
   else return hipErrorInvalidValue;  // blocks would straddle tile strips (rejected by the caller)
-  return launch_tiled(fa, fb, o, dgrad_rows(cv), cv.cin, cv.sh * cv.sw, st);
+  return launch_tiled(fa, fb, o, dgrad_rows(cv), cv.cin, cv.sh * cv.sw, st, dgrad_ksteps(cv));
 }
 
 }  // namespace mq

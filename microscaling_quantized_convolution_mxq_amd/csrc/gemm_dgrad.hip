@@ -59,6 +59,11 @@ hipError_t prepare_backward_data(const Conv& cv, MxView dy, MxView w, float* dx,
 
 // rows of the problem: every parity class spans at most maxHc x maxWc pixels
 int dgrad_rows(const Conv& cv) { return ceil_div(cv.h, cv.sh) * ceil_div(cv.w, cv.sw) * cv.n; }
+// K-steps of a tile on average over the parity classes: taps per class times
+// the pairs of Cout blocks
+int dgrad_ksteps(const Conv& cv) {
+  return (cv.kh * cv.kw + cv.sh * cv.sw - 1) / (cv.sh * cv.sw) * ((ceil_div(cv.cout, 32) + 1) / 2);
+}
 
 hipError_t launch_backward_data(const Conv& cv, MxView dy, MxView w, float* dx, void* ws, size_t,
                                 hipStream_t st) {
@@ -67,8 +72,8 @@ hipError_t launch_backward_data(const Conv& cv, MxView dy, MxView w, float* dx, 
   bool natural = false;
   const hipError_t e = prepare_backward_data(cv, dy, w, dx, ws, st, &q, &p, &natural);
   if (e != hipSuccess) return e;
-  if (natural) return launch_tiled(dy.fmt, w.fmt, q, dgrad_rows(cv), cv.cin, cv.sh * cv.sw, st);
-  return launch_tiled(dy.fmt, w.fmt, p, dgrad_rows(cv), cv.cin, cv.sh * cv.sw, st);
+  if (natural) return launch_tiled(dy.fmt, w.fmt, q, dgrad_rows(cv), cv.cin, cv.sh * cv.sw, st, dgrad_ksteps(cv));
+  return launch_tiled(dy.fmt, w.fmt, p, dgrad_rows(cv), cv.cin, cv.sh * cv.sw, st, dgrad_ksteps(cv));
 }
 
 

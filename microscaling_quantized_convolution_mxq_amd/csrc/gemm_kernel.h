@@ -1211,6 +1211,10 @@ hipError_t launch_gemm(int fa, int fb, const P& prob, dim3 grid, hipStream_t st)
 //   2: 256 x 128  (2 x 2 waves of 128 x 64)
 //   3: 64 x 256   (1 x 4 waves of 64 x 64)   short outputs
 //   4: 64 x 192   (2 x 2 waves of 32 x 96)   short outputs of 3 x 64 columns
+//   5: 128 x 128 with a 2-stage ring: a tile of few K-steps spends most of its
+//      life outside the K-loop (set-up, first loads, epilogue), so smaller
+//      workgroups that fit more per CU overlap those phases better (measured
+//      on the stride-2 backward-data of 9 K-steps per tile on average)
 struct TileChoice { int id, bm, bn; };
 inline TileChoice tile_shape(int id) {
   switch (id) {
@@ -1218,6 +1222,7 @@ inline TileChoice tile_shape(int id) {
     case 1: return {1, 128, 128};
     case 2: return {2, 256, 128};
     case 4: return {4, 64, 192};
+    case 5: return {5, 128, 128};
     default: return {3, 64, 256};
   }
 }
@@ -1244,6 +1249,9 @@ hipError_t launch_tile_id(int id, int fa, int fb, const P& prob, dim3 grid, hipS
       if constexpr (P::kQuad && KH) return hipErrorInvalidValue;  // not chosen (see launch_tiled)
       else return launch_gemm<P, 2, 2, 4, 2, NS, GS, KH>(fa, fb, prob, grid, st);
     case 4: return launch_gemm<P, 2, 2, 1, 3, NS, GS, KH>(fa, fb, prob, grid, st);
+    case 5:  // 128 x 128 with a 2-deep ring (backward-data with few K-steps per tile)
+      if constexpr (std::is_base_of<DgradProb, P>::value) return launch_gemm<P, 2, 2, 2, 2, 2, GS, KH>(fa, fb, prob, grid, st);
+      else return hipErrorInvalidValue;
     default: return launch_gemm<P, 1, 4, 2, 2, NS, GS, KH>(fa, fb, prob, grid, st);
   }
 }
@@ -1265,9 +1273,14 @@ inline bool half_k_blocks(int ga, int gb, int khalf, int fa, int fb) {
   return ga >= 8 && gb >= 8 && khalf && fa <= 1 && fb <= 1;
 }
 
+// ksteps: K-steps per tile (on average over the problem), when known
 template <class P>
-hipError_t launch_tiled(int fa, int fb, const P& prob_in, int M, int Ncols, int Z, hipStream_t st) {
+hipError_t launch_tiled(int fa, int fb, const P& prob_in, int M, int Ncols, int Z, hipStream_t st,
+                        int ksteps = 1 << 30) {
   TileChoice t = choose_tile(M, Ncols, Z);
+  if constexpr (std::is_base_of<DgradProb, P>::value) {
+    if (t.id == 2 && ksteps <= 12) t = tile_shape(5);
+  }
   // four K-blocks per step double the operand registers: the 256 x 128 tile
   // would then exceed the budget of two waves per SIMD
   if constexpr (P::kQuad) {
@@ -1298,12 +1311,20 @@ inline bool offsets_fit(long long bytes, long long bias) { return bytes + bias <
 // Number of K slices for an output of Ma x Nb with nkb K-blocks: up to two
 // workgroups per compute unit (a partial last wave of workgroups would
 // double the time), while the fp32 partial sums that the slices write and
-// the reduction reads stay below twice the operand bytes.
-inline int splitk_slices(long long Ma, long long Nb, long long nkb, long long operand_bytes) {
-  const TileChoice t = choose_tile(Ma, Nb, 1);
-  const long long tiles = ceil_div(Ma, t.bm) * ceil_div(Nb, t.bn);
+// the reduction reads stay below traffic_factor times the operand bytes.
+inline int splitk_slices(long long Ma, long long Nb, long long nkb, long long operand_bytes, int traffic_factor = 2) {
+  TileChoice t = choose_tile(Ma, Nb, 1);
+  long long tiles = ceil_div(Ma, t.bm) * ceil_div(Nb, t.bn);
   long long s = 512 / tiles;
-  const long long cap_traffic = operand_bytes / (4 * Ma * Nb) + 1;  // 2 x 4 bytes per partial
+  // the launch picks its tile from the slice count too: count with that tile
+  const TileChoice tz = choose_tile(Ma, Nb, s > 0 ? s : 1);
+  if (tz.id != t.id) {
+    t = tz;
+    tiles = ceil_div(Ma, t.bm) * ceil_div(Nb, t.bn);
+    s = 512 / tiles;
+  }
+  // 2 x 4 bytes per partial, at most traffic_factor / 2 times the operand bytes
+  const long long cap_traffic = operand_bytes * traffic_factor / (8 * Ma * Nb) + 1;
   if (s > cap_traffic) s = cap_traffic;
   if (s > nkb / 4) s = nkb / 4;  // at least 4 K-blocks per slice
   if (s < 1) s = 1;

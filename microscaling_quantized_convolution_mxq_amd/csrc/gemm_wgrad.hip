@@ -89,7 +89,13 @@ static int wgrad_splits(const Conv& cv, int fdy, int fx) {
   // the same count for either step size: capped by the number of four-block steps
   const WgradSteps ks = wgrad_steps(cv, 4);
   const long long nkb = (long long)cv.ho() * cv.wo() * ceil_div(cv.n, 32);
-  int s = splitk_slices(cv.cout, (long long)cv.kh * cv.kw * cv.cin, nkb, ops);
+  // workgroups of one wave group (full K-blocks) run one per CU at the
+  // two-times cap on the large layers; partial sums of up to four times the
+  // operand bytes let two run per CU, which measured faster despite the
+  // extra bytes (c5: 97.8 -> 83.7 us); the two-group half-block kernel
+  // keeps the tighter cap
+  const bool half = half_k_blocks(32, cv.cin % 32 == 0 ? 32 : 0, cv.n <= 16, fdy, fx);
+  int s = splitk_slices(cv.cout, (long long)cv.kh * cv.kw * cv.cin, nkb, ops, half ? 2 : 4);
   if (s > ks.total) s = ks.total;
   if (s < 1) s = 1;
   return s;

@@ -3,6 +3,7 @@
 // enqueues nothing), converts descriptors and hands off to the launchers.
 #include "mqconv.h"
 #include "mqconv_internal.h"
+#include "cuyckens.h"
 
 #include <limits.h>
 
@@ -360,6 +361,83 @@ int mqconv_naive_backward_weight(const mq_conv* cv, const float* dy, const float
   int s = naive_common(cv, dy, x, fdy, fx, dw, ws, ws_bytes, 2);
   if (s != MQ_OK) return s;
   return hip_status(launch_naive_backward_weight(to_conv(cv), dy, x, fdy, fx, dw, ws, (hipStream_t)stream));
+}
+
+// ---- square-block comparator -------------------------------------------------
+// the classic im2col extent M x K, and the GEMMs' 32-bit byte offsets over
+// the expanded tensors (fp32 G_X' of the backward-data is the largest)
+static bool cuyckens_fits(const mq_conv* cv) {
+  const Conv c = to_conv(cv);
+  const long long M = (long long)c.ho() * c.wo() * c.n, K = (long long)c.cin * c.kh * c.kw;
+  return M * (long long)((K + 31) / 32 * 32) <= kMaxElems && M * K * 4 < 0x7f000000LL;
+}
+
+size_t mqconv_cuyckens_col_codes_bytes(const mq_conv* cv, mq_elem fx) {
+  if (!conv_ok(cv) || !fmt_ok(fx) || !cuyckens_fits(cv)) return 0;
+  return cuyckens_col_codes_bytes(to_conv(cv), fx);
+}
+
+size_t mqconv_cuyckens_col_scales_bytes(const mq_conv* cv) {
+  if (!conv_ok(cv) || !cuyckens_fits(cv)) return 0;
+  return cuyckens_col_scales_bytes(to_conv(cv));
+}
+
+size_t mqconv_cuyckens_workspace_bytes(const mq_conv* cv, int op, mq_elem fa, mq_elem fb) {
+  if (!conv_ok(cv) || !fmt_ok(fa) || !fmt_ok(fb) || op < 0 || op > 2 || !cuyckens_fits(cv)) return 0;
+  return cuyckens_workspace_bytes(to_conv(cv), op, fa, fb);
+}
+
+// common checks of the comparator's calls (pointers a, b, out; formats; workspace)
+static int cuyckens_common(const mq_conv* cv, const void* a, const void* b, const void* out, int fa, int fb,
+                           void* ws, size_t ws_bytes, int op) {
+  if (!cv) return MQ_ERR_NULL;
+  if (!conv_ok(cv) || !cuyckens_fits(cv)) return MQ_ERR_SHAPE;
+  if (!a || !b || !out) return MQ_ERR_NULL;
+  if (!fmt_ok(fa) || !fmt_ok(fb)) return MQ_ERR_FORMAT;
+  if (((uintptr_t)a & 3u) || ((uintptr_t)b & 3u) || ((uintptr_t)out & 3u)) return MQ_ERR_ALIGN;
+  if (op >= 0) {
+    const size_t need = cuyckens_workspace_bytes(to_conv(cv), op, fa, fb);
+    if (!ws || ws_bytes < need) return MQ_ERR_WORKSPACE;
+    if (!aligned16(ws)) return MQ_ERR_ALIGN;
+  }
+  return MQ_OK;
+}
+
+int mqconv_cuyckens_im2col_quantize(const mq_conv* cv, const float* x, mq_elem fx, void* col_codes,
+                                    uint8_t* col_scales, void* stream) {
+  const int s = cuyckens_common(cv, x, col_codes, col_scales, fx, fx, nullptr, 0, -1);
+  if (s != MQ_OK) return s;
+  if (!aligned16(col_codes) || !aligned16(col_scales)) return MQ_ERR_ALIGN;
+  return hip_status(launch_cuyckens_im2col_quantize(to_conv(cv), x, fx, static_cast<uint8_t*>(col_codes), col_scales,
+                                                    (hipStream_t)stream));
+}
+
+int mqconv_cuyckens_forward(const mq_conv* cv, const void* col_codes, const uint8_t* col_scales, mq_elem fx,
+                            const float* w, mq_elem fw, float* y, void* ws, size_t ws_bytes, void* stream) {
+  if (!col_scales) return MQ_ERR_NULL;
+  const int s = cuyckens_common(cv, col_codes, w, y, fx, fw, ws, ws_bytes, 0);
+  if (s != MQ_OK) return s;
+  if (!aligned16(col_codes) || !aligned16(col_scales)) return MQ_ERR_ALIGN;
+  return hip_status(launch_cuyckens_forward(to_conv(cv), static_cast<const uint8_t*>(col_codes), col_scales, fx, w,
+                                            fw, y, ws, (hipStream_t)stream));
+}
+
+int mqconv_cuyckens_backward_data(const mq_conv* cv, const float* dy, const float* w, mq_elem fdy, mq_elem fw,
+                                  float* dx, void* ws, size_t ws_bytes, void* stream) {
+  const int s = cuyckens_common(cv, dy, w, dx, fdy, fw, ws, ws_bytes, 1);
+  if (s != MQ_OK) return s;
+  return hip_status(launch_cuyckens_backward_data(to_conv(cv), dy, w, fdy, fw, dx, ws, (hipStream_t)stream));
+}
+
+int mqconv_cuyckens_backward_weight(const mq_conv* cv, const float* dy, const void* col_codes,
+                                    const uint8_t* col_scales, mq_elem fdy, mq_elem fx, float* dw, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  if (!col_scales) return MQ_ERR_NULL;
+  const int s = cuyckens_common(cv, dy, col_codes, dw, fdy, fx, ws, ws_bytes, 2);
+  if (s != MQ_OK) return s;
+  if (!aligned16(col_codes) || !aligned16(col_scales)) return MQ_ERR_ALIGN;
+  return hip_status(launch_cuyckens_backward_weight(to_conv(cv), dy, static_cast<const uint8_t*>(col_codes),
+                                                    col_scales, fdy, fx, dw, ws, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -47,7 +47,7 @@ def test_noalloc_equals_workspace_call_twice_then_smaller(key):
 
 def test_noalloc_rejects_problems_beyond_the_scratch_array():
     wl = WORKLOADS["c5"]
-    big = ConvShape(64, 128, 160, 160, 256, 3, 3, 2, 1)  # needs 181.5 MiB
+    big = ConvShape(64, 128, 160, 160, 256, 3, 3, 2, 1)  # needs 213 MiB
     need = mq.mqconv_workspace_bytes(big, 2, wl.fdy, wl.fx)
     assert need > mq.NOALLOC_SCRATCH_BYTES
     xq = mq.MxTensor.empty(mq.ROLE_ACT, wl.fx, 32, (big.h, big.w, big.n, big.cin))
