@@ -15,6 +15,8 @@ Microscaling in Training and Inference":
   naive_* ......... §II-C (classic im2col, kernel flattening, the three GEMMs
                     G_W = G_Y . X'^T, G_X' = W^T . G_Y) and §III-C (quantize
                     the im2col-expanded tensor along each GEMM direction)
+  nvfp_* .......... §II-D / §III-A Eqs. (4)-(6): FP32 tensor scale, E4M3
+                    block scales, 8 x 8 square blocks (§IV-B, B = 64)
   cuyckens_* ...... §III-C (the square-block method of [25] extended to
                     convolution: the im2col-expanded X' quantized once in
                     square blocks and saved for the backward pass)
@@ -73,6 +75,8 @@ def lib():
             "mqref_encode_sr": (I, [I, D, ctypes.c_uint32]),
             "mqref_quantize_view_sr": (LL, [I, I, P, LL, LL, LL, LL, ctypes.c_uint64, P, P]),
             "mqref_dequant_view": (None, [I, I, P, P, LL, LL, LL, LL, P]),
+            "mqref_nvfp_quantize_view": (ctypes.c_float, [I, P, LL, LL, LL, LL, P, P]),
+            "mqref_nvfp_dequant_view": (None, [I, P, P, ctypes.c_float, LL, LL, LL, LL, P]),
             "mqref_row_bytes": (LL, [I, LL]),
             "mqref_pack_rows": (None, [I, P, LL, LL, P]),
             "mqref_unpack_rows": (None, [I, P, LL, LL, P]),
@@ -541,3 +545,27 @@ def activation_mse(shape, x, fmt, method, bp=32):
     e1 = (fq - xcol)[inside]
     e2 = (bq.T - xcol)[inside]
     return float((np.sum(e1 ** 2) + np.sum(e2 ** 2)) / (e1.size + e2.size))
+
+
+# --------------------------------------------------------------------------
+# Two-level (NVFP-style) scaling, Eqs. (4)-(6) (see mqref.c)
+# --------------------------------------------------------------------------
+def nvfp_quantize(role: int, fmt: int, x: np.ndarray):
+    """Returns (logical codes shaped like x, E4M3 block scales
+    [A][B][ceil(P/8)][ceil(C/8)] of the role's view, fp32 tensor scale T)."""
+    dims = x.shape
+    A, P, B, C = _role_view(role, dims)
+    src = np.ascontiguousarray(x, dtype=np.float32).reshape(-1)
+    codes = np.empty(src.size, np.uint8)
+    bs = np.empty(A * B * (-(-P // 8)) * (-(-C // 8)), np.uint8)
+    T = lib().mqref_nvfp_quantize_view(fmt, _p(src), A, P, B, C, _p(codes), _p(bs))
+    return codes.reshape(dims), bs.reshape(A, B, -(-P // 8), -(-C // 8)), float(np.float32(T))
+
+
+def nvfp_dequantize(role: int, fmt: int, codes: np.ndarray, bscales: np.ndarray, T: float):
+    dims = codes.shape
+    A, P, B, C = _role_view(role, dims)
+    out = np.empty(codes.size, np.float64)
+    lib().mqref_nvfp_dequant_view(fmt, _p(np.ascontiguousarray(codes, np.uint8).reshape(-1)),
+                                  _p(np.ascontiguousarray(bscales, np.uint8).reshape(-1)), T, A, P, B, C, _p(out))
+    return out.reshape(dims)

@@ -20,6 +20,9 @@
  *   - convolution, input and weight gradients: §II-A, Eqs. (1)-(3), with
  *     stride and zero padding, kernel not flipped (§II-C1 patch definition).
  *   - classic im2col and kernel flattening: §II-C1, §II-C2.
+ *   - stochastic rounding of the gradient: §III-A (Philox4x32-10 words).
+ *   - two-level (NVFP-style) scaling: §II-D / §III-A, Eqs. (4)-(6), square
+ *     blocks of 64 (§IV-B).
  *
  * Build: gcc -O2 -fopenmp -fPIC -shared mqref.c -o libmqref.so -lm
  */
@@ -303,6 +306,77 @@ long long mqref_quantize_view_sr(int f, int bp, const float* src, long long A, l
           count += (p1 - p0) * (c1 - c0);
         }
   return count;
+}
+
+/* ------------------------------------------------------------------------
+ * Two-level (NVFP-style) microscaling, Eqs. (4)-(6) of §II-D / §III-A: one
+ * FP32 scale for the whole tensor and one E4M3 scale per block,
+ *   T   = max|X| / (448 * m)                     (m = largest element value)
+ *   B_i = E4M3(max|X_i| / (T * m)), rounded to nearest
+ *   q   = element code of X_i / (B_i * T), rounded to nearest even
+ * with the pages' square blocks of B = 64 elements: 8 channels x 8 partner
+ * indices inside one pixel (activations, gradients) or one tap (weights).
+ * T, the divisions and products are fp32 operations, as the formula is
+ * written for an FP32 tensor scale. Readings where the pages are silent: an
+ * all-zero tensor gets T = 0 and all-zero codes; a block whose E4M3 scale
+ * rounds to 0 gets all-zero codes; non-finite values are left out of T and
+ * their block gets the E4M3 NaN scale (0x7F) and zero codes.
+ * Block scale of block (a, b, pb, cb) at bscales[((a*B + b)*nPB8 + pb)*nCB8 + cb].
+ * Returns T.
+ * ------------------------------------------------------------------------ */
+float mqref_nvfp_quantize_view(int f, const float* src, long long A, long long P, long long B, long long C,
+                               uint8_t* codes, uint8_t* bscales) {
+  const long long nPB = (P + 7) / 8, nCB = (C + 7) / 8, n = A * P * B * C;
+  float amax = 0.0f;
+  for (long long i = 0; i < n; i++)
+    if (isfinite(src[i]) && fabsf(src[i]) > amax) amax = fabsf(src[i]);
+  const float m = (float)FMT[f].maxnorm;
+  const float T = amax / (448.0f * m);
+  const float Tm = T * m;
+#pragma omp parallel for collapse(2) schedule(static)
+  for (long long a = 0; a < A; a++)
+    for (long long b = 0; b < B; b++)
+      for (long long pb = 0; pb < nPB; pb++)
+        for (long long cb = 0; cb < nCB; cb++) {
+          const long long p0 = pb * 8, p1 = p0 + 8 < P ? p0 + 8 : P;
+          const long long c0 = cb * 8, c1 = c0 + 8 < C ? c0 + 8 : C;
+          float bmax = 0.0f;
+          int nonfinite = 0;
+          for (long long p = p0; p < p1; p++)
+            for (long long c = c0; c < c1; c++) {
+              const float x = src[((a * P + p) * B + b) * C + c];
+              if (!isfinite(x)) nonfinite = 1;
+              else if (fabsf(x) > bmax) bmax = fabsf(x);
+            }
+          int sc;
+          if (nonfinite) sc = 0x7F;
+          else if (T == 0.0f) sc = 0;
+          else sc = mqref_encode(0, (double)(bmax / Tm)); /* E4M3, nearest even, saturating */
+          bscales[((a * B + b) * nPB + pb) * nCB + cb] = (uint8_t)sc;
+          const float d = (float)mqref_decode(0, sc) * T;
+          for (long long p = p0; p < p1; p++)
+            for (long long c = c0; c < c1; c++) {
+              const long long i = ((a * P + p) * B + b) * C + c;
+              if (nonfinite || sc == 0) codes[i] = 0;
+              else codes[i] = (uint8_t)mqref_encode(f, (double)(src[i] / d));
+            }
+        }
+  return T;
+}
+
+/* Dequantized values of the same view: code value * B_i * T (fp64). */
+void mqref_nvfp_dequant_view(int f, const uint8_t* codes, const uint8_t* bscales, float T, long long A, long long P,
+                             long long B, long long C, double* out) {
+  const long long nPB = (P + 7) / 8, nCB = (C + 7) / 8;
+#pragma omp parallel for collapse(2) schedule(static)
+  for (long long a = 0; a < A; a++)
+    for (long long p = 0; p < P; p++)
+      for (long long b = 0; b < B; b++)
+        for (long long c = 0; c < C; c++) {
+          const long long i = ((a * P + p) * B + b) * C + c;
+          const int sc = bscales[((a * B + b) * nPB + p / 8) * nCB + c / 8];
+          out[i] = mqref_decode(f, codes[i]) * mqref_decode(0, sc) * (double)T;
+        }
 }
 
 /* Dequantize (fake quantization): code value times 2^(S-127). Same view. */
