@@ -305,6 +305,33 @@ int mqconv_naive_backward_weight(const mq_conv* cv, const float* dy, const float
                                  void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Two-level (NVFP-style) microscaling, §II-D / §III-A Eqs. (4)-(6), the
+ * pages' experimental format: one FP32 scale for the whole tensor and one
+ * E4M3 scale per square block of 64 elements (8 channels x 8 partner
+ * indices inside one pixel or tap, §IV-B):
+ *   T   = max|X| / (448 * m)             m = largest element value (6 for E2M1)
+ *   B_i = E4M3(max|X_i| / (T * m))       rounded to nearest even, saturating
+ *   q   = code of X_i / (B_i * T)        rounded to nearest even, saturating
+ * evaluated in fp32 (IEEE division and products); dequantized value =
+ * value(q) * B_i * T. An all-zero tensor gets T = 0 and zero codes; a block
+ * whose scale rounds to 0 gets zero codes; non-finite values are left out of
+ * T and their block gets the E4M3 NaN byte 0x7F and zero codes.
+ * Codes: the packed layout of the role above (mqconv_codes_bytes).
+ * Block scales (E4M3 bytes): ACT/GRAD [H][W][ceil(N/8)][ceil(C/8)],
+ * WEIGHT [Kh][Kw][ceil(Cout/8)][ceil(Cin/8)] (mqconv_nvfp_scales_bytes).
+ * tensor_scale: one fp32 on the device. ws: mqconv_nvfp_workspace_bytes()
+ * bytes of device scratch (partial maxima).
+ * The GEMMs of the path take E8M0 block scales (what gfx950's block-scaled
+ * MFMA applies per 32 K-elements); this format is quantized and measured
+ * (error against the E8M0 format at equal element bits), not multiplied.
+ * --------------------------------------------------------------------------- */
+size_t mqconv_nvfp_scales_bytes(mq_role role, int32_t d0, int32_t d1, int32_t d2, int32_t d3);
+size_t mqconv_nvfp_workspace_bytes(void);
+int mqconv_nvfp_quantize(const float* src, mq_role role, mq_elem fmt, int32_t d0, int32_t d1, int32_t d2, int32_t d3,
+                         void* codes, uint8_t* block_scales, float* tensor_scale, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/* ---------------------------------------------------------------------------
  * Square-block comparator (§III-C: the method of ref. [25], square blocks on
  * the im2col-expanded activation of a fully connected layer, extended to
  * convolution), kept to compare bytes moved and quantization error:

@@ -75,6 +75,9 @@ def lib() -> ctypes.CDLL:
             "mqconv_backward_weight": (I, [CV, mq_mx, mq_mx, P, P, S, P]),
             "mqconv_backward_weight_noalloc": (I, [CV, mq_mx, mq_mx, P, P]),
             "mqconv_naive_workspace_bytes": (S, [CV, I, I, I]),
+            "mqconv_nvfp_scales_bytes": (S, [I, I32, I32, I32, I32]),
+            "mqconv_nvfp_workspace_bytes": (S, []),
+            "mqconv_nvfp_quantize": (I, [P, I, I, I32, I32, I32, I32, P, P, P, P, S, P]),
             "mqconv_cuyckens_col_codes_bytes": (S, [CV, I]),
             "mqconv_cuyckens_col_scales_bytes": (S, [CV]),
             "mqconv_cuyckens_workspace_bytes": (S, [CV, I, I, I]),
@@ -100,7 +103,8 @@ EXPORTED = ("mqconv_abi_version", "mqconv_status_string", "mqconv_codes_bytes", 
             "mqconv_cbf_im2col", "mqconv_workspace_bytes", "mqconv_forward", "mqconv_forward_mx", "mqconv_backward_data",
             "mqconv_backward_data_mx", "mqconv_backward_weight", "mqconv_backward_weight_noalloc",
             "mqconv_naive_workspace_bytes", "mqconv_naive_forward",
-            "mqconv_naive_backward_data", "mqconv_naive_backward_weight", "mqconv_cuyckens_col_codes_bytes",
+            "mqconv_naive_backward_data", "mqconv_naive_backward_weight", "mqconv_nvfp_scales_bytes",
+            "mqconv_nvfp_workspace_bytes", "mqconv_nvfp_quantize", "mqconv_cuyckens_col_codes_bytes",
             "mqconv_cuyckens_col_scales_bytes", "mqconv_cuyckens_workspace_bytes", "mqconv_cuyckens_im2col_quantize",
             "mqconv_cuyckens_forward", "mqconv_cuyckens_backward_data", "mqconv_cuyckens_backward_weight")
 
@@ -396,3 +400,24 @@ def mqconv_cuyckens_backward_weight(shape, dy, col_codes, col_scales, fdy: int, 
     _check(lib().mqconv_cuyckens_backward_weight(ctypes.byref(_conv(shape)), _f32(dy, _ny(shape), "dy"), cc, cs, fdy,
                                                  fx, _f32(dw, _nw(shape), "dw"), p, n, _stream(stream)),
            "mqconv_cuyckens_backward_weight")
+
+
+# ---- two-level (NVFP-style) quantization (include/mqconv.h) -------------------------
+def mqconv_nvfp_scales_bytes(role: int, d0: int, d1: int, d2: int, d3: int) -> int:
+    return lib().mqconv_nvfp_scales_bytes(role, d0, d1, d2, d3)
+
+
+def mqconv_nvfp_workspace_bytes() -> int:
+    return lib().mqconv_nvfp_workspace_bytes()
+
+
+def mqconv_nvfp_quantize(src, role: int, fmt: int, dims, codes, block_scales, tensor_scale, ws, stream=None) -> None:
+    """Two-level quantization of the fp32 tensor src (role layout, dims) into
+    packed codes, E4M3 block scales and one fp32 tensor scale (device)."""
+    d = tuple(int(v) for v in dims)
+    p, n = _ws(ws)
+    _check(lib().mqconv_nvfp_quantize(_f32(src, _prod(d), "src"), role, fmt, *d,
+                                      _buf(codes, mqconv_codes_bytes(role, fmt, *d), "uint8", "codes"),
+                                      _buf(block_scales, mqconv_nvfp_scales_bytes(role, *d), "uint8", "block_scales"),
+                                      _f32(tensor_scale, 1, "tensor_scale"), p, n, _stream(stream)),
+           "mqconv_nvfp_quantize")

@@ -4,6 +4,7 @@
 #include "mqconv.h"
 #include "mqconv_internal.h"
 #include "cuyckens.h"
+#include "nvfp.h"
 
 #include <limits.h>
 
@@ -361,6 +362,34 @@ int mqconv_naive_backward_weight(const mq_conv* cv, const float* dy, const float
   int s = naive_common(cv, dy, x, fdy, fx, dw, ws, ws_bytes, 2);
   if (s != MQ_OK) return s;
   return hip_status(launch_naive_backward_weight(to_conv(cv), dy, x, fdy, fx, dw, ws, (hipStream_t)stream));
+}
+
+// ---- two-level (NVFP-style) quantization ---------------------------------------
+size_t mqconv_nvfp_scales_bytes(mq_role role, int32_t d0, int32_t d1, int32_t d2, int32_t d3) {
+  if (!dims_ok(d0, d1, d2, d3)) return 0;
+  const long long nc8 = (d3 + 7) / 8;
+  if (role == MQ_ROLE_ACT || role == MQ_ROLE_GRAD) return (size_t)((long long)d0 * d1 * ceil_div(d2, 8) * nc8);
+  if (role == MQ_ROLE_WEIGHT) return (size_t)((long long)d1 * d2 * ceil_div(d0, 8) * nc8);
+  return 0;
+}
+
+size_t mqconv_nvfp_workspace_bytes(void) { return nvfp_workspace_bytes(); }
+
+int mqconv_nvfp_quantize(const float* src, mq_role role, mq_elem fmt, int32_t d0, int32_t d1, int32_t d2, int32_t d3,
+                         void* codes, uint8_t* block_scales, float* tensor_scale, void* ws, size_t ws_bytes,
+                         void* stream) {
+  if (!src || !codes || !block_scales || !tensor_scale) return MQ_ERR_NULL;
+  if (!fmt_ok(fmt)) return MQ_ERR_FORMAT;
+  if (role != MQ_ROLE_ACT && role != MQ_ROLE_GRAD && role != MQ_ROLE_WEIGHT) return MQ_ERR_FORMAT;
+  if (!dims_ok(d0, d1, d2, d3)) return MQ_ERR_SHAPE;
+  if (!ws || ws_bytes < nvfp_workspace_bytes()) return MQ_ERR_WORKSPACE;
+  if (!aligned16(codes) || ((uintptr_t)src & 3u) || ((uintptr_t)tensor_scale & 3u) || ((uintptr_t)ws & 3u))
+    return MQ_ERR_ALIGN;
+  int A, P, B;
+  if (role == MQ_ROLE_WEIGHT) { A = 1; P = d0; B = d1 * d2; }
+  else { A = d0 * d1; P = d2; B = 1; }
+  return hip_status(launch_nvfp_quantize(src, static_cast<uint8_t*>(codes), block_scales, tensor_scale, fmt, A, P, B,
+                                         d3, ws, (hipStream_t)stream));
 }
 
 // ---- square-block comparator -------------------------------------------------

@@ -26,7 +26,7 @@ def _declared():
 
 def test_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 28
+    assert len(names) == 31
     out = subprocess.run(["nm", "-D", "--defined-only", mq.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT\s+(mqconv_\w+)", out))
     assert set(names) <= exported
