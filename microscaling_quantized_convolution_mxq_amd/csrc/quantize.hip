@@ -142,9 +142,9 @@ __device__ __forceinline__ void quantize_tiles(const float* __restrict__ src, ui
 
   // cbs > 1 splits the channel blocks of small tensors over workgroups
   // (never with LDS staging, which needs a tile's whole rows)
-  for (int cb = cb0; cb < nCB; cb += cbs) {
+  // the 16 values of channel block cb of this lane (zeros past the row or C)
+  auto load16 = [&](int cb, float (&x)[16]) {
     const int c0 = cb * 32 + half * 16;
-    float x[16];
     if (row_ok && vec && c0 + 16 <= C) {
       const float4* s4 = reinterpret_cast<const float4*>(srow + c0);
 #pragma unroll
@@ -156,6 +156,17 @@ __device__ __forceinline__ void quantize_tiles(const float* __restrict__ src, ui
 #pragma unroll
       for (int i = 0; i < 16; i++) x[i] = (row_ok && c0 + i < C) ? srow[c0 + i] : 0.0f;
     }
+  };
+  // software pipelined: the loads of the next channel block leave before the
+  // current one is reduced, converted and stored
+  float xn[16];
+  if (cb0 < nCB) load16(cb0, xn);
+  for (int cb = cb0; cb < nCB; cb += cbs) {
+    const int c0 = cb * 32 + half * 16;
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; i++) x[i] = xn[i];
+    if (cb + cbs < nCB) load16(cb + cbs, xn);
     uint32_t m = 0;
 #pragma unroll
     for (int i = 0; i < 16; i++) m = max(m, __float_as_uint(x[i]) & 0x7fffffffu);
