@@ -9,17 +9,14 @@
 
 namespace mq {
 
-// X'[m][k] (transposed = false) or X'^T[k][m] (transposed = true).
-template <bool TR>
+// X'[m][k], k = (ci, kh, kw): one thread per element, in row order.
 static __global__ __launch_bounds__(256) void classic_im2col_kernel(const float* __restrict__ x, float* __restrict__ out,
-                                                            int N, int C, int H, int W, int KH, int KW, int sh,
-                                                            int sw, int ph, int pw, int Wo, long long M, int K) {
+                                                                    int N, int C, int H, int W, int KH, int KW, int sh,
+                                                                    int sw, int ph, int pw, int Wo, long long M, int K) {
   const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
   if (idx >= M * K) return;
-  long long m;
-  int k;
-  if (TR) { k = (int)(idx / M); m = idx - (long long)k * M; }
-  else { m = idx / K; k = (int)(idx - m * K); }
+  const long long m = idx / K;
+  const int k = (int)(idx - m * K);
   const int n = (int)(m % N);
   const int o = (int)(m / N);
   const int ho = o / Wo, wo = o - ho * Wo;
@@ -32,16 +29,49 @@ static __global__ __launch_bounds__(256) void classic_im2col_kernel(const float*
   out[idx] = v;
 }
 
-// W_f[co][k] (TR = false) or W_f^T[k][co] (TR = true), k = (ci, kh, kw); w is [Cout][Kh][Kw][Cin].
-template <bool TR>
-static __global__ __launch_bounds__(256) void flatten_w_kernel(const float* __restrict__ w, float* __restrict__ out, int Cout,
-                                                       int Cin, int KH, int KW) {
+// X'^T with its rows in tap-major order, out[(kh*KW + kw)*C + ci][m] =
+// X'[m][(ci, kh, kw)] (the same rows as the channel-major X'^T, permuted):
+// one 32 x 32 tile of (m, ci) of one tap per workgroup, through LDS, so the
+// reads run along ci (contiguous in X) and the writes along m.
+// Grid: (ceil(M/32), ceil(C/32), KH*KW).
+static __global__ __launch_bounds__(256) void classic_im2col_t_kernel(const float* __restrict__ x,
+                                                                      float* __restrict__ out, int N, int C, int H,
+                                                                      int W, int KW, int sh, int sw, int ph, int pw,
+                                                                      int Wo, long long M) {
+  __shared__ float t[32][33];
+  const long long m0 = (long long)blockIdx.x * 32;
+  const int c0 = blockIdx.y * 32;
+  const int tap = blockIdx.z, kh = tap / KW, kw = tap - kh * KW;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  for (int i = ty; i < 32; i += 8) {
+    const long long m = m0 + i;
+    const int ci = c0 + tx;
+    float v = 0.0f;
+    if (m < M && ci < C) {
+      const long long o = m / N;
+      const int n = (int)(m - o * N);
+      const int ho = (int)(o / Wo), wo = (int)(o - (long long)ho * Wo);
+      const int hi = ho * sh + kh - ph, wi = wo * sw + kw - pw;
+      if (hi >= 0 && hi < H && wi >= 0 && wi < W) v = x[(((long long)hi * W + wi) * N + n) * C + ci];
+    }
+    t[i][tx] = v;
+  }
+  __syncthreads();
+  for (int i = ty; i < 32; i += 8) {
+    const int ci = c0 + i;
+    const long long m = m0 + tx;
+    if (ci < C && m < M) out[((long long)tap * C + ci) * M + m] = t[tx][i];
+  }
+}
+
+// W_f[co][k], k = (ci, kh, kw); w is [Cout][Kh][Kw][Cin].
+static __global__ __launch_bounds__(256) void flatten_w_kernel(const float* __restrict__ w, float* __restrict__ out,
+                                                               int Cout, int Cin, int KH, int KW) {
   const long long K = (long long)Cin * KH * KW;
   const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
   if (idx >= K * Cout) return;
-  int co, k;
-  if (TR) { k = (int)(idx / Cout); co = (int)(idx - (long long)k * Cout); }
-  else { co = (int)(idx / K); k = (int)(idx - (long long)co * K); }
+  const int co = (int)(idx / K);
+  const int k = (int)(idx - (long long)co * K);
   const int ci = k / (KH * KW);
   const int r = k - ci * KH * KW;
   const int kh = r / KW, kw = r - kh * KW;
@@ -69,7 +99,11 @@ static __global__ __launch_bounds__(256) void transpose_f32_kernel(const float* 
 }
 
 // col2im (the adjoint of classic im2col) in gather form: every G_X element
-// sums the G_X' entries copied from it. gcol is [M][K] with K = (ci, kh, kw).
+// sums the G_X' entries copied from it, taps in (kh, kw) order. gcol is
+// [M][K] with columns k = (ci, kh, kw) (TAPS = false) or (kh, kw, ci) (TAPS =
+// true: neighbouring threads, neighbouring channels, read neighbouring
+// words).
+template <bool TAPS>
 static __global__ __launch_bounds__(256) void col2im_kernel(const float* __restrict__ gcol, float* __restrict__ dx, int N,
                                                      int C, int H, int W, int KH, int KW, int sh, int sw, int ph,
                                                      int pw, int Ho, int Wo) {
@@ -94,7 +128,7 @@ static __global__ __launch_bounds__(256) void col2im_kernel(const float* __restr
       const int wo = tw / sw;
       if (wo >= Wo) continue;
       const long long m = ((long long)ho * Wo + wo) * N + n;
-      s += gcol[m * K + (ci * KH + kh) * KW + kw];
+      s += gcol[m * K + (TAPS ? (kh * KW + kw) * C + ci : (ci * KH + kh) * KW + kw)];
     }
   }
   dx[idx] = s;
@@ -115,6 +149,17 @@ static __global__ __launch_bounds__(256) void wgrad_reduce_permute_kernel(const 
   const long long k = ((long long)ci * KH + kh) * KW + kw;
   float s = 0.0f;
   for (int z = 0; z < splits; z++) s += part[((long long)z * Cout + co) * K + k];
+  dw[idx] = s;
+}
+
+// dw[i] = sum_z part[z][i] over the split-K slices, in slice order (the
+// slices already hold dW's own [Cout][Kh][Kw][Cin] order).
+static __global__ __launch_bounds__(256) void sum_slices_kernel(const float* __restrict__ part, float* __restrict__ dw,
+                                                                long long total, int splits) {
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= total) return;
+  float s = 0.0f;
+  for (int z = 0; z < splits; z++) s += part[(long long)z * total + idx];
   dw[idx] = s;
 }
 

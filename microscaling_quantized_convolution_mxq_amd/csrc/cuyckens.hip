@@ -58,13 +58,13 @@ __global__ __launch_bounds__(256) void square_im2col_quantize_kernel(const float
   uint32_t a = 0;
 #pragma unroll
   for (int i = 0; i < 16; i++) a = max(a, __float_as_uint(xv[i]) & 0x7fffffffu);
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) a = max(a, (uint32_t)__shfl_xor((int)a, off));
+  a = group_max(a, 64);
   const uint32_t S = scale_byte_from_amax<F>(a);
   float v[16];
   scale_clamp16<F>(xv, S, v);
   constexpr int RB = run_bytes_of(F);
-  if (row_ok) convert_store_half_run<F>(codes + m * ((long long)nKB * RB) + (long long)kb * RB + half * (RB / 2), v);
+  if (row_ok)
+    convert_store_half_run<F>(codes + m * ((long long)nKB * RB) + (long long)kb * RB + half * (RB / 2), v, code_keep(S));
   if (lane == 0) scales[mb * nKB + kb] = (uint8_t)S;
 }
 
@@ -179,7 +179,7 @@ hipError_t launch_cuyckens_im2col_quantize(const Conv& cv, const float* x, int f
 static hipError_t square_weight(const Conv& cv, const float* w, int fw, float* wf, uint8_t* wc, uint8_t* wsc,
                                 hipStream_t st) {
   const SqSizes s = sq_sizes(cv);
-  hipLaunchKernelGGL(flatten_w_kernel<false>, dim3(nblk(cv.cout * s.K)), dim3(256), 0, st, w, wf, cv.cout, cv.cin,
+  hipLaunchKernelGGL(flatten_w_kernel, dim3(nblk(cv.cout * s.K)), dim3(256), 0, st, w, wf, cv.cout, cv.cin,
                      cv.kh, cv.kw);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -221,7 +221,7 @@ hipError_t launch_cuyckens_backward_data(const Conv& cv, const float* dy, const 
   const SqOperand a{gc, gs, (int)s.M, fdy, 5, s.nCoB, 1, (long long)s.nMB * s.nCoB};
   const SqOperand b{wct, wsc, (int)s.K, fw, 5, 1, s.nKB, (long long)s.nCoB * s.nKB};
   if ((e = square_gemm(a, b, s.nCoB, gcol, 1, st)) != hipSuccess) return e;
-  hipLaunchKernelGGL(col2im_kernel, dim3(nblk((long long)cv.h * cv.w * cv.n * cv.cin)), dim3(256), 0, st, gcol, dx,
+  hipLaunchKernelGGL(col2im_kernel<false>, dim3(nblk((long long)cv.h * cv.w * cv.n * cv.cin)), dim3(256), 0, st, gcol, dx,
                      cv.n, cv.cin, cv.h, cv.w, cv.kh, cv.kw, cv.sh, cv.sw, cv.ph, cv.pw, cv.ho(), cv.wo());
   return hipGetLastError();
 }

@@ -625,48 +625,43 @@ __device__ __forceinline__ void stage_barrier() {
 // NG times the K range with NG times the waves.
 // At least two waves per SIMD: the register budget (VGPRs + accumulation
 // registers) stays within 256, so two 256x128 workgroups share a CU.
-// Maximum over aligned groups of g lanes (g = 2, 4, ..., 64, uniform), every
-// lane of a group receiving it: swaps within quads, mirrors within 8 and 16
-// lanes (DPP), a swizzle across the two 16-lane rows of 32 lanes, and the two
-// wave halves.
-template <int CTRL>
-__device__ __forceinline__ uint32_t max_dpp(uint32_t a) {
-  return max(a, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, CTRL, 0xF, 0xF, false));
-}
-__device__ __forceinline__ uint32_t group_max(uint32_t a, int g) {
-  a = max_dpp<0xB1>(a);                // quad_perm [1,0,3,2]: lane ^ 1
-  if (g >= 4) a = max_dpp<0x4E>(a);    // quad_perm [2,3,0,1]: lane ^ 2
-  if (g >= 8) a = max_dpp<0x141>(a);   // row_half_mirror: 7 - lane within 8
-  if (g >= 16) a = max_dpp<0x140>(a);  // row_mirror: 15 - lane within 16
-  if (g >= 32) a = max(a, (uint32_t)__builtin_amdgcn_ds_swizzle((int)a, 0x401F));  // lane ^ 16 within 32
-  if (g >= 64) a = max((uint32_t)__builtin_amdgcn_readlane((int)a, 0), (uint32_t)__builtin_amdgcn_readlane((int)a, 32));
-  return a;
-}
-
 // MX epilogue of one 32-row strip (rows ms.., columns c0.. of the wave, in
 // LDS with pitch EP floats): lane l takes row l/2 and the 16 channels
 // (l%2)*16.. of each 32-column block; the block maximum is a cross-lane
 // maximum over the lanes of the block's rows; codes and scale bytes follow
 // the element rule of the quantizer (scale_clamp16, convert_store_half_run).
-// The codes are packed in LDS (cst: 32 rows of TN runs) and leave as
-// consecutive dwords of each row segment (whole rows are one contiguous
-// stretch), not as scattered half runs.
-// LEAN (tiles whose accumulators already fill most registers): one block at
-// a time and one copy piece at a time, so the epilogue needs few registers.
+// FP6 converts two blocks per instruction. The codes are packed in LDS
+// (cst: 32 rows of TN runs) and leave as consecutive dwords of each row
+// segment (whole rows are one contiguous stretch), not as scattered half
+// runs.
+// LEAN (tiles whose accumulators already fill most registers): one block
+// (FP6: one pair) at a time and one copy piece at a time, so the epilogue
+// needs few registers.
 template <int F, int TN, bool LEAN, class P>
 __device__ __forceinline__ void mx_store_strip(const P& p, const typename P::Ctx& cx, const float* strip, int EP,
                                                int ms, int c0, int lane, uint8_t* cst) {
   constexpr int RB = run_bytes_of(F), SEG = TN * RB;
+  constexpr bool PAIR = Fmt<F>::bits == 6 && TN % 2 == 0;
   const int r = lane >> 1, half = lane & 1;
   const int m = ms + r;
   const int M = p.rows_a(cx);
   const int cb0 = c0 >> 5;
   const int nb = min(TN, p.ynCB - cb0);  // blocks of this wave inside the padded row (uniform)
   const int glanes = p.ymode == 0 ? 2 : (p.ymode == 1 ? 64 : 2 * p.N);  // lanes of one block
+  // the scale bytes of this lane's blocks, written by the first lane of each
+  // block's lane group (one address per strip, not one per block)
+  const bool first = p.ymode == 0 ? half == 0 : (p.ymode == 1 ? lane == 0 : (lane & (2 * p.N - 1)) == 0);
+  uint8_t* srow = nullptr;
+  if (first && m < M) {
+    const long long gm = p.out_index(cx, m);
+    const long long pix = gm / p.N, n = gm - pix * p.N;
+    const long long blk = p.ymode == 0 ? gm : pix * p.ynPB + (n >> 5);
+    srow = p.ys + blk * p.ynCB + cb0;
+  }
   typedef float v4f __attribute__((ext_vector_type(4)));
-#pragma unroll(LEAN ? 1 : TN)
-  for (int j = 0; j < TN; j++) {
-    if (j >= nb) break;  // uniform
+  // block j: this lane's 16 values scaled and clamped into v; returns the
+  // block's scale byte (already stored)
+  auto block = [&](int j, float (&v)[16]) -> uint32_t {
     float x[16];
 #pragma unroll
     for (int k = 0; k < 4; k++) {
@@ -678,15 +673,31 @@ __device__ __forceinline__ void mx_store_strip(const P& p, const typename P::Ctx
     for (int i = 0; i < 16; i++) a = max(a, __float_as_uint(x[i]) & 0x7fffffffu);
     a = group_max(a, glanes);
     const uint32_t S = scale_byte_from_amax<F>(a);
-    float v[16];
     scale_clamp16<F>(x, S, v);
-    convert_store_half_run<F>(cst + r * SEG + j * RB + half * (RB / 2), v);
-    const bool first = p.ymode == 0 ? half == 0 : (p.ymode == 1 ? lane == 0 : (lane & (2 * p.N - 1)) == 0);
-    if (first && m < M) {
-      const long long gm = p.out_index(cx, m);
-      const long long pix = gm / p.N, n = gm - pix * p.N;
-      const long long blk = p.ymode == 0 ? gm : pix * p.ynPB + (n >> 5);
-      p.ys[blk * p.ynCB + cb0 + j] = (uint8_t)S;
+    if (srow) srow[j] = (uint8_t)S;
+    return S;
+  };
+  uint8_t* const crow = cst + r * SEG + half * (RB / 2);
+  if constexpr (PAIR) {
+#pragma unroll(LEAN ? 1 : TN / 2)
+    for (int j = 0; j < TN; j += 2) {
+      if (j >= nb) break;  // uniform
+      float v0[16], v1[16];
+      const uint32_t S0 = block(j, v0);
+      if (j + 1 < nb) {
+        const uint32_t S1 = block(j + 1, v1);
+        convert_store_two_half_runs6<F>(crow + j * RB, crow + (j + 1) * RB, v0, v1, code_keep(S0), code_keep(S1));
+      } else {
+        convert_store_half_run<F>(crow + j * RB, v0, code_keep(S0));
+      }
+    }
+  } else {
+#pragma unroll(LEAN ? 1 : TN)
+    for (int j = 0; j < TN; j++) {
+      if (j >= nb) break;  // uniform
+      float v[16];
+      const uint32_t S = block(j, v);
+      convert_store_half_run<F>(crow + j * RB, v, code_keep(S));
     }
   }
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the packed codes are in LDS (same wave)
@@ -695,19 +706,29 @@ __device__ __forceinline__ void mx_store_strip(const P& p, const typename P::Ctx
   // run, row and segment start is a multiple of VW)
   constexpr int VW = RB % 16 == 0 ? 16 : 8;
   typedef uint32_t vw_t __attribute__((ext_vector_type(VW / 4)));
-  if (!LEAN && nb == TN) {  // the usual case: all reads first, then all stores
+  if (nb == TN) {  // the usual case: a piece count known at compile time
     constexpr int PR = SEG / VW, IT = (32 * PR + 63) / 64;
-    vw_t val[IT];
+    if constexpr (LEAN) {
 #pragma unroll
-    for (int it = 0; it < IT; it++) {
-      const int d = min(it * 64 + lane, 32 * PR - 1), row = d / PR, off = d - row * PR;
-      val[it] = *reinterpret_cast<const vw_t*>(cst + row * SEG + off * VW);
-    }
+      for (int it = 0; it < IT; it++) {
+        const int d = it * 64 + lane, row = d / PR, off = d - row * PR;
+        if (d < 32 * PR && ms + row < M)
+          *reinterpret_cast<vw_t*>(p.yc + p.out_index(cx, ms + row) * p.yrb + cb0 * RB + off * VW) =
+              *reinterpret_cast<const vw_t*>(cst + row * SEG + off * VW);
+      }
+    } else {  // all reads first, then all stores
+      vw_t val[IT];
 #pragma unroll
-    for (int it = 0; it < IT; it++) {
-      const int d = it * 64 + lane, row = d / PR, off = d - row * PR;
-      if (d < 32 * PR && ms + row < M)
-        *reinterpret_cast<vw_t*>(p.yc + p.out_index(cx, ms + row) * p.yrb + cb0 * RB + off * VW) = val[it];
+      for (int it = 0; it < IT; it++) {
+        const int d = min(it * 64 + lane, 32 * PR - 1), row = d / PR, off = d - row * PR;
+        val[it] = *reinterpret_cast<const vw_t*>(cst + row * SEG + off * VW);
+      }
+#pragma unroll
+      for (int it = 0; it < IT; it++) {
+        const int d = it * 64 + lane, row = d / PR, off = d - row * PR;
+        if (d < 32 * PR && ms + row < M)
+          *reinterpret_cast<vw_t*>(p.yc + p.out_index(cx, ms + row) * p.yrb + cb0 * RB + off * VW) = val[it];
+      }
     }
   } else {
     const int pr = nb * RB / VW;
@@ -1246,7 +1267,9 @@ hipError_t launch_tile_id(int id, int fa, int fb, const P& prob, dim3 grid, hipS
     case 0: return launch_gemm<P, 4, 1, 2, 2, NS, GS, KH>(fa, fb, prob, grid, st);
     case 1: return launch_gemm<P, 2, 2, 2, 2, NS, GS, KH>(fa, fb, prob, grid, st);
     case 2:
-      if constexpr (P::kQuad && KH) return hipErrorInvalidValue;  // not chosen (see launch_tiled)
+      // not chosen (see launch_tiled), so not built
+      if constexpr ((P::kQuad && KH) || !GS || (MxOut<P>::value && std::is_base_of<DgradProb, P>::value))
+        return hipErrorInvalidValue;
       else return launch_gemm<P, 2, 2, 4, 2, NS, GS, KH>(fa, fb, prob, grid, st);
     case 4: return launch_gemm<P, 2, 2, 1, 3, NS, GS, KH>(fa, fb, prob, grid, st);
     case 5:  // 128 x 128 with a 2-deep ring (backward-data with few K-steps per tile)
@@ -1278,8 +1301,17 @@ template <class P>
 hipError_t launch_tiled(int fa, int fb, const P& prob_in, int M, int Ncols, int Z, hipStream_t st,
                         int ksteps = 1 << 30) {
   TileChoice t = choose_tile(M, Ncols, Z);
+  // one scale per row (no grouped scales) needs more registers than the
+  // 256 x 128 tile leaves at two waves per SIMD: 128 x 128 instead
+  bool grouped = false;
+  if constexpr (P::kCanGroup) grouped = prob_in.ga >= 8 && prob_in.gb >= 8;
+  if (!grouped && t.id == 2) t = tile_shape(1);
   if constexpr (std::is_base_of<DgradProb, P>::value) {
     if (t.id == 2 && ksteps <= 12) t = tile_shape(5);
+    // the backward-data problem with the MX epilogue needs more registers
+    // than the 256 x 128 tile leaves at two waves per SIMD (it would spill
+    // to scratch memory): 128 x 128 instead
+    if (MxOut<P>::value && t.id == 2) t = tile_shape(1);
   }
   // four K-blocks per step double the operand registers: the 256 x 128 tile
   // would then exceed the budget of two waves per SIMD
@@ -1293,7 +1325,7 @@ hipError_t launch_tiled(int fa, int fb, const P& prob_in, int M, int Ncols, int 
   if constexpr (P::kCanGroup) {
     // one 64-lane load holds both K-blocks' group scales of a 256-row tile
     // when groups have at least 8 rows
-    if (prob.ga >= 8 && prob.gb >= 8) {
+    if (grouped) {
       if (half_k_blocks(prob.ga, prob.gb, prob.khalf, fa, fb))
         return launch_tile_id<P, true, true>(t.id, fa, fb, prob, grid, st);
       return launch_tile_id<P, true, false>(t.id, fa, fb, prob, grid, st);
@@ -1312,12 +1344,19 @@ inline bool offsets_fit(long long bytes, long long bias) { return bytes + bias <
 // workgroups per compute unit (a partial last wave of workgroups would
 // double the time), while the fp32 partial sums that the slices write and
 // the reduction reads stay below traffic_factor times the operand bytes.
-inline int splitk_slices(long long Ma, long long Nb, long long nkb, long long operand_bytes, int traffic_factor = 2) {
-  TileChoice t = choose_tile(Ma, Nb, 1);
+// grouped: whether the launch will use grouped scales (without them it
+// takes the 128 x 128 tile where choose_tile says 256 x 128).
+inline int splitk_slices(long long Ma, long long Nb, long long nkb, long long operand_bytes, int traffic_factor = 2,
+                         bool grouped = true) {
+  auto pick = [&](long long z) {
+    const TileChoice c = choose_tile(Ma, Nb, z);
+    return (!grouped && c.id == 2) ? tile_shape(1) : c;
+  };
+  TileChoice t = pick(1);
   long long tiles = ceil_div(Ma, t.bm) * ceil_div(Nb, t.bn);
   long long s = 512 / tiles;
   // the launch picks its tile from the slice count too: count with that tile
-  const TileChoice tz = choose_tile(Ma, Nb, s > 0 ? s : 1);
+  const TileChoice tz = pick(s > 0 ? s : 1);
   if (tz.id != t.id) {
     t = tz;
     tiles = ceil_div(Ma, t.bm) * ceil_div(Nb, t.bn);

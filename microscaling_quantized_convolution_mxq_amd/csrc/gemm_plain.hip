@@ -5,7 +5,7 @@
 namespace mq {
 
 int plain_gemm_splits(long long Ma, long long Nb, long long nkb) {
-  return splitk_slices(Ma, Nb, nkb, (Ma + Nb) * nkb * 32);
+  return splitk_slices(Ma, Nb, nkb, (Ma + Nb) * nkb * 32, 2, false);  // per-row scales
 }
 
 hipError_t launch_plain_gemm(int fa, int fb, const uint8_t* ac, const uint8_t* as, const uint8_t* bc,

@@ -71,25 +71,48 @@ __device__ __forceinline__ float inv_scale_from_byte(uint32_t S) {
 }
 
 // The 16 values of half a block run divided by the block's scale 2^(S-127)
-// and clamped to the format's largest finite value (saturation); a block
-// holding a NaN or an infinity (S = 0xFF) gets all-zero codes.
+// and clamped to the format's largest finite value (saturation). A block
+// holding a NaN or an infinity (S = 0xFF) is divided by 1 here and its codes
+// are zeroed at conversion (code_keep(S) as the keep mask): a mask after the
+// conversion instead of a select per value, so no value takes a branch.
 template <int F>
 __device__ __forceinline__ void scale_clamp16(const float (&x)[16], uint32_t S, float (&v)[16]) {
   constexpr float maxv = Fmt<F>::maxv;
   const float inv = inv_scale_from_byte(S == 255u ? 127u : S);
 #pragma unroll
-  for (int i = 0; i < 16; i++) v[i] = S == 255u ? 0.0f : fminf(fmaxf(x[i] * inv, -maxv), maxv);
+  for (int i = 0; i < 16; i++) v[i] = fminf(fmaxf(x[i] * inv, -maxv), maxv);
+}
+
+// Mask of the code words of a block with scale byte S: all-zero codes for a
+// block that holds a NaN or an infinity.
+__device__ __forceinline__ uint32_t code_keep(uint32_t S) { return S == 255u ? 0u : ~0u; }
+
+typedef int v6i __attribute__((ext_vector_type(6)));
+// The 2 x 16 FP6 conversion (output code 2i from a[i], 2i+1 from b[i]). The
+// instruction writes its six result registers while it still reads its
+// operands, so a result register placed on an operand register that is read
+// later corrupts that operand; the compiler does not keep them apart by
+// itself. The empty statement after it takes the result and both operands,
+// so all three are live together and no result register can share an
+// operand register.
+template <int F>
+__device__ __forceinline__ v6i cvt_2xpk16_fp6(const v16f& a, const v16f& b) {
+  v6i p;
+  if constexpr (F == 2) p = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(a, b, 1.0f);
+  else p = __builtin_amdgcn_cvt_scalef32_2xpk16_bf6_f32(a, b, 1.0f);
+  asm volatile("" : "+v"(p) : "v"(a), "v"(b));
+  return p;
 }
 
 // Converts 16 scaled values (|v| <= max normal already) to codes and stores
-// them as half a packed run, with gfx950's conversion instructions: FP8 two
-// codes per instruction, FP4 two codes per byte, FP6 sixteen codes per
-// instruction (its output interleaves the two 16-value operands, so the even
-// values go in the first operand and the odd ones in the second). These
-// instructions round to nearest even, keep the sign of zero and produce the
-// element formats' subnormals.
+// them as half a packed run, each code word ANDed with keep, with gfx950's
+// conversion instructions: FP8 two codes per instruction, FP4 two codes per
+// byte, FP6 sixteen codes per instruction (its output interleaves the two
+// 16-value operands, so the even values go in the first operand and the odd
+// ones in the second). These instructions round to nearest even, keep the
+// sign of zero and produce the element formats' subnormals.
 template <int F>
-__device__ __forceinline__ void convert_store_half_run(uint8_t* dst, const float (&v)[16]) {
+__device__ __forceinline__ void convert_store_half_run(uint8_t* dst, const float (&v)[16], uint32_t keep = ~0u) {
   constexpr int bits = Fmt<F>::bits;
   if constexpr (bits == 8) {
     uint32_t w[4];
@@ -103,7 +126,7 @@ __device__ __forceinline__ void convert_store_half_run(uint8_t* dst, const float
         r = __builtin_amdgcn_cvt_pk_bf8_f32(v[4 * i], v[4 * i + 1], 0, false);
         r = __builtin_amdgcn_cvt_pk_bf8_f32(v[4 * i + 2], v[4 * i + 3], r, true);
       }
-      w[i] = r;
+      w[i] = r & keep;
     }
     *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
   } else if constexpr (bits == 6) {
@@ -113,12 +136,9 @@ __device__ __forceinline__ void convert_store_half_run(uint8_t* dst, const float
       even[i] = v[2 * i]; odd[i] = v[2 * i + 1];
       even[8 + i] = 0.0f; odd[8 + i] = 0.0f;
     }
-    typedef int v6i __attribute__((ext_vector_type(6)));
-    v6i p;
-    if constexpr (F == 2) p = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(even, odd, 1.0f);
-    else p = __builtin_amdgcn_cvt_scalef32_2xpk16_bf6_f32(even, odd, 1.0f);
+    const v6i p = cvt_2xpk16_fp6<F>(even, odd);
     uint32_t* d = reinterpret_cast<uint32_t*>(dst);  // 4-byte aligned: offsets are multiples of 12
-    d[0] = p[0]; d[1] = p[1]; d[2] = p[2];
+    d[0] = p[0] & keep; d[1] = p[1] & keep; d[2] = p[2] & keep;
   } else {
     uint32_t w[2];
 #pragma unroll
@@ -128,10 +148,47 @@ __device__ __forceinline__ void convert_store_half_run(uint8_t* dst, const float
       r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * i + 2], v[8 * i + 3], 1.0f, 1);
       r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * i + 4], v[8 * i + 5], 1.0f, 2);
       r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * i + 6], v[8 * i + 7], 1.0f, 3);
-      w[i] = r;
+      w[i] = r & keep;
     }
     *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
   }
+}
+
+// FP6 only: two half runs (v0 to dst0, v1 to dst1) from one conversion
+// instruction, whose 32 outputs are v0's 16 codes then v1's.
+template <int F>
+__device__ __forceinline__ void convert_store_two_half_runs6(uint8_t* dst0, uint8_t* dst1, const float (&v0)[16],
+                                                             const float (&v1)[16], uint32_t keep0, uint32_t keep1) {
+  static_assert(Fmt<F>::bits == 6, "FP6 formats");
+  v16f even, odd;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    even[i] = v0[2 * i]; odd[i] = v0[2 * i + 1];
+    even[8 + i] = v1[2 * i]; odd[8 + i] = v1[2 * i + 1];
+  }
+  const v6i p = cvt_2xpk16_fp6<F>(even, odd);
+  uint32_t* d0 = reinterpret_cast<uint32_t*>(dst0);
+  uint32_t* d1 = reinterpret_cast<uint32_t*>(dst1);
+  d0[0] = p[0] & keep0; d0[1] = p[1] & keep0; d0[2] = p[2] & keep0;
+  d1[0] = p[3] & keep1; d1[1] = p[4] & keep1; d1[2] = p[5] & keep1;
+}
+
+// Maximum over aligned groups of g lanes (g = 2, 4, ..., 64, uniform), every
+// lane of a group receiving it: swaps within quads, mirrors within 8 and 16
+// lanes (DPP), a swizzle across the two 16-lane rows of 32 lanes, and the two
+// wave halves.
+template <int CTRL>
+__device__ __forceinline__ uint32_t max_dpp(uint32_t a) {
+  return max(a, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ uint32_t group_max(uint32_t a, int g) {
+  a = max_dpp<0xB1>(a);                // quad_perm [1,0,3,2]: lane ^ 1
+  if (g >= 4) a = max_dpp<0x4E>(a);    // quad_perm [2,3,0,1]: lane ^ 2
+  if (g >= 8) a = max_dpp<0x141>(a);   // row_half_mirror: 7 - lane within 8
+  if (g >= 16) a = max_dpp<0x140>(a);  // row_mirror: 15 - lane within 16
+  if (g >= 32) a = max(a, (uint32_t)__builtin_amdgcn_ds_swizzle((int)a, 0x401F));  // lane ^ 16 within 32
+  if (g >= 64) a = max((uint32_t)__builtin_amdgcn_readlane((int)a, 0), (uint32_t)__builtin_amdgcn_readlane((int)a, 32));
+  return a;
 }
 
 // Block-scaled MFMA 32x32x64 with E8M0 scales (gfx950 v_mfma_scale_f32_32x32x64_f8f6f4).

@@ -10,6 +10,13 @@
 //   forward:          Y    = Q_k(X')  . Q_k(W_f)^T
 //   backward-data:    G_X' = Q_co(G_Y) . Q_co(W_f), then col2im -> G_X
 //   backward-weight:  G_W  = Q_m(G_Y)^T . Q_m(X')
+// The operands that are quantized along co or m (W_f^T for backward-data,
+// X'^T for backward-weight) keep their rows in tap-major order k' = (kh, kw,
+// ci): a block runs along one row, so the row order leaves every block, and
+// every product, as in the channel-major order, but the products' columns
+// then come out in (kh, kw, ci) order. col2im then reads whole channel runs,
+// W_f^T is a plain transpose of W, and the backward-weight GEMM writes dW in
+// its own [Cout][Kh][Kw][Cin] layout.
 #include "comparator_kernels.h"
 
 namespace mq {
@@ -60,13 +67,13 @@ hipError_t launch_naive_forward(const Conv& cv, const float* x, const float* w, 
   float* wf = reinterpret_cast<float*>(p); p += al(cv.cout * s.K * 4);
   uint8_t* wc = p; p += al(cv.cout * row_bytes(fw, s.K));
   uint8_t* wsc = p;
-  hipLaunchKernelGGL(classic_im2col_kernel<false>, dim3(nblk(s.M * s.K)), dim3(256), 0, st, x, xcol, cv.n, cv.cin,
+  hipLaunchKernelGGL(classic_im2col_kernel, dim3(nblk(s.M * s.K)), dim3(256), 0, st, x, xcol, cv.n, cv.cin,
                      cv.h, cv.w, cv.kh, cv.kw, cv.sh, cv.sw, cv.ph, cv.pw, cv.wo(), s.M, (int)s.K);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if ((e = quantize_rows(xcol, xc, xs, fx, s.M, (int)s.K, st)) != hipSuccess) return e;
-  hipLaunchKernelGGL(flatten_w_kernel<false>, dim3(nblk(cv.cout * s.K)), dim3(256), 0, st, w, wf, cv.cout, cv.cin,
-                     cv.kh, cv.kw);
+  hipLaunchKernelGGL(flatten_w_kernel, dim3(nblk(cv.cout * s.K)), dim3(256), 0, st, w, wf, cv.cout, cv.cin, cv.kh,
+                     cv.kw);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = quantize_rows(wf, wc, wsc, fw, cv.cout, (int)s.K, st)) != hipSuccess) return e;
   return launch_plain_gemm(fx, fw, xc, xs, wc, wsc, (int)s.M, cv.cout, ceil_div(s.K, 32), y, 1, st);
@@ -84,14 +91,15 @@ hipError_t launch_naive_backward_data(const Conv& cv, const float* dy, const flo
   float* gcol = reinterpret_cast<float*>(p);
   hipError_t e;
   if ((e = quantize_rows(dy, gc, gs, fdy, s.M, cv.cout, st)) != hipSuccess) return e;
-  hipLaunchKernelGGL(flatten_w_kernel<true>, dim3(nblk(cv.cout * s.K)), dim3(256), 0, st, w, wft, cv.cout, cv.cin,
-                     cv.kh, cv.kw);
+  // W_f^T with tap-major rows: W viewed as [Cout][(kh, kw, ci)], transposed
+  hipLaunchKernelGGL(transpose_f32_kernel, dim3((unsigned)ceil_div(cv.cout, 32), (unsigned)ceil_div(s.K, 32)),
+                     dim3(256), 0, st, w, wft, (long long)cv.cout, (int)s.K);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = quantize_rows(wft, wc, wsc, fw, s.K, cv.cout, st)) != hipSuccess) return e;
   if ((e = launch_plain_gemm(fdy, fw, gc, gs, wc, wsc, (int)s.M, (int)s.K, ceil_div(cv.cout, 32), gcol, 1, st)) !=
       hipSuccess)
     return e;
-  hipLaunchKernelGGL(col2im_kernel, dim3(nblk((long long)cv.h * cv.w * cv.n * cv.cin)), dim3(256), 0, st, gcol, dx,
+  hipLaunchKernelGGL(col2im_kernel<true>, dim3(nblk((long long)cv.h * cv.w * cv.n * cv.cin)), dim3(256), 0, st, gcol, dx,
                      cv.n, cv.cin, cv.h, cv.w, cv.kh, cv.kw, cv.sh, cv.sw, cv.ph, cv.pw, cv.ho(), cv.wo());
   return hipGetLastError();
 }
@@ -114,13 +122,15 @@ hipError_t launch_naive_backward_weight(const Conv& cv, const float* dy, const f
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if ((e = quantize_rows(gt, gc, gs, fdy, cv.cout, (int)s.M, st)) != hipSuccess) return e;
-  hipLaunchKernelGGL(classic_im2col_kernel<true>, dim3(nblk(s.M * s.K)), dim3(256), 0, st, x, xt, cv.n, cv.cin, cv.h,
-                     cv.w, cv.kh, cv.kw, cv.sh, cv.sw, cv.ph, cv.pw, cv.wo(), s.M, (int)s.K);
+  hipLaunchKernelGGL(classic_im2col_t_kernel,
+                     dim3((unsigned)ceil_div(s.M, 32), (unsigned)ceil_div(cv.cin, 32), (unsigned)(cv.kh * cv.kw)),
+                     dim3(256), 0, st, x, xt, cv.n, cv.cin, cv.h, cv.w, cv.kw, cv.sh, cv.sw, cv.ph, cv.pw, cv.wo(), s.M);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = quantize_rows(xt, xc, xs, fx, s.K, (int)s.M, st)) != hipSuccess) return e;
+  // the GEMM's columns are tap-major: its output is dW's own layout
+  if (S == 1) return launch_plain_gemm(fdy, fx, gc, gs, xc, xs, cv.cout, (int)s.K, nmb, dw, 1, st);
   if ((e = launch_plain_gemm(fdy, fx, gc, gs, xc, xs, cv.cout, (int)s.K, nmb, part, S, st)) != hipSuccess) return e;
-  hipLaunchKernelGGL(wgrad_reduce_permute_kernel, dim3(nblk(cv.cout * s.K)), dim3(256), 0, st, part, dw, cv.cout,
-                     cv.cin, cv.kh, cv.kw, S);
+  hipLaunchKernelGGL(sum_slices_kernel, dim3(nblk(cv.cout * s.K)), dim3(256), 0, st, part, dw, cv.cout * s.K, S);
   return hipGetLastError();
 }
 

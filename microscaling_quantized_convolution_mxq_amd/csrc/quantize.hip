@@ -67,7 +67,8 @@ __device__ __forceinline__ void philox4x32_10(uint32_t c0, uint32_t c1, uint32_t
 // `row`, c0 a multiple of 16), divided by the block scale 2^(S - 127) and
 // rounded stochastically onto the element grid; the results are grid points
 // (or +-max), which the round-to-nearest conversions then encode exactly. A
-// block holding a NaN or an infinity (S = 0xFF) gets all-zero codes.
+// block holding a NaN or an infinity (S = 0xFF) is divided by 1 here and its
+// codes are zeroed at conversion (code_keep).
 template <int F>
 __device__ __forceinline__ void sr_scale16(const float (&x)[16], uint32_t S, uint32_t row, int c0, uint32_t k0,
                                            uint32_t k1, float (&v)[16]) {
@@ -93,7 +94,7 @@ __device__ __forceinline__ void sr_scale16(const float (&x)[16], uint32_t S, uin
     const uint32_t thr = (uint32_t)floorf((u - fl) * 4294967296.0f);
     float r = (fl + (rw[i] < thr ? 1.0f : 0.0f)) * __uint_as_float((uint32_t)(127 + e) << 23);
     r = fminf(r, T::maxv);
-    v[i] = S == 255u ? 0.0f : copysignf(r, t);
+    v[i] = copysignf(r, t);  // a block with S = 0xFF is zeroed at conversion
   }
 }
 
@@ -172,24 +173,16 @@ __device__ __forceinline__ void quantize_tiles(const float* __restrict__ src, ui
     for (int i = 0; i < 16; i++) m = max(m, __float_as_uint(x[i]) & 0x7fffffffu);
     // block max: the lane pair (a line of 32 channels), the whole wave
     // (32 partner rows) or the 2P lanes of one pixel
-    m = max(m, (uint32_t)__shfl_xor((int)m, 1));
-    if constexpr (MODE == 1) {
-#pragma unroll
-      for (int o = 2; o < 64; o <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
-    } else if constexpr (MODE == 2) {
-#pragma unroll
-      for (int o = 2; o < 32; o <<= 1)
-        if (o < 2 * P) m = max(m, (uint32_t)__shfl_xor((int)m, o));
-    }
+    m = group_max(m, MODE == 0 ? 2 : (MODE == 1 ? 64 : 2 * P));
     const uint32_t S = scale_byte_from_amax<F>(m);
     float v[16];
     if constexpr (SR) sr_scale16<F>(x, S, (uint32_t)row, c0, k0, k1, v);
     else scale_clamp16<F>(x, S, v);
     if constexpr (ST) {
-      convert_store_half_run<F>(&stage[r * row_bytes + cb * RB + half * (RB / 2)], v);
+      convert_store_half_run<F>(&stage[r * row_bytes + cb * RB + half * (RB / 2)], v, code_keep(S));
       if (row_ok && writes_scale) scales[sidx + cb] = (uint8_t)S;
     } else if (row_ok) {
-      convert_store_half_run<F>(codes + row * row_bytes + (long long)cb * RB + half * (RB / 2), v);
+      convert_store_half_run<F>(codes + row * row_bytes + (long long)cb * RB + half * (RB / 2), v, code_keep(S));
       if (writes_scale) scales[sidx + cb] = (uint8_t)S;
     }
   }
