@@ -128,9 +128,15 @@ typedef enum {
   MQ_ERR_HIP = -7          /* a HIP launch or runtime call failed */
 } mq_status;
 
-typedef enum { MQ_E4M3 = 0, MQ_E5M2 = 1, MQ_E2M3 = 2, MQ_E3M2 = 3, MQ_E2M1 = 4 } mq_elem;
+/* Element formats and tensor roles. mq_elem and mq_role are plain 32-bit
+ * integers holding one of these constants, so that any value a caller passes
+ * is representable and can be checked (an out-of-range value is rejected
+ * with MQ_ERR_FORMAT, or a size of 0 from the size queries). */
+enum { MQ_E4M3 = 0, MQ_E5M2 = 1, MQ_E2M3 = 2, MQ_E3M2 = 3, MQ_E2M1 = 4 };
+typedef int32_t mq_elem;
 
-typedef enum { MQ_ROLE_ACT = 0, MQ_ROLE_WEIGHT = 1, MQ_ROLE_GRAD = 2 } mq_role;
+enum { MQ_ROLE_ACT = 0, MQ_ROLE_WEIGHT = 1, MQ_ROLE_GRAD = 2 };
+typedef int32_t mq_role;
 
 /* Convolution geometry (host struct). All fields >= 1 except pads (>= 0).
  * Supported: kh, kw <= 15; stride <= 8; pad < kernel size; Ho, Wo >= 1;
@@ -154,6 +160,17 @@ int mqconv_abi_version(void);
 
 /* Static English text for a status code; never NULL. */
 const char* mqconv_status_string(int status);
+
+/* Failure injection, for tests of the error paths (callers that must see
+ * how an entry point behaves when a kernel launch fails). After
+ * mqconv_inject_launch_failure(n), n >= 1, the n-th launch check from then
+ * on (each entry point checks after each kernel it enqueues) reports a
+ * launch failure: that entry point returns MQ_ERR_HIP at once, with the
+ * kernels before it enqueued as usual and none after it, so its outputs
+ * are undefined; later calls run normally. n = 0 cancels a pending
+ * injection. Process-wide (one countdown shared by all threads and
+ * devices). Returns MQ_OK, or MQ_ERR_SHAPE for n < 0. */
+int mqconv_inject_launch_failure(int n);
 
 /* Bytes of the packed code / scale buffers of a tensor with the given role
  * and dims (layouts above). 0 for invalid arguments. Host-only, no HIP call. */

@@ -14,7 +14,9 @@ import os
 from typing import Optional, Sequence, Tuple, Union
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmqconv.so")
+# MQCONV_LIB names another build of the same library (the host-sanitizer
+# build of the tests); there is no fallback if it is missing
+LIB_PATH = os.environ.get("MQCONV_LIB") or os.path.join(_HERE, "libmqconv.so")
 
 MQ_OK = 0
 MQ_ERR_SHAPE = -2
@@ -59,6 +61,7 @@ def lib() -> ctypes.CDLL:
         sig = {
             "mqconv_abi_version": (I, []),
             "mqconv_status_string": (ctypes.c_char_p, [I]),
+            "mqconv_inject_launch_failure": (I, [I]),
             "mqconv_codes_bytes": (S, [I, I, I32, I32, I32, I32]),
             "mqconv_scales_bytes": (S, [I, I32, I32, I32, I32, I32]),
             "mqconv_im2col_codes_bytes": (S, [CV, I]),
@@ -97,7 +100,7 @@ def lib() -> ctypes.CDLL:
     return _lib
 
 
-EXPORTED = ("mqconv_abi_version", "mqconv_status_string", "mqconv_codes_bytes", "mqconv_scales_bytes",
+EXPORTED = ("mqconv_abi_version", "mqconv_status_string", "mqconv_inject_launch_failure", "mqconv_codes_bytes", "mqconv_scales_bytes",
             "mqconv_im2col_codes_bytes", "mqconv_im2col_scales_bytes", "mqconv_quantize", "mqconv_quantize_group",
             "mqconv_quantize_sr",
             "mqconv_cbf_im2col", "mqconv_workspace_bytes", "mqconv_forward", "mqconv_forward_mx", "mqconv_backward_data",
@@ -219,6 +222,12 @@ class MxTensor:
 
 def mqconv_abi_version() -> int:
     return lib().mqconv_abi_version()
+
+
+def mqconv_inject_launch_failure(n: int) -> None:
+    """The n-th launch check from now reports a launch failure (n = 0: none);
+    for tests of the error paths."""
+    _check(lib().mqconv_inject_launch_failure(int(n)), "mqconv_inject_launch_failure")
 
 
 def mqconv_status_string(status: int) -> str:

@@ -172,7 +172,7 @@ hipError_t launch_cuyckens_im2col_quantize(const Conv& cv, const float* x, int f
     default: MQ_SQ(4); break;
   }
 #undef MQ_SQ
-  return hipGetLastError();
+  return launch_check();
 }
 
 // W_f [Cout][K] quantized in squares into (codes, scales) of the workspace.
@@ -181,7 +181,7 @@ static hipError_t square_weight(const Conv& cv, const float* w, int fw, float* w
   const SqSizes s = sq_sizes(cv);
   hipLaunchKernelGGL(flatten_w_kernel, dim3(nblk(cv.cout * s.K)), dim3(256), 0, st, w, wf, cv.cout, cv.cin,
                      cv.kh, cv.kw);
-  const hipError_t e = hipGetLastError();
+  const hipError_t e = launch_check();
   if (e != hipSuccess) return e;
   return launch_quantize(wf, wc, wsc, fw, 32, 1, cv.cout, 1, (int)s.K, st);
 }
@@ -223,7 +223,7 @@ hipError_t launch_cuyckens_backward_data(const Conv& cv, const float* dy, const 
   if ((e = square_gemm(a, b, s.nCoB, gcol, 1, st)) != hipSuccess) return e;
   hipLaunchKernelGGL(col2im_kernel<false>, dim3(nblk((long long)cv.h * cv.w * cv.n * cv.cin)), dim3(256), 0, st, gcol, dx,
                      cv.n, cv.cin, cv.h, cv.w, cv.kh, cv.kw, cv.sh, cv.sw, cv.ph, cv.pw, cv.ho(), cv.wo());
-  return hipGetLastError();
+  return launch_check();
 }
 
 hipError_t launch_cuyckens_backward_weight(const Conv& cv, const float* dy, const uint8_t* col_codes,
@@ -247,7 +247,7 @@ hipError_t launch_cuyckens_backward_weight(const Conv& cv, const float* dy, cons
   if ((e = square_gemm(a, b, s.nMB, part, S, st)) != hipSuccess) return e;
   hipLaunchKernelGGL(wgrad_reduce_permute_kernel, dim3(nblk(cv.cout * s.K)), dim3(256), 0, st, part, dw, cv.cout,
                      cv.cin, cv.kh, cv.kw, S);
-  return hipGetLastError();
+  return launch_check();
 }
 
 }  // namespace mq

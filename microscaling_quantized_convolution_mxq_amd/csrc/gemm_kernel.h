@@ -1202,7 +1202,7 @@ hipError_t launch_gemm(int fa, int fb, const P& prob, dim3 grid, hipStream_t st)
   if (fa == A && fb == B) {                                                                             \
     hipLaunchKernelGGL((mx_gemm_kernel<A, B, P, WM, WN, TM, TN, NS, GS, KH, KPS, NG>), grid, dim3(256 * NG), 0, \
                        st, prob);                                                                       \
-    return hipGetLastError();                                                                           \
+    return launch_check();                                                                           \
   }
   if constexpr (KH || (P::kKMajA && P::kKMajB)) {
     MQ_CASE(0, 0) MQ_CASE(0, 1) MQ_CASE(1, 0) MQ_CASE(1, 1)

@@ -249,7 +249,7 @@ hipError_t launch_backward_weight(const Conv& cv, MxView dy, MxView x, float* dw
       hipLaunchKernelGGL(splitk_reduce_kernel<false>, dim3((unsigned)ceil_div(n, C)), dim3(256), 0, st,
                          part, dw, n, S);
     }
-    e = hipGetLastError();
+    e = launch_check();
   }
   return e;
 }

@@ -104,7 +104,7 @@ hipError_t launch_cbf_im2col(const Conv& cv, MxView x, uint8_t* col_codes, uint8
     hipLaunchKernelGGL(cbf_im2col_kernel<8>, grid, dim3(256), 0, st, x.codes, x.scales, col_codes,
                        col_scales, cv.n, cv.h, cv.w, cv.sh, cv.sw, cv.ph, cv.pw, T, cpr, nsb, dtc, dc, dkw,
                        dnsb, dwo);
-  return hipGetLastError();
+  return launch_check();
 }
 
 // ----------------------------------------------------------------------------
@@ -256,7 +256,7 @@ hipError_t launch_transpose_codes(const uint8_t* in, uint8_t* out, int fmt, bool
     const long long ntiles = (long long)A * B * nPB * nCC;
     hipLaunchKernelGGL(transpose_codes8_kernel, dim3((unsigned)((ntiles + 3) / 4)), dim3(256), 0, st, in, out,
                        P, B, C, nPB, nCC, ntiles, half ? 16 : 32);
-    return hipGetLastError();
+    return launch_check();
   }
   const int nPB = ceil_div(P, 32);
   const long long blocks = (long long)A * B * nPB;
@@ -270,7 +270,7 @@ hipError_t launch_transpose_codes(const uint8_t* in, uint8_t* out, int fmt, bool
     default:
       hipLaunchKernelGGL(transpose_codes_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, st, in, out, P, B, C, nPB);
   }
-  return hipGetLastError();
+  return launch_check();
 }
 
 }  // namespace mq

@@ -8,6 +8,7 @@
 
 #include <limits.h>
 
+#include <atomic>
 #include <mutex>
 
 using namespace mq;
@@ -78,7 +79,18 @@ MxView view(const mq_mx& t) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MQ_OK : MQ_ERR_HIP; }
 
+// launch checks until the injected failure (0: none pending)
+std::atomic<int> g_fail_countdown{0};
+
 }  // namespace
+
+hipError_t mq::launch_check() {
+  const hipError_t e = hipGetLastError();
+  int c = g_fail_countdown.load(std::memory_order_relaxed);
+  while (c > 0 && !g_fail_countdown.compare_exchange_weak(c, c - 1, std::memory_order_relaxed)) {
+  }
+  return c == 1 ? hipErrorLaunchFailure : e;
+}
 
 // ---------------------------------------------------------------------------
 // Backward-weight without any allocation: the scratch space (re-laid codes,
@@ -111,6 +123,12 @@ void* scratch_for_current_device() {
 extern "C" {
 
 int mqconv_abi_version(void) { return MQCONV_ABI_VERSION; }
+
+int mqconv_inject_launch_failure(int n) {
+  if (n < 0) return MQ_ERR_SHAPE;
+  g_fail_countdown.store(n, std::memory_order_relaxed);
+  return MQ_OK;
+}
 
 const char* mqconv_status_string(int status) {
   switch (status) {

@@ -66,6 +66,11 @@ struct QReq {
 };
 hipError_t launch_quantize_group(const QReq* reqs, int count, hipStream_t st);
 
+// Status of the kernel launches enqueued so far (hipGetLastError), or a
+// launch failure when a failure injected for the tests of the error paths
+// (mqconv_inject_launch_failure) falls due at this check.
+hipError_t launch_check();
+
 hipError_t launch_cbf_im2col(const Conv& cv, MxView x, uint8_t* col_codes, uint8_t* col_scales,
                              hipStream_t st);
 

@@ -69,12 +69,12 @@ hipError_t launch_naive_forward(const Conv& cv, const float* x, const float* w, 
   uint8_t* wsc = p;
   hipLaunchKernelGGL(classic_im2col_kernel, dim3(nblk(s.M * s.K)), dim3(256), 0, st, x, xcol, cv.n, cv.cin,
                      cv.h, cv.w, cv.kh, cv.kw, cv.sh, cv.sw, cv.ph, cv.pw, cv.wo(), s.M, (int)s.K);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_check();
   if (e != hipSuccess) return e;
   if ((e = quantize_rows(xcol, xc, xs, fx, s.M, (int)s.K, st)) != hipSuccess) return e;
   hipLaunchKernelGGL(flatten_w_kernel, dim3(nblk(cv.cout * s.K)), dim3(256), 0, st, w, wf, cv.cout, cv.cin, cv.kh,
                      cv.kw);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launch_check()) != hipSuccess) return e;
   if ((e = quantize_rows(wf, wc, wsc, fw, cv.cout, (int)s.K, st)) != hipSuccess) return e;
   return launch_plain_gemm(fx, fw, xc, xs, wc, wsc, (int)s.M, cv.cout, ceil_div(s.K, 32), y, 1, st);
 }
@@ -94,14 +94,14 @@ hipError_t launch_naive_backward_data(const Conv& cv, const float* dy, const flo
   // W_f^T with tap-major rows: W viewed as [Cout][(kh, kw, ci)], transposed
   hipLaunchKernelGGL(transpose_f32_kernel, dim3((unsigned)ceil_div(cv.cout, 32), (unsigned)ceil_div(s.K, 32)),
                      dim3(256), 0, st, w, wft, (long long)cv.cout, (int)s.K);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launch_check()) != hipSuccess) return e;
   if ((e = quantize_rows(wft, wc, wsc, fw, s.K, cv.cout, st)) != hipSuccess) return e;
   if ((e = launch_plain_gemm(fdy, fw, gc, gs, wc, wsc, (int)s.M, (int)s.K, ceil_div(cv.cout, 32), gcol, 1, st)) !=
       hipSuccess)
     return e;
   hipLaunchKernelGGL(col2im_kernel<true>, dim3(nblk((long long)cv.h * cv.w * cv.n * cv.cin)), dim3(256), 0, st, gcol, dx,
                      cv.n, cv.cin, cv.h, cv.w, cv.kh, cv.kw, cv.sh, cv.sw, cv.ph, cv.pw, cv.ho(), cv.wo());
-  return hipGetLastError();
+  return launch_check();
 }
 
 hipError_t launch_naive_backward_weight(const Conv& cv, const float* dy, const float* x, int fdy, int fx, float* dw,
@@ -119,19 +119,19 @@ hipError_t launch_naive_backward_weight(const Conv& cv, const float* dy, const f
   float* part = reinterpret_cast<float*>(p);
   hipLaunchKernelGGL(transpose_f32_kernel, dim3((unsigned)ceil_div(s.M, 32), (unsigned)ceil_div(cv.cout, 32)), dim3(256),
                      0, st, dy, gt, s.M, cv.cout);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_check();
   if (e != hipSuccess) return e;
   if ((e = quantize_rows(gt, gc, gs, fdy, cv.cout, (int)s.M, st)) != hipSuccess) return e;
   hipLaunchKernelGGL(classic_im2col_t_kernel,
                      dim3((unsigned)ceil_div(s.M, 32), (unsigned)ceil_div(cv.cin, 32), (unsigned)(cv.kh * cv.kw)),
                      dim3(256), 0, st, x, xt, cv.n, cv.cin, cv.h, cv.w, cv.kw, cv.sh, cv.sw, cv.ph, cv.pw, cv.wo(), s.M);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launch_check()) != hipSuccess) return e;
   if ((e = quantize_rows(xt, xc, xs, fx, s.K, (int)s.M, st)) != hipSuccess) return e;
   // the GEMM's columns are tap-major: its output is dW's own layout
   if (S == 1) return launch_plain_gemm(fdy, fx, gc, gs, xc, xs, cv.cout, (int)s.K, nmb, dw, 1, st);
   if ((e = launch_plain_gemm(fdy, fx, gc, gs, xc, xs, cv.cout, (int)s.K, nmb, part, S, st)) != hipSuccess) return e;
   hipLaunchKernelGGL(sum_slices_kernel, dim3(nblk(cv.cout * s.K)), dim3(256), 0, st, part, dw, cv.cout * s.K, S);
-  return hipGetLastError();
+  return launch_check();
 }
 
 }  // namespace mq

@@ -114,7 +114,7 @@ hipError_t launch_nvfp_quantize(const float* src, uint8_t* codes, uint8_t* bscal
   const long long n = (long long)A * P * B * C;
   const int nparts = (int)std::min<long long>(kNvfpParts, std::max<long long>(1, (n + 4095) / 4096));
   hipLaunchKernelGGL(nvfp_amax_kernel, dim3(nparts), dim3(256), 0, st, src, n, partial);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_check();
   if (e != hipSuccess) return e;
   const long long ntiles = (long long)A * B * ((P + 31) / 32);
   const dim3 grid((unsigned)((ntiles + 3) / 4));
@@ -129,7 +129,7 @@ hipError_t launch_nvfp_quantize(const float* src, uint8_t* codes, uint8_t* bscal
     default: MQ_NV(4); break;
   }
 #undef MQ_NV
-  return hipGetLastError();
+  return launch_check();
 }
 
 }  // namespace mq

@@ -287,7 +287,7 @@ static hipError_t launch_f(const QReq& r, uint64_t seed, hipStream_t st) {
     case 4: launch_one<F, 2, false, SR>(r, q, seed, st); break;
     default: launch_one<F, 2, true, SR>(r, q, seed, st); break;
   }
-  return hipGetLastError();
+  return launch_check();
 }
 
 template <bool SR>
@@ -353,7 +353,7 @@ hipError_t launch_quantize_group(const QReq* reqs, int count, hipStream_t st) {
         case 3: hipLaunchKernelGGL(mxq_quantize_group_kernel<3>, dim3((unsigned)total), dim3(256), 0, st, g); break;
         default: hipLaunchKernelGGL(mxq_quantize_group_kernel<4>, dim3((unsigned)total), dim3(256), 0, st, g); break;
       }
-      const hipError_t e = hipGetLastError();
+      const hipError_t e = launch_check();
       if (e != hipSuccess) return e;
     }
   }

@@ -156,6 +156,50 @@ def _source_sha() -> str:
     return h.hexdigest()[:16]
 
 
+def _run_bytes(fmt: int) -> int:
+    return 32 if fmt <= 1 else (24 if fmt <= 3 else 16)
+
+
+def model_bytes(wl) -> dict:
+    """Full-kernel byte model of one training step of one layer: every kernel
+    reads each of its inputs once and writes each output once (fp32: 4 B per
+    element; MX: packed codes of whole 32-channel runs plus one scale byte per
+    block), no re-reads, no split-K partial sums, no caches.
+      quantize-once: quantize X, W, dY (fp32 in, codes out); forward (X_q,
+        W_q in, fp32 Y out); backward-data (dY_q, W_q in, fp32 dX out);
+        backward-weight (dY_q, X_q in, fp32 dW out).
+      naive: per GEMM, its fp32 operands are laid out along that GEMM's
+        contraction (classic im2col of X, flattening or transposing W and
+        dY: fp32 in, fp32 out), then quantized in line blocks along it;
+        the GEMM reads both and writes fp32 (backward-data: G_X', then
+        col2im folds it into dX)."""
+    s = wl.shape
+    ho, wo = s.ho, s.wo
+    X, Wn, G = s.h * s.w * s.n * s.cin, s.cout * s.kh * s.kw * s.cin, ho * wo * s.n * s.cout
+    M, K = ho * wo * s.n, s.cin * s.kh * s.kw
+    cdiv = lambda a, b: -(-a // b)
+
+    def mx(rows, chans, partner_rows, fmt, bp):  # CBF tensor: rows x chans codes, blocks over partner_rows
+        nb = cdiv(chans, 32)
+        return rows * nb * _run_bytes(fmt) + cdiv(partner_rows, bp) * (rows // partner_rows) * nb
+
+    def lines(R, L, fmt):  # R rows quantized in line blocks of 32 along L
+        nb = cdiv(L, 32)
+        return R * nb * _run_bytes(fmt) + R * nb
+
+    xq = mx(s.h * s.w * s.n, s.cin, s.n, wl.fx, wl.bp)
+    wq = mx(s.cout * s.kh * s.kw, s.cin, s.cout, wl.fw, wl.bp)
+    gq = mx(ho * wo * s.n, s.cout, s.n, wl.fdy, wl.bp)
+    once = (4 * (X + Wn + G) + xq + wq + gq) + (xq + wq + 4 * G) + (gq + wq + 4 * X) + (gq + xq + 4 * Wn)
+    fwd = (4 * X + 4 * M * K) + (4 * M * K + lines(M, K, wl.fx)) + 8 * Wn + (4 * Wn + lines(s.cout, K, wl.fw)) \
+        + (lines(M, K, wl.fx) + lines(s.cout, K, wl.fw) + 4 * G)
+    dgrad = (4 * G + lines(M, s.cout, wl.fdy)) + 8 * Wn + (4 * Wn + lines(K, s.cout, wl.fw)) \
+        + (lines(M, s.cout, wl.fdy) + lines(K, s.cout, wl.fw) + 4 * M * K) + (4 * M * K + 4 * X)
+    wgrad = 8 * G + (4 * G + lines(s.cout, M, wl.fdy)) + (4 * X + 4 * M * K) + (4 * M * K + lines(K, M, wl.fx)) \
+        + (lines(s.cout, M, wl.fdy) + lines(K, M, wl.fx) + 4 * Wn)
+    return {"microqonv": float(once), "naive": float(fwd + dgrad + wgrad)}
+
+
 def summarize(d: str, workload: str, out_dir: str) -> dict:
     copy_bytes = COPY_MB * (1 << 20)
     cf = [v for k, v in _read(d, "copy_fetch", "FETCH_SIZE") if "mq::" not in k]
@@ -191,6 +235,16 @@ def summarize(d: str, workload: str, out_dir: str) -> dict:
     m, n = res["paths"]["microqonv"]["total_bytes"], res["paths"]["naive"]["total_bytes"]
     res["naive_over_microqonv"] = round(n / m, 3)
     lines.append(f"naive / quantize-once bytes: x{n / m:.2f}")
+    mod = {"microqonv": 0.0, "naive": 0.0}
+    for wl in _workloads(workload):
+        for k, v in model_bytes(wl).items():
+            mod[k] += v
+    res["model_bytes"] = mod
+    res["model_naive_over_microqonv"] = round(mod["naive"] / mod["microqonv"], 3)
+    lines.append("full-kernel model (each kernel's inputs read once, outputs written once): "
+                 f"quantize-once {mod['microqonv'] / 1e6:.1f} MB, naive {mod['naive'] / 1e6:.1f} MB, "
+                 f"x{mod['naive'] / mod['microqonv']:.2f}")
+    lines.append(f"measured / model: quantize-once x{m / mod['microqonv']:.2f}, naive x{n / mod['naive']:.2f}")
     text = "\n".join(lines)
     os.makedirs(out_dir, exist_ok=True)
     with open(os.path.join(out_dir, f"bytes_{workload}.json"), "w") as fh:

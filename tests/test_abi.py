@@ -26,13 +26,20 @@ def _declared():
 
 def test_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 31
+    assert len(names) == 32
     out = subprocess.run(["nm", "-D", "--defined-only", mq.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT\s+(mqconv_\w+)", out))
     assert set(names) <= exported
     assert set(mq.EXPORTED) == set(names)
     for n in names:
         assert getattr(mq.lib(), n) is not None
+
+
+def test_launch_failure_injection_arguments():
+    # only sets a countdown (no GPU call): n < 0 is rejected, 0 cancels
+    assert mq.lib().mqconv_inject_launch_failure(-1) == mq.MQ_ERR_SHAPE
+    assert mq.lib().mqconv_inject_launch_failure(3) == mq.MQ_OK
+    assert mq.lib().mqconv_inject_launch_failure(0) == mq.MQ_OK
 
 
 def test_version_and_status_strings():
