@@ -306,7 +306,7 @@ def summarize_mfma(d: str, stem: str, workload: str, out_dir: str, command: str)
     flops = sum(wl.shape.flops() for wl in wls)
     lines = [f"MFMA counters of one training step, workload {workload} ({len(wls)} layer(s)); "
              f"algorithmic FLOP per GEMM kind {flops / 1e9:.2f} G", "", "Command (run from the repository root on one MI355X):",
-             "  " + command, "",
+             "  " + command, f"Library source hash: {_source_sha()}", "",
              f"{'kernel':74s} {'calls':>5s} {'cycles':>9s} {'MFMA busy':>9s} {'exec GFLOP':>10s}"]
     agg = {}
     for (_, name), c in per.items():
