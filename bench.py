@@ -2,7 +2,8 @@
 
 One step = one pass of every step of the path over one batch of synthetic
 input: quantize X and W (one grouped call, as before a layer's forward
-pass) and G_Y once (MX, E8M0 scales), channel-batch-first
+pass; one launch when they share an element format) and G_Y once (MX, E8M0
+scales, round-to-nearest), channel-batch-first
 im2col of the quantized activation, then the forward, backward-data and
 backward-weight block-scaled GEMMs. Inputs are resident in HBM before the
 timed region; R copies of every buffer are rotated so the live set exceeds
@@ -15,10 +16,15 @@ time). Every entry point is also timed on its own (a graph of repeated
 calls on rotating buffer sets, HIP events on the stream the kernels run
 on); `roofline` covers the entry point that takes the most time per step,
 with its algorithmic bytes or FLOPs per call. The forward whose epilogue
-writes Y as MX codes (`mqconv_forward_mx`) and the backward-data whose
-epilogue writes dX as MX codes (`mqconv_backward_data_mx`) are timed the same
-way and listed with `in_step: false`. `cpu_baseline` times the CPU
-oracle on a bounded sample of the same workload.
+writes Y as MX codes (`mqconv_forward_mx`), the backward-data whose
+epilogue writes dX as MX codes (`mqconv_backward_data_mx`), the gradient
+quantized with stochastic rounding (`mqconv_quantize_sr`) and the
+backward-weight without allocation (`mqconv_backward_weight_noalloc`) are
+timed the same way and listed with `in_step: false`. `roofline.traffic` is
+taken from the committed counter summary of that entry point when its
+source hash matches the kernels. `cpu_baseline` times the CPU oracle on a
+bounded sample of the same workload. The default workload is the stride-2
+MXFP6 layer (N=32, 128 -> 256 channels, 160x160), the largest one.
 
 Prints one JSON line.
 """
