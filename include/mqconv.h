@@ -293,7 +293,7 @@ int mqconv_backward_weight(const mq_conv* cv, mq_mx dyq, mq_mx xq, float* dw, vo
  *   Every call on one device uses that device's one array: calls that
  *   overlap in time on one device (two streams, two host threads) race and
  *   give undefined results; calls ordered on one stream are safe. */
-#define MQ_NOALLOC_SCRATCH_BYTES (160u << 20)
+#define MQ_NOALLOC_SCRATCH_BYTES (96u << 20)
 int mqconv_backward_weight_noalloc(const mq_conv* cv, mq_mx dyq, mq_mx xq, float* dw, void* stream);
 
 /* ---------------------------------------------------------------------------

@@ -331,7 +331,7 @@ def mqconv_backward_weight(shape, dyq: MxTensor, xq: MxTensor, dw, ws=None, stre
 
 
 # scratch bytes the library holds per device for mqconv_backward_weight_noalloc
-NOALLOC_SCRATCH_BYTES = 160 << 20
+NOALLOC_SCRATCH_BYTES = 96 << 20
 
 
 def mqconv_backward_weight_noalloc(shape, dyq: MxTensor, xq: MxTensor, dw, stream=None) -> None:

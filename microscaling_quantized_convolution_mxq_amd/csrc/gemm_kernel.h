@@ -144,6 +144,11 @@ template <class P, class = void>
 struct MxOut : std::false_type {};
 template <class P>
 struct MxOut<P, std::void_t<decltype(P::kMxOut)>> : std::bool_constant<P::kMxOut> {};
+// problems whose K-major B operand holds 6- or 4-bit codes (kSubB)
+template <class P, class = void>
+struct SubB : std::false_type {};
+template <class P>
+struct SubB<P, std::void_t<decltype(P::kSubB)>> : std::bool_constant<P::kSubB> {};
 
 // Backward-data: rows of parity class z are h = hq*sh + ph_c, w = wq*sw + pw_c
 // (and all n); the taps reaching them are kh = kh0 + sh*ih, kw = kw0 + sw*iw,
@@ -409,6 +414,7 @@ struct DgradNatProb : DgradProb {
 // pixel; lines past N, when N < 32, read zeros).
 struct WgradNatProb : WgradProb {
   int dyrb, xrb;
+  int xbits;  // bits per activation code (8; 6 or 4 in WgradNatSubProb)
   static constexpr bool kKMajA = true, kKMajB = true;
   __device__ int kext_a() const { return N < 32 ? N : 32; }
   __device__ int kext_b() const { return N < 32 ? N : 32; }
@@ -434,12 +440,22 @@ struct WgradNatProb : WgradProb {
     const int kh = (int)fdiv((unsigned)tap, dKW), kw = tap - kh * KW;
     r.p0 = kh - ph; r.p1 = kw - pw;
     const int p = r.p0 * W + r.p1;
-    r.code = p * N * xrb + ci + xtcb; r.scale = p * nNB * ncbi + ci / 32 + xsb; return r;
+    r.code = p * N * xrb + ((ci * xbits) >> 3) + xtcb; r.scale = p * nNB * ncbi + ci / 32 + xsb; return r;
   }
   __device__ KInfo k_b(const Ctx&, const KS& k) const {
     const int g0 = k.ho * sh, g1 = k.wo * sw, d = g0 * W + g1;
     return KInfo{(d * N + 32 * k.v) * xrb, (d * nNB + k.v) * ncbi, g0, g1};
   }
+};
+
+// Backward-weight reading the 8-bit gradient codes and 6- or 4-bit
+// activation codes both where quantization left them: as WgradNatProb, with
+// the activation's 16-channel chunks (12 or 8 code bytes) staged one per
+// 16-byte LDS slot and read with the 6/4-bit transposing LDS reads
+// (lds_operand_k_sub). Needs Cin % 16 == 0 (chunk offsets ci * bits / 8 stay
+// whole bytes and a chunk stays in one tap); never half K-blocks.
+struct WgradNatSubProb : WgradNatProb {
+  static constexpr bool kSubB = true;
 };
 
 // Backward-weight with the 8-bit gradient codes read where quantization
@@ -575,6 +591,40 @@ __device__ __forceinline__ v8i lds_operand_k(const uint8_t* stage, int r0, int l
     const bool upper = lane >= 32;
 #pragma unroll
     for (int e = 0; e < 8; e++) r[e] = upper ? 0 : r[e];
+  }
+  return r;
+}
+
+// Operand image of rows r0..r0+31 from a K-major stage of 6- or 4-bit codes:
+// the stage is laid out as for 8-bit codes ([kb][k][BR / 16 slots of 16
+// bytes], slots permuted by kswz(k)), but slot c of line k holds the 12
+// (6-bit) or 8 (4-bit) code bytes of the line's 16-row chunk c, copied with
+// the bytes after them. The image is the packed 32-code run of K-block q
+// (dwords 0-5 for 6-bit, 0-3 for 4-bit): lane t of each 16-lane group
+// addresses line 16h + t of K-block q in the slot of the group's rows
+// (16-byte aligned, as ds_read_b96_tr_b6 needs), and
+// ds_read_b96_tr_b6 / ds_read_b64_tr_b4 hand lane t its row's 16 values on
+// those lines, line j at bits [bits*j, bits*(j+1)).
+template <int F, int BR>
+__device__ __forceinline__ v8i lds_operand_k_sub(const uint8_t* stage, int r0, int lane) {
+  static_assert(Fmt<F>::bits == 6 || Fmt<F>::bits == 4, "6- or 4-bit codes");
+  typedef v2i __attribute__((address_space(3)))* lds_v2i_ptr;
+  typedef int v3i_t __attribute__((ext_vector_type(3)));
+  typedef v3i_t __attribute__((address_space(3)))* lds_v3i_ptr;
+  const int g = lane >> 4, t = lane & 15, q = g >> 1;
+  const int chunk = (r0 >> 4) + (g & 1);
+  v8i r = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int h = 0; h < 2; h++) {
+    const int k = 16 * h + t;  // line within K-block q
+    const uint8_t* src = stage + (32 * q + k) * BR + 16 * (chunk ^ kswz(k));
+    if constexpr (Fmt<F>::bits == 6) {
+      const v3i_t x = __builtin_amdgcn_ds_read_tr6_b96_v3i32((lds_v3i_ptr)src);
+      r[3 * h] = x[0]; r[3 * h + 1] = x[1]; r[3 * h + 2] = x[2];
+    } else {
+      const v2i x = __builtin_amdgcn_ds_read_tr4_b64_v2i32((lds_v2i_ptr)src);
+      r[2 * h] = x[0]; r[2 * h + 1] = x[1];
+    }
   }
   return r;
 }
@@ -744,22 +794,27 @@ __device__ __forceinline__ void mx_store_strip(const P& p, const typename P::Ctx
 template <int FA, int FB, class P, int WM, int WN, int TM, int TN, int NS, bool GS, bool KH, int KPS, int NG>
 __global__ __launch_bounds__(256 * NG) __attribute__((amdgpu_waves_per_eu(2))) void mx_gemm_kernel(P prob) {
   static_assert(!KH || (FA <= 1 && FB <= 1), "half K-blocks only for 8-bit codes");
-  // K-major operands (8-bit codes, full runs): the staging order of the
-  // contraction's natural layout, read back with transposing LDS reads
+  // K-major operands (8-bit codes; 6/4-bit B codes without half K-blocks):
+  // the staging order of the contraction's natural layout, read back with
+  // transposing LDS reads
   constexpr bool TA = P::kKMajA, TB = P::kKMajB;
-  static_assert((!TA || FA <= 1) && (!TB || FB <= 1), "K-major staging: 8-bit codes");
+  static_assert(!TA || FA <= 1, "K-major A: 8-bit codes");
+  static_assert(!TB || FB <= 1 || (SubB<P>::value && !KH), "K-major 6/4-bit B: its own problem, full K-blocks");
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
   using OA = Op<FA>;
   using OB = Op<FB>;
   // KPS: K-blocks per step (a pair, or two pairs)
   static_assert(KPS == 2 || KPS == 4, "K-blocks per step");
-  constexpr int A_BYTES = KPS * BM * (KH ? 1 : OA::NPK) * 16, B_BYTES = KPS * BN * (KH ? 1 : OB::NPK) * 16;
+  // 16-byte slots per row (row-major) or per 16-row chunk and 16 lines
+  // (K-major: KL lines of BR bytes per K-block, whatever the code width)
+  constexpr int NPKA = TA ? (KH ? 1 : 2) : (KH ? 1 : OA::NPK), NPKB = TB ? (KH ? 1 : 2) : (KH ? 1 : OB::NPK);
+  constexpr int A_BYTES = KPS * BM * NPKA * 16, B_BYTES = KPS * BN * NPKB * 16;
   constexpr int SA_BYTES = GS ? 256 : 4 * KPS * BM, SB_BYTES = GS ? 256 : 4 * KPS * BN;
   constexpr int OFF_B = A_BYTES, OFF_SA = OFF_B + B_BYTES, OFF_SB = OFF_SA + SA_BYTES;
   constexpr int STAGE = OFF_SB + SB_BYTES;
   // LDS-writing loads (64 lanes each) per stage and per wave; load g of a
   // kind belongs to K-block g / (loads per K-block)
-  constexpr int NCA = KPS * BM * (KH ? 1 : OA::NPK) / 64, NCB = KPS * BN * (KH ? 1 : OB::NPK) / 64;
+  constexpr int NCA = KPS * BM * NPKA / 64, NCB = KPS * BN * NPKB / 64;
   constexpr int NSA = GS ? 1 : KPS * BM / 64, NSB = GS ? 1 : KPS * BN / 64;
   constexpr int WCA = (NCA + 3) / 4, WCB = (NCB + 3) / 4;
   constexpr int WSA = GS ? 1 : (NSA + 3) / 4, WSB = GS ? 0 : (NSB + 3) / 4;
@@ -859,13 +914,13 @@ __global__ __launch_bounds__(256 * NG) __attribute__((amdgpu_waves_per_eu(2))) v
   for (int k = 0; k < WCA; k++) {
     if constexpr (TA)
       make_lane_k(ca[k], wave + 4 * k, NCA, std::integral_constant<int, BM>{}, std::true_type{}, innerA, prob);
-    else make_lane(ca[k], wave + 4 * k, NCA, BM * (KH ? 1 : OA::NPK), KH ? 1 : OA::NPK, OA::CH, true, true, innerA);
+    else make_lane(ca[k], wave + 4 * k, NCA, BM * NPKA, NPKA, OA::CH, true, true, innerA);
   }
 #pragma unroll
   for (int k = 0; k < WCB; k++) {
     if constexpr (TB)
       make_lane_k(cb[k], wave + 4 * k, NCB, std::integral_constant<int, BN>{}, std::false_type{}, innerB, prob);
-    else make_lane(cb[k], wave + 4 * k, NCB, BN * (KH ? 1 : OB::NPK), KH ? 1 : OB::NPK, OB::CH, true, false, innerB);
+    else make_lane(cb[k], wave + 4 * k, NCB, BN * NPKB, NPKB, OB::CH, true, false, innerB);
   }
   // grouped scales: lane e of wave 0 (A) or wave 1 (B) loads the scale of
   // group e % ngroups of K-block e / ngroups (e < KPS * ngroups <= 64)
@@ -951,14 +1006,14 @@ __global__ __launch_bounds__(256 * NG) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
     for (int k = 0; k < WCA; k++) {
       const int g = wave + 4 * k;
-      const int kbi = (g * 64) / (BM * (KH ? 1 : OA::NPK));
+      const int kbi = (g * 64) / (BM * NPKA);
       dma16(rs[0], g < NCA ? stage + g * 64 * 16 : arena + DUMMY, voff(ca[k], ka, P::kGeoA, inA, la0, la1),
             soff(ka.code, kbi, live, nv));
     }
 #pragma unroll
     for (int k = 0; k < WCB; k++) {
       const int g = wave + 4 * k;
-      const int kbi = (g * 64) / (BN * (KH ? 1 : OB::NPK));
+      const int kbi = (g * 64) / (BN * NPKB);
       dma16(rs[2], g < NCB ? stage + OFF_B + g * 64 * 16 : arena + DUMMY, voff(cb[k], kb, P::kGeoB, inB, lb0, lb1),
             soff(kb.code, kbi, live, nv));
     }
@@ -1007,7 +1062,7 @@ __global__ __launch_bounds__(256 * NG) __attribute__((amdgpu_waves_per_eu(2))) v
   // operand images and scales of the step's KPS / 2 pairs of K-blocks; pair
   // p starts 2 K-blocks (KBA / KBB bytes each) into the operand's stage
   constexpr int NP = KPS / 2;
-  constexpr int KBA = BM * (KH ? 1 : OA::NPK) * 16, KBB = BN * (KH ? 1 : OB::NPK) * 16;
+  constexpr int KBA = BM * NPKA * 16, KBB = BN * NPKB * 16;
   v8i a[NP][TM], b[NP][TN];
   int xa[NP][TM], xb[NP][TN];
   auto read_operands = [&](int st) {
@@ -1030,7 +1085,8 @@ __global__ __launch_bounds__(256 * NG) __attribute__((amdgpu_waves_per_eu(2))) v
         const int row = (wn * TN + j) * 32 + r32;
         // (with KH the other operand's upper lanes are zero: a K-major A is
         // zeroed above, a row-major A reads the zero slot)
-        if constexpr (TB) b[p][j] = lds_operand_k<BN, KH, false>(sB, (wn * TN + j) * 32, lane);
+        if constexpr (TB && FB >= 2) b[p][j] = lds_operand_k_sub<FB, BN>(sB, (wn * TN + j) * 32, lane);
+        else if constexpr (TB) b[p][j] = lds_operand_k<BN, KH, false>(sB, (wn * TN + j) * 32, lane);
         else if constexpr (KH) b[p][j] = lds_operand_half<BN>(sB, arena + ZERO, row, q);
         else b[p][j] = lds_operand<FB, BN>(sB, row, swz, q);
         xb[p][j] = *reinterpret_cast<const int*>(stage + OFF_SB + (GS ? kq * (BN / gsb) + row / gsb : kq * BN + row) * 4);
@@ -1068,7 +1124,7 @@ __global__ __launch_bounds__(256 * NG) __attribute__((amdgpu_waves_per_eu(2))) v
   tab = fill(s_lo);
   int cs = 0;
   // LDS reads per step of a wave, for the instruction schedule below
-  constexpr int RDA = TA ? 4 : F_READS<FA>(), RDB = TB ? 4 : F_READS<FB>();
+  constexpr int RDA = TA ? 4 : F_READS<FA>(), RDB = TB ? (FB <= 1 ? 4 : 2) : F_READS<FB>();
   constexpr int NDS = NP * (TM * (RDA + 1) + TN * (RDB + 1));
   constexpr int NMF = NP * TM * TN;
   constexpr int VPM = (WPS + NMF - 1) / NMF;  // loads issued after each MFMA
@@ -1204,7 +1260,10 @@ hipError_t launch_gemm(int fa, int fb, const P& prob, dim3 grid, hipStream_t st)
                        st, prob);                                                                       \
     return launch_check();                                                                           \
   }
-  if constexpr (KH || (P::kKMajA && P::kKMajB)) {
+  if constexpr (SubB<P>::value) {  // 8-bit A, 6/4-bit B, full K-blocks only
+    if constexpr (!KH) { MQ_CASE(0, 2) MQ_CASE(0, 3) MQ_CASE(0, 4) MQ_CASE(1, 2) MQ_CASE(1, 3) MQ_CASE(1, 4) }
+    return hipErrorInvalidValue;
+  } else if constexpr (KH || (P::kKMajA && P::kKMajB)) {
     MQ_CASE(0, 0) MQ_CASE(0, 1) MQ_CASE(1, 0) MQ_CASE(1, 1)
     return hipErrorInvalidValue;
   } else if constexpr (P::kKMajB) {

@@ -4,6 +4,10 @@
 
 namespace mq {
 
+// The GEMM launch of the 6/4-bit in-place path (gemm_wgrad_sub.hip, its own
+// translation unit so its kernels compile in parallel).
+hipError_t launch_wgrad_nat_sub(int fa, int fb, const WgradNatSubProb& q, int Ma, int Nb, int S, hipStream_t st);
+
 // out[i] = sum_z part[z][i] in a fixed order (deterministic): the G thread
 // groups of a block sum the slices z = g, g+G, g+2G, ... in turn, then the G
 // group sums are added in order g = 0..G-1. VEC: four consecutive outputs
@@ -103,14 +107,16 @@ static int wgrad_splits(const Conv& cv, int fdy, int fx) {
 }
 
 // How the backward-weight GEMM reads its operands and how much workspace it
-// uses: 8-bit codes are read where quantization left them (K-major staging)
-// when a 16-channel chunk of B stays in one tap and a K-block's lines are
-// the N values of one pixel (natural); otherwise both are first re-laid with
-// runs along N; with 8-bit gradient codes and other activation codes
-// (mixed) only the activation is re-laid. Workspace: [re-laid dY][re-laid
-// X][fp32 partial sums of the S slices], each part present only when used.
+// uses: with 8-bit gradient codes, the codes are read where quantization
+// left them (K-major staging) when a 16-channel chunk of B stays in one tap
+// and a K-block's lines are the N values of one pixel (natural: 8-bit
+// activation codes; natural_sub: 6- or 4-bit ones, read with the sub-byte
+// transposing LDS reads); otherwise the activation (mixed: 8-bit gradient
+// codes), or both, are first re-laid with runs along N. Workspace: [re-laid
+// dY][re-laid X][fp32 partial sums of the S slices], each part present only
+// when used.
 struct WgradPlan {
-  bool natural, mixed, half;
+  bool natural, natural_sub, mixed, half;
   int kps, S;
   size_t dyt_b, xt_b, part_b;
 };
@@ -119,16 +125,18 @@ static WgradPlan wgrad_plan(const Conv& cv, int fdy, int fx) {
   const int ga = 32, gb = cv.cin % 32 == 0 ? 32 : 0, khalf = cv.n <= 16;
   const bool kext_ok = cv.n <= 32 || cv.n % 32 == 0;
   w.natural = fdy <= 1 && fx <= 1 && cv.cin % 16 == 0 && kext_ok;
-  w.mixed = !w.natural && fdy <= 1 && kext_ok;
-  w.half = !w.natural && half_k_blocks(ga, gb, khalf, fdy, fx);
+  w.natural_sub = fdy <= 1 && fx >= 2 && cv.cin % 16 == 0 && kext_ok;
+  w.mixed = !w.natural && !w.natural_sub && fdy <= 1 && kext_ok;
+  w.half = !w.natural && !w.natural_sub && half_k_blocks(ga, gb, khalf, fdy, fx);
   // half K-blocks take four K-blocks per step and two wave groups per
   // workgroup, so half as many slices cover the K range
   w.kps = half_k_blocks(ga, gb, khalf, fdy, fx) ? 4 : 2;
   const int S0 = wgrad_splits(cv, fdy, fx);
   w.S = w.kps == 4 ? ceil_div(S0, 2) : S0;
   const long long npix_o = (long long)cv.ho() * cv.wo();
-  w.dyt_b = (!w.natural && !w.mixed) ? align256(transposed_bytes(fdy, npix_o, cv.n, 1, cv.cout)) : 0;
-  w.xt_b = !w.natural ? align256(transposed_bytes(fx, (long long)cv.h * cv.w, cv.n, 1, cv.cin)) : 0;
+  const bool in_place = w.natural || w.natural_sub;
+  w.dyt_b = (!in_place && !w.mixed) ? align256(transposed_bytes(fdy, npix_o, cv.n, 1, cv.cout)) : 0;
+  w.xt_b = !in_place ? align256(transposed_bytes(fx, (long long)cv.h * cv.w, cv.n, 1, cv.cin)) : 0;
   w.part_b = w.S > 1 ? align256((size_t)w.S * cv.cout * cv.kh * cv.kw * cv.cin * 4) : 0;
   return w;
 }
@@ -165,7 +173,7 @@ bool gemm_offsets_ok(const Conv& cv, int op, int fa, int fb, int bpa) {
   const long long xRB = w.half ? 16 : run_bytes(fb);
   const long long lead = (long long)cv.ph * cv.w + cv.pw;
   bool ok = offsets_fit((long long)cv.h * cv.w * nNB * ncbi, lead * nNB * ncbi);
-  if (w.natural) {
+  if (w.natural || w.natural_sub) {
     const long long xrb = row_bytes(fb, cv.cin);
     ok = ok && offsets_fit((long long)cv.h * cv.w * cv.n * xrb, lead * cv.n * xrb);
   } else {
@@ -182,7 +190,7 @@ hipError_t launch_backward_weight(const Conv& cv, MxView dy, MxView x, float* dw
   uint8_t* dyt = base;
   uint8_t* xt = base + plan.dyt_b;
   float* part = reinterpret_cast<float*>(base + plan.dyt_b + plan.xt_b);
-  const bool natural = plan.natural, mixed = plan.mixed, half = plan.half;
+  const bool natural = plan.natural || plan.natural_sub, mixed = plan.mixed, half = plan.half;
   const int S = plan.S;
   WgradProb p;
   // rows of A are Cout (32 to a block); rows of B are (tap, Cin), whose
@@ -212,6 +220,7 @@ hipError_t launch_backward_weight(const Conv& cv, MxView dy, MxView x, float* dw
   if (natural) {
     static_cast<WgradProb&>(q) = p;
     q.dyrb = (int)row_bytes(dy.fmt, cv.cout); q.xrb = (int)row_bytes(x.fmt, cv.cin);
+    q.xbits = bits_of(x.fmt);
     q.dytc = dy.codes; q.dytc_bytes = npix_o * cv.n * q.dyrb;
     q.xtc = x.codes; q.xtc_bytes = (long long)cv.h * cv.w * cv.n * q.xrb;
     q.xtcb = (int)(lead * cv.n * q.xrb);
@@ -227,7 +236,11 @@ hipError_t launch_backward_weight(const Conv& cv, MxView dy, MxView x, float* dw
     e = launch_transpose_codes(x.codes, xt, x.fmt, half, cv.h * cv.w, cv.n, 1, cv.cin, st);
     if (e != hipSuccess) return e;
   }
-  if (natural) {
+  if (plan.natural_sub) {
+    WgradNatSubProb r;
+    static_cast<WgradNatProb&>(r) = q;
+    e = launch_wgrad_nat_sub(dy.fmt, x.fmt, r, cv.cout, (int)nj, S, st);
+  } else if (natural) {
     e = launch_tiled(dy.fmt, x.fmt, q, cv.cout, (int)nj, S, st);
   } else if (mixed) {  // (half K-blocks need 8-bit activation codes: never here)
     WgradMixProb r;

@@ -228,10 +228,11 @@ def test_noalloc_validation_without_gpu():
     assert _call(mq.mqconv_backward_weight_noalloc, s, dy, x, 0) == -1
     assert _call(mq.mqconv_backward_weight_noalloc, s, dy, _mx(mq.ROLE_ACT, (s.h, s.w, s.n, s.cin), bp=1), FAKE) == -6
     assert _call(mq.mqconv_backward_weight_noalloc, s, x, x, FAKE) == -3
+    # 6-bit gradient and activation codes are both re-laid: 288 MiB of scratch
     big = ConvShape(64, 128, 160, 160, 256, 3, 3, 2, 1)
-    assert mq.mqconv_workspace_bytes(big, 2, 1, 3) > mq.NOALLOC_SCRATCH_BYTES
+    assert mq.mqconv_workspace_bytes(big, 2, 3, 3) > mq.NOALLOC_SCRATCH_BYTES
     xb = _mx(mq.ROLE_ACT, (big.h, big.w, big.n, big.cin), fmt=3)
-    dyb = _mx(mq.ROLE_GRAD, (big.ho, big.wo, big.n, big.cout), fmt=1)
+    dyb = _mx(mq.ROLE_GRAD, (big.ho, big.wo, big.n, big.cout), fmt=3)
     assert _call(mq.mqconv_backward_weight_noalloc, big, dyb, xb, FAKE) == -5
 
 

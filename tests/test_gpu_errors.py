@@ -43,15 +43,16 @@ def test_quantize_fails_then_recovers():
 
 @pytest.mark.parametrize("noalloc", [False, True])
 def test_backward_weight_fails_at_each_launch_then_recovers(noalloc):
-    # 6-bit X and 8-bit dY: X re-laid, split-K GEMM, fixed-order reduction
+    # 6-bit dY and X: both re-laid, then the split-K GEMM and the fixed-order
+    # reduction (four launches)
     s = ConvShape(32, 64, 18, 14, 96)
     say(f"errors: backward_weight noalloc={noalloc} shape={s.as_tuple()}")
     rng = np.random.default_rng(72)
     x = rng.standard_normal((s.h, s.w, s.n, s.cin)).astype(np.float32)
     dy = rng.standard_normal((s.ho, s.wo, s.n, s.cout)).astype(np.float32)
     xq = gpu_quantize(x, mq.ROLE_ACT, 3, 32)
-    gq = gpu_quantize(dy, mq.ROLE_GRAD, 1, 32)
-    ws = torch.empty(max(1, mq.mqconv_workspace_bytes(s, mq.OP_WGRAD, 1, 3)), dtype=torch.uint8, device="cuda")
+    gq = gpu_quantize(dy, mq.ROLE_GRAD, 3, 32)
+    ws = torch.empty(max(1, mq.mqconv_workspace_bytes(s, mq.OP_WGRAD, 3, 3)), dtype=torch.uint8, device="cuda")
 
     def call(dw):
         if noalloc:
@@ -77,8 +78,8 @@ def test_backward_weight_fails_at_each_launch_then_recovers(noalloc):
         mq.mqconv_inject_launch_failure(0)
         np.testing.assert_array_equal(host(dw), ref_h)
         break
-    # the re-laying, the GEMM and the reduction each failed once
-    assert failed >= 3, failed
+    # the two re-layings, the GEMM and the reduction each failed once
+    assert failed == 4, failed
     dw = torch.full_like(ref, float("nan"))
     call(dw)
     np.testing.assert_array_equal(host(dw), ref_h)

@@ -47,11 +47,12 @@ def test_noalloc_equals_workspace_call_twice_then_smaller(key):
 
 def test_noalloc_rejects_problems_beyond_the_scratch_array():
     wl = WORKLOADS["c5"]
-    big = ConvShape(64, 128, 160, 160, 256, 3, 3, 2, 1)  # needs 213 MiB
-    need = mq.mqconv_workspace_bytes(big, 2, wl.fdy, wl.fx)
+    # 6-bit gradient and activation codes, both re-laid: needs 288 MiB
+    big = ConvShape(64, 128, 160, 160, 256, 3, 3, 2, 1)
+    need = mq.mqconv_workspace_bytes(big, 2, 3, wl.fx)
     assert need > mq.NOALLOC_SCRATCH_BYTES
     xq = mq.MxTensor.empty(mq.ROLE_ACT, wl.fx, 32, (big.h, big.w, big.n, big.cin))
-    gq = mq.MxTensor.empty(mq.ROLE_GRAD, wl.fdy, 32, (big.ho, big.wo, big.n, big.cout))
+    gq = mq.MxTensor.empty(mq.ROLE_GRAD, 3, 32, (big.ho, big.wo, big.n, big.cout))
     dw = torch.empty((big.cout, big.kh, big.kw, big.cin), device="cuda")
     with pytest.raises(mq.MqConvError) as e:
         mq.mqconv_backward_weight_noalloc(big, gq, xq, dw)
