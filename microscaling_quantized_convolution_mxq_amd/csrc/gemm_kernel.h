@@ -847,8 +847,17 @@ __global__ __launch_bounds__(256 * NG) __attribute__((amdgpu_waves_per_eu(2))) v
     const int lin = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
     const int xcd = lin % 8, idx = lin / 8, q8 = nb / 8, r8 = nb % 8;
     const int logical = xcd < r8 ? xcd * (q8 + 1) + idx : r8 * (q8 + 1) + (xcd - r8) * q8 + idx;
-    z = (int)fdiv((unsigned)logical, prob.grid.nxy);
-    const int rem = logical - z * nx * ny;
+    int rem;
+    if constexpr (std::is_base_of<DgradProb, P>::value) {
+      // backward-data: the stride-parity classes of one tile position run
+      // side by side (they read the same dY rows through different taps)
+      const int nz = gridDim.z;
+      rem = logical / nz;
+      z = logical - rem * nz;
+    } else {
+      z = (int)fdiv((unsigned)logical, prob.grid.nxy);
+      rem = logical - z * nx * ny;
+    }
     by = (int)fdiv((unsigned)rem, prob.grid.nx);
     bx = rem - by * nx;
   }
