@@ -558,9 +558,22 @@ __device__ __forceinline__ v8i lds_operand_half(const uint8_t* stage, const uint
 // K-major stage of an 8-bit operand with BR rows: [kb][k][BR] bytes, one
 // line of BR codes per K index k (the operand's rows side by side, as they
 // lie in memory when the contraction runs along the partner or the tap
-// dimension). Its 16-byte chunks are permuted within each aligned group of
-// four by kswz(k), so that the transposing reads below hit distinct banks.
-__device__ __forceinline__ int kswz(int k) { return (k >> 1) & 3; }
+// dimension). Its 16-byte chunks (CPR = BR / 16 per line) are permuted
+// within aligned groups by kswz, so that the transposing reads below hit
+// distinct LDS banks (a 16-byte slot covers 4 of the 64 banks; two lines
+// of 128 bytes cover all of them):
+//   8-bit codes, CPR a multiple of 8: 2 * ((k >> 1) & 3) in groups of 8 --
+//     the 32 lanes of a ds_read_b64_tr_b8 read 8 lines of two neighbouring
+//     chunks, which then sit in 16 different bank groups;
+//   6/4-bit codes, CPR a multiple of 8: (k >> 1) & 7 -- a 16-lane group of
+//     ds_read_b96_tr_b6 / ds_read_b64_tr_b4 reads 16 lines of one chunk;
+//   otherwise (k >> 1) & 3 in groups of 4.
+template <bool SUB, int CPR>
+__device__ __forceinline__ int kswz(int k) {
+  if constexpr (CPR % 8 != 0) return (k >> 1) & 3;
+  else if constexpr (SUB) return (k >> 1) & 7;
+  else return ((k >> 1) & 3) << 1;
+}
 // Operand image of rows r0..r0+31 from a K-major stage with ds_read_b64_tr_b8:
 // in each 16-lane group, lanes 2i and 2i+1 address the two halves of the
 // 16-byte chunk of line k0+i that holds the group's 16 rows, and lane t
@@ -576,8 +589,8 @@ __device__ __forceinline__ v8i lds_operand_k(const uint8_t* stage, int r0, int l
   constexpr int KL = HALF ? 16 : 32;  // lines per K-block
   const int g = lane >> 4, t = lane & 15, q = HALF ? 0 : g >> 1;
   const int chunk = (r0 >> 4) + (g & 1);
-  // k = 16q + 8h + t/2, so kswz(k) = (t >> 2) & 3 for every read
-  const uint8_t* base = stage + (16 * q + (t >> 1)) * BR + 16 * (chunk ^ ((t >> 2) & 3)) + 8 * (t & 1);
+  // k = 16q + 8h + t/2, so kswz(k) = kswz(t/2) for every read
+  const uint8_t* base = stage + (16 * q + (t >> 1)) * BR + 16 * (chunk ^ kswz<false, BR / 16>(t >> 1)) + 8 * (t & 1);
   v8i r;
 #pragma unroll
   for (int kb = 0; kb < 2; kb++)
@@ -617,7 +630,7 @@ __device__ __forceinline__ v8i lds_operand_k_sub(const uint8_t* stage, int r0, i
 #pragma unroll
   for (int h = 0; h < 2; h++) {
     const int k = 16 * h + t;  // line within K-block q
-    const uint8_t* src = stage + (32 * q + k) * BR + 16 * (chunk ^ kswz(k));
+    const uint8_t* src = stage + (32 * q + k) * BR + 16 * (chunk ^ kswz<true, BR / 16>(k));
     if constexpr (Fmt<F>::bits == 6) {
       const v3i_t x = __builtin_amdgcn_ds_read_tr6_b96_v3i32((lds_v3i_ptr)src);
       r[3 * h] = x[0]; r[3 * h + 1] = x[1]; r[3 * h + 2] = x[2];
@@ -838,8 +851,9 @@ __global__ __launch_bounds__(256 * NG) __attribute__((amdgpu_waves_per_eu(2))) v
   uint8_t* const ring = arena + grp * NS * STAGE;  // this group's stages
   // XCD-aware tile order: the hardware hands consecutive workgroups to the 8
   // XCDs in turn, each with its own L2. Remap so that every XCD works on a
-  // contiguous range of tiles (x fastest): neighbouring row tiles share the
-  // weight tile and the rows of the implicit im2col, and now share an L2.
+  // contiguous range of tiles (column tiles fastest, then row tiles):
+  // neighbouring row tiles share the weight tile and the rows of the
+  // implicit im2col, and now share an L2.
   int bx, by, z;
   {
     const int nx = gridDim.x, ny = gridDim.y;
@@ -858,8 +872,10 @@ __global__ __launch_bounds__(256 * NG) __attribute__((amdgpu_waves_per_eu(2))) v
       z = (int)fdiv((unsigned)logical, prob.grid.nxy);
       rem = logical - z * nx * ny;
     }
-    by = (int)fdiv((unsigned)rem, prob.grid.nx);
-    bx = rem - by * nx;
+    // column tiles fastest: the column tiles of one row tile read the same
+    // A rows, now from the same XCD's L2
+    bx = rem / ny;
+    by = rem - bx * ny;
   }
   const typename P::Ctx cx = prob.ctx(z);
   const int m0 = bx * BM, n0 = by * BN;
@@ -901,7 +917,8 @@ __global__ __launch_bounds__(256 * NG) __attribute__((amdgpu_waves_per_eu(2))) v
     const bool real = g < ngl;
     const int t = real ? 64 * g + lane : 0;
     const int kb = t / KBS, u = t - kb * KBS;
-    const int k = u / CPR, chunk = (u - k * CPR) ^ kswz(k);
+    constexpr bool SUB = (is_a ? FA : FB) >= 2;
+    const int k = u / CPR, chunk = (u - k * CPR) ^ kswz<SUB, CPR>(k);
     const PairDelta& d = is_a ? dA : dB;
     RowInfo r;
     int kext, ks;
