@@ -2,7 +2,7 @@
 
 One step = one pass of every step of the path over one batch of synthetic
 input: quantize X and W (one grouped call, as before a layer's forward
-pass; one launch when they share an element format) and G_Y once (MX, E8M0
+pass; one launch for up to two element formats) and G_Y once (MX, E8M0
 scales, round-to-nearest), channel-batch-first
 im2col of the quantized activation, then the forward, backward-data and
 backward-weight block-scaled GEMMs. Inputs are resident in HBM before the
@@ -55,8 +55,8 @@ CALLS = ["quantize_xw", "quantize_dy", "cbf_im2col", "forward", "backward_data",
 EXTRA = ["forward_mx", "backward_data_mx", "quantize_dy_sr", "backward_weight_noalloc"]
 # kernels each entry point launches (see the launchers in csrc/)
 CALL_KERNELS = {
-    # X and W share one launch when their formats match, else one launch each
-    "quantize_xw": ["mxq_quantize_group_kernel (same format; else 2 x mxq_quantize_kernel)"],
+    # X and W share one launch (the grouped quantizer takes up to two formats)
+    "quantize_xw": ["mxq_quantize_group_kernel (X and W in one launch, of one or two element formats)"],
     "quantize_dy": ["mxq_quantize_kernel"], "cbf_im2col": ["cbf_im2col_kernel"],
     "quantize_dy_sr": ["mxq_quantize_kernel (stochastic rounding)"],
     "backward_weight_noalloc": ["as backward_weight, scratch in the library's fixed array"],

@@ -207,8 +207,9 @@ int mqconv_quantize_sr(const float* src, mq_mx dst, uint64_t seed, void* stream)
 /* mqconv_quantize of several tensors at once, e.g. a layer's activation and
  * weight before its forward pass (each still quantized once, §III-A, §IV-B):
  * src[i] -> dst[i] for i < count, every pair exactly as mqconv_quantize
- * would write it. Tensors that share an element format share one launch, so
- * a small tensor runs beside a large one instead of after it.
+ * would write it. Tensors of up to two element formats share one launch
+ * (more formats: one launch per format), so a small tensor runs beside a
+ * large one instead of after it.
  * src, dst: host arrays of count entries (read during the call only).
  * count: 1 .. MQ_QUANTIZE_GROUP_MAX, else MQ_ERR_SHAPE.
  * Every pair is checked (as mqconv_quantize) before anything is enqueued;

@@ -210,15 +210,16 @@ __global__ __launch_bounds__(256) void mxq_quantize_kernel(const float* __restri
                                   stage_buf[ST ? threadIdx.x >> 6 : 0], k0, k1);
 }
 
-// Several tensors of one element format in one launch (a small tensor, such
-// as a weight, then runs beside a large one instead of after it): member i
-// owns workgroups [begin, begin + nbx * gy) of the 1-D grid, nbx workgroups
-// of tiles for each of its gy channel-block phases.
+// Several tensors of one or two element formats in one launch (a small
+// tensor, such as a weight, then runs beside a large one instead of after
+// it): member i owns workgroups [begin, begin + nbx * gy) of the 1-D grid,
+// nbx workgroups of tiles for each of its gy channel-block phases; its codes
+// take the launch's first format, or the second one when alt is set.
 struct QMember {
   const float* src;
   uint8_t *codes, *scales;
   long long ntiles;
-  int A, P, B, C, bp, variant, nbx, gy, begin;  // variant = 2 * MODE + ST
+  int A, P, B, C, bp, variant, nbx, gy, begin, alt;  // variant = 2 * MODE + ST
 };
 constexpr int kQGroupMax = 8;
 struct QGroup {
@@ -226,7 +227,7 @@ struct QGroup {
   int count;
 };
 
-template <int F>
+template <int F0, int F1>
 __global__ __launch_bounds__(256) void mxq_quantize_group_kernel(QGroup g) {
   __shared__ __attribute__((aligned(16))) uint8_t stage_buf[4][kStageBytes];
   const int b = blockIdx.x;
@@ -236,17 +237,46 @@ __global__ __launch_bounds__(256) void mxq_quantize_group_kernel(QGroup g) {
     if (j < g.count && b >= g.m[j].begin) q = g.m[j];
   const int lb = b - q.begin, by = lb / q.nbx, bx = lb - by * q.nbx;
   uint8_t* stage = stage_buf[threadIdx.x >> 6];
-#define MQ_QT(MODE, ST) \
+#define MQ_QT(F, MODE, ST) \
   quantize_tiles<F, MODE, ST>(q.src, q.codes, q.scales, q.A, q.P, q.B, q.C, q.bp, q.ntiles, bx, by, q.gy, stage)
-  switch (q.variant) {
-    case 0: MQ_QT(0, false); break;
-    case 1: MQ_QT(0, true); break;
-    case 2: MQ_QT(1, false); break;
-    case 3: MQ_QT(1, true); break;
-    case 4: MQ_QT(2, false); break;
-    default: MQ_QT(2, true); break;
+#define MQ_QV(F)                          \
+  switch (q.variant) {                    \
+    case 0: MQ_QT(F, 0, false); break;    \
+    case 1: MQ_QT(F, 0, true); break;     \
+    case 2: MQ_QT(F, 1, false); break;    \
+    case 3: MQ_QT(F, 1, true); break;     \
+    case 4: MQ_QT(F, 2, false); break;    \
+    default: MQ_QT(F, 2, true); break;    \
   }
+  if constexpr (F0 == F1) {
+    MQ_QV(F0)
+  } else if (q.alt) {  // uniform: one member per workgroup
+    MQ_QV(F1)
+  } else {
+    MQ_QV(F0)
+  }
+#undef MQ_QV
 #undef MQ_QT
+}
+
+template <int F0>
+static void launch_group_f0(int f1, const QGroup& g, unsigned blocks, hipStream_t st) {
+  switch (f1) {
+    case 0: hipLaunchKernelGGL((mxq_quantize_group_kernel<F0, 0>), dim3(blocks), dim3(256), 0, st, g); break;
+    case 1: hipLaunchKernelGGL((mxq_quantize_group_kernel<F0, 1>), dim3(blocks), dim3(256), 0, st, g); break;
+    case 2: hipLaunchKernelGGL((mxq_quantize_group_kernel<F0, 2>), dim3(blocks), dim3(256), 0, st, g); break;
+    case 3: hipLaunchKernelGGL((mxq_quantize_group_kernel<F0, 3>), dim3(blocks), dim3(256), 0, st, g); break;
+    default: hipLaunchKernelGGL((mxq_quantize_group_kernel<F0, 4>), dim3(blocks), dim3(256), 0, st, g); break;
+  }
+}
+static void launch_group(int f0, int f1, const QGroup& g, unsigned blocks, hipStream_t st) {
+  switch (f0) {
+    case 0: launch_group_f0<0>(f1, g, blocks, st); break;
+    case 1: launch_group_f0<1>(f1, g, blocks, st); break;
+    case 2: launch_group_f0<2>(f1, g, blocks, st); break;
+    case 3: launch_group_f0<3>(f1, g, blocks, st); break;
+    default: launch_group_f0<4>(f1, g, blocks, st); break;
+  }
 }
 
 // Block geometry of one tensor: MODE 0 for line blocks, 2 when a pixel's
@@ -311,20 +341,39 @@ hipError_t launch_quantize_sr(const float* src, uint8_t* codes, uint8_t* scales,
   return launch_fmt<true>(QReq{src, codes, scales, fmt, bp, A, P, B, C}, seed, st);
 }
 
-// One grouped launch per element format present (and per kQGroupMax
+// One grouped launch for up to kQGroupMax members of at most two element
+// formats (more formats or members: one launch per format, per kQGroupMax
 // members); members in increasing size, so the small ones are dispatched
-// first and finish inside the large ones' time. A format with one member
-// takes the single-tensor launch.
+// first and finish inside the large ones' time. A single tensor takes the
+// single-tensor launch.
 hipError_t launch_quantize_group(const QReq* reqs, int count, hipStream_t st) {
-  for (int f = 0; f < 5; f++) {
-    std::vector<int> idx;
-    for (int i = 0; i < count; i++)
-      if (reqs[i].fmt == f) idx.push_back(i);
-    if (idx.empty()) continue;
+  std::vector<int> fmts;
+  for (int i = 0; i < count; i++)
+    if (std::find(fmts.begin(), fmts.end(), reqs[i].fmt) == fmts.end()) fmts.push_back(reqs[i].fmt);
+  // the launches: lists of members and the (first, second) formats of each
+  std::vector<std::vector<int>> sets;
+  std::vector<std::pair<int, int>> fpair;
+  if (fmts.size() <= 2 && count <= kQGroupMax) {
+    std::vector<int> all(count);
+    for (int i = 0; i < count; i++) all[i] = i;
+    sets.push_back(all);
+    fpair.push_back({fmts[0], fmts.size() > 1 ? fmts[1] : fmts[0]});
+  } else {
+    for (int f : fmts) {
+      std::vector<int> idx;
+      for (int i = 0; i < count; i++)
+        if (reqs[i].fmt == f) idx.push_back(i);
+      for (size_t c0 = 0; c0 < idx.size(); c0 += kQGroupMax) {
+        sets.push_back(std::vector<int>(idx.begin() + c0, idx.begin() + std::min(idx.size(), c0 + kQGroupMax)));
+        fpair.push_back({f, f});
+      }
+    }
+  }
+  for (size_t s = 0; s < sets.size(); s++) {
+    std::vector<int>& idx = sets[s];
     if (idx.size() == 1) {
-      const hipError_t e = launch_quantize(reqs[idx[0]].src, reqs[idx[0]].codes, reqs[idx[0]].scales, f,
-                                           reqs[idx[0]].bp, reqs[idx[0]].A, reqs[idx[0]].P, reqs[idx[0]].B,
-                                           reqs[idx[0]].C, st);
+      const QReq& r = reqs[idx[0]];
+      const hipError_t e = launch_quantize(r.src, r.codes, r.scales, r.fmt, r.bp, r.A, r.P, r.B, r.C, st);
       if (e != hipSuccess) return e;
       continue;
     }
@@ -332,30 +381,23 @@ hipError_t launch_quantize_group(const QReq* reqs, int count, hipStream_t st) {
     for (int i : idx) plans[i] = quantize_plan(reqs[i].A, reqs[i].P, reqs[i].B, reqs[i].C, reqs[i].bp);
     std::stable_sort(idx.begin(), idx.end(),
                      [&](int a, int b) { return plans[a].blocks * plans[a].gy < plans[b].blocks * plans[b].gy; });
-    for (size_t c0 = 0; c0 < idx.size(); c0 += kQGroupMax) {
-      QGroup g{};
-      long long total = 0;
-      g.count = (int)std::min<size_t>(kQGroupMax, idx.size() - c0);
-      for (int k = 0; k < g.count; k++) {
-        const QReq& r = reqs[idx[c0 + k]];
-        const QPlan& q = plans[idx[c0 + k]];
-        QMember& m = g.m[k];
-        m.src = r.src; m.codes = r.codes; m.scales = r.scales; m.ntiles = q.ntiles;
-        m.A = r.A; m.P = r.P; m.B = r.B; m.C = r.C; m.bp = r.bp;
-        m.variant = 2 * q.mode + q.st; m.nbx = (int)q.blocks; m.gy = q.gy; m.begin = (int)total;
-        total += q.blocks * q.gy;
-        if (total > 0x7fffffffLL) return hipErrorInvalidValue;
-      }
-      switch (f) {
-        case 0: hipLaunchKernelGGL(mxq_quantize_group_kernel<0>, dim3((unsigned)total), dim3(256), 0, st, g); break;
-        case 1: hipLaunchKernelGGL(mxq_quantize_group_kernel<1>, dim3((unsigned)total), dim3(256), 0, st, g); break;
-        case 2: hipLaunchKernelGGL(mxq_quantize_group_kernel<2>, dim3((unsigned)total), dim3(256), 0, st, g); break;
-        case 3: hipLaunchKernelGGL(mxq_quantize_group_kernel<3>, dim3((unsigned)total), dim3(256), 0, st, g); break;
-        default: hipLaunchKernelGGL(mxq_quantize_group_kernel<4>, dim3((unsigned)total), dim3(256), 0, st, g); break;
-      }
-      const hipError_t e = launch_check();
-      if (e != hipSuccess) return e;
+    QGroup g{};
+    long long total = 0;
+    g.count = (int)idx.size();
+    for (int k = 0; k < g.count; k++) {
+      const QReq& r = reqs[idx[k]];
+      const QPlan& q = plans[idx[k]];
+      QMember& m = g.m[k];
+      m.src = r.src; m.codes = r.codes; m.scales = r.scales; m.ntiles = q.ntiles;
+      m.A = r.A; m.P = r.P; m.B = r.B; m.C = r.C; m.bp = r.bp;
+      m.variant = 2 * q.mode + q.st; m.nbx = (int)q.blocks; m.gy = q.gy; m.begin = (int)total;
+      m.alt = r.fmt != fpair[s].first;
+      total += q.blocks * q.gy;
+      if (total > 0x7fffffffLL) return hipErrorInvalidValue;
     }
+    launch_group(fpair[s].first, fpair[s].second, g, (unsigned)total, st);
+    const hipError_t e = launch_check();
+    if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }

@@ -112,6 +112,12 @@ def test_quantize_group_small_mixed():
              (r(4, 4, 8, 300), mq.ROLE_ACT, 1, 32), (r(70, 3, 3, 64), mq.ROLE_WEIGHT, 1, 32)]
     assert len(eight) == mq.QUANTIZE_GROUP_MAX
     _check_group(eight, "eight")
+    # two formats in one launch, every block mode and the staged and
+    # unstaged stores on both sides
+    two = [(r(2, 3, 16, 64), mq.ROLE_GRAD, 3, 32), (r(4, 5, 7, 300), mq.ROLE_ACT, 0, 1),
+           (r(5, 3, 3, 20), mq.ROLE_WEIGHT, 3, 32), (r(3, 3, 8, 96), mq.ROLE_ACT, 0, 32),
+           (r(6, 3, 1, 40), mq.ROLE_WEIGHT, 3, 1), (r(2, 2, 40, 33), mq.ROLE_ACT, 0, 32)]
+    _check_group(two, "two formats")
 
 
 @pytest.mark.parametrize("key", ["c2", "c4", "c5"])
