@@ -65,8 +65,10 @@ CALL_KERNELS = {
                          "mx_gemm_kernel<MxOutProb<DgradProb>>)"],
     # 8-bit codes are read in place; other formats are first re-laid by transpose_codes_kernel
     "backward_data": ["mx_gemm_kernel<DgradNatProb> (8-bit W; else transpose_codes_kernel + mx_gemm_kernel<DgradProb>)"],
-    "backward_weight": ["mx_gemm_kernel<WgradNatProb> (8-bit dY and X; 8-bit dY only: transpose_codes_kernel (X) + "
-                        "mx_gemm_kernel<WgradMixProb>; else 2 x transpose_codes_kernel + mx_gemm_kernel<WgradProb>)",
+    "backward_weight": ["mx_gemm_kernel<WgradNatProb> (8-bit dY and X) or mx_gemm_kernel<WgradNatSubProb> (8-bit "
+                        "dY, 6/4-bit X), both read in place when Cin % 16 == 0; else transpose_codes_kernel (X) + "
+                        "mx_gemm_kernel<WgradMixProb> (8-bit dY), or 2 x transpose_codes_kernel + "
+                        "mx_gemm_kernel<WgradProb>",
                         "splitk_reduce_kernel (when split)"],
 }
 
