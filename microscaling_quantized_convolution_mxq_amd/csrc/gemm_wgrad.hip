@@ -94,13 +94,15 @@ static int wgrad_splits(const Conv& cv, int fdy, int fx) {
   const WgradSteps ks = wgrad_steps(cv, 4);
   const long long nkb = (long long)cv.ho() * cv.wo() * ceil_div(cv.n, 32);
   // workgroups of one wave group (full K-blocks) run one per CU at the
-  // two-times cap on the large layers; partial sums of up to four times the
+  // two-times cap on the large layers; partial sums of up to eight times the
   // operand bytes let two run per CU, which measured faster despite the
   // extra bytes (3x3 stride-2 layer, N 32, 128 -> 256 channels, 160 x 160:
-  // 97.8 -> 83.7 us); the two-group half-block kernel keeps the tighter cap
+  // 97.8 -> 83.7 us at four times; 3x3 layer, N 128, 256 channels, 20 x 20:
+  // 57.7 -> 49.2 us going from four to eight times); the two-group
+  // half-block kernel keeps the tighter cap
   const int gb = cv.cin % 32 == 0 ? 32 : 0;
   const bool half = half_k_blocks(32, gb, cv.n <= 16, fdy, fx);
-  int s = splitk_slices(cv.cout, (long long)cv.kh * cv.kw * cv.cin, nkb, ops, half ? 2 : 4, gb >= 8);
+  int s = splitk_slices(cv.cout, (long long)cv.kh * cv.kw * cv.cin, nkb, ops, half ? 2 : 8, gb >= 8);
   if (s > ks.total) s = ks.total;
   if (s < 1) s = 1;
   return s;
