@@ -501,56 +501,68 @@ __device__ inline void rsrcs(const PlainProb& p, __amdgpu_buffer_rsrc_t (&r)[4])
 // ---------------------------------------------------------------------------
 // LDS image of one operand stage
 // ---------------------------------------------------------------------------
-// Stage layout of an operand with BR rows: [kb][row][NPK] 16-byte slots, kb
-// the K-block of the pair. A run is NPK slots (8-bit and 6-bit codes: 2, the
-// 6-bit ones carrying 12 code bytes each; 4-bit codes: 1). With NPK = 2 the
-// two slots of a row are swapped for rows with swz(row) = 1, so that the
-// 16-byte operand reads of 8 (or 16) consecutive rows hit distinct LDS
-// banks. Scales: one dword per (kb, row), [kb][row]. A 64-lane load that
-// writes LDS fills 64 consecutive slots (or scale dwords), so each load
-// belongs to one K-block.
+// Stage layout of a row-major operand: [row][SPR] 16-byte slots, SPR = the
+// step's K-blocks x NPK slots per run (8-bit and 6-bit codes: NPK = 2, the
+// 6-bit ones carrying 12 code bytes each; 4-bit codes and half K-blocks: 1).
+// A 64-lane load that writes LDS fills 64 consecutive slots, so it covers
+// 64 / SPR whole rows, and each row's part of the step (all its K-blocks)
+// comes from one stretch of memory: 64 bytes per row (8-bit, two K-blocks)
+// instead of 32 per lane pair. The L1 serves loads of 64-byte pieces at
+// about twice the rate of loads of 32-byte pieces (measured on MI355X: 18.7
+// against 8.7 TB/s of L2-to-LDS traffic over the whole chip). Slot u of row
+// r holds the row's logical slot u ^ row_swz(r) (logical slot kb * NPK +
+// piece), so that the 16-byte reads of one logical slot by 8 or 16
+// consecutive rows hit distinct LDS banks. Scales: one dword per (kb, row),
+// [kb][row].
 template <int F>
 struct Op {
   static constexpr int RB = run_bytes_of(F);
   static constexpr int NPK = RB == 16 ? 1 : 2;   // slots per run
   static constexpr int CH = RB == 24 ? 12 : 16;  // code bytes per slot
 };
-__device__ __forceinline__ int slot_swz(int row) { return ((row >> 2) ^ (row >> 3)) & 1; }
+template <int SPR>
+__device__ __forceinline__ int row_swz(int r) {
+  static_assert(SPR == 2 || SPR == 4, "slots per row");
+  if constexpr (SPR == 2) return ((r >> 2) ^ (r >> 3)) & 1;
+  else return ((r >> 2) & 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 1);
+}
 // LDS code reads per 32x32x64 operand image
 template <int F>
 constexpr int F_READS() { return F <= 3 ? 2 : 1; }
 
-// Reads one 32x32x64 operand register image (see mx_common.h) of row `row`
-// from an operand stage with BR rows.
-template <int F, int BR>
-__device__ __forceinline__ v8i lds_operand(const uint8_t* stage, int row, int swz, int q) {
+// Reads one 32x32x64 operand register image (see mx_common.h) of row `row`,
+// pair p of the step (K-blocks 2p and 2p+1), from a row-major stage with SPR
+// slots per row; h = row_swz(row).
+template <int F, int SPR>
+__device__ __forceinline__ v8i lds_operand(const uint8_t* op, int row, int h, int p, int q) {
+  const uint8_t* const base = op + row * SPR * 16;
+  auto slot = [&](int L) { return *reinterpret_cast<const v4i*>(base + 16 * (L ^ h)); };
   v8i r = {0, 0, 0, 0, 0, 0, 0, 0};
   if constexpr (F <= 1) {
-    // bytes 0..15: K-block 0, piece q; bytes 16..31: K-block 1, piece q
-    const v4i lo = *reinterpret_cast<const v4i*>(stage + row * 32 + 16 * (q ^ swz));
-    const v4i hi = *reinterpret_cast<const v4i*>(stage + BR * 32 + row * 32 + 16 * (q ^ swz));
+    // bytes 0..15: K-block 2p, piece q; bytes 16..31: K-block 2p+1, piece q
+    const v4i lo = slot(4 * p + q), hi = slot(4 * p + 2 + q);
     r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3]; r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
   } else if constexpr (F <= 3) {
-    // the 24-byte run of K-block q: 12 bytes from each of its two slots
-    const uint8_t* base = stage + q * BR * 32 + row * 32;
-    const v4i lo = *reinterpret_cast<const v4i*>(base + 16 * swz);
-    const v4i hi = *reinterpret_cast<const v4i*>(base + 16 * (1 ^ swz));
+    // the 24-byte run of K-block 2p+q: 12 bytes from each of its two slots
+    const int kb = 2 * p + q;
+    const v4i lo = slot(2 * kb), hi = slot(2 * kb + 1);
     r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = hi[0]; r[4] = hi[1]; r[5] = hi[2];
   } else {
-    // the 16-byte run of K-block q
-    const v4i x = *reinterpret_cast<const v4i*>(stage + q * BR * 16 + row * 16);
+    // the 16-byte run of K-block 2p+q
+    const v4i x = slot(2 * p + q);
     r[0] = x[0]; r[1] = x[1]; r[2] = x[2]; r[3] = x[3];
   }
   return r;
 }
 
 // Operand image of an 8-bit row from a stage that holds only the first 16
-// codes of each run ([kb][row] 16-byte slots), for K-blocks with at most 16
+// codes of each run (one slot per K-block), for K-blocks with at most 16
 // valid codes: lanes of the upper half (q = 1) read a 16-byte zero slot.
-template <int BR>
-__device__ __forceinline__ v8i lds_operand_half(const uint8_t* stage, const uint8_t* zero, int row, int q) {
-  const v4i lo = *reinterpret_cast<const v4i*>(q ? zero : stage + row * 16);
-  const v4i hi = *reinterpret_cast<const v4i*>(q ? zero : stage + (BR + row) * 16);
+template <int SPR>
+__device__ __forceinline__ v8i lds_operand_half(const uint8_t* op, const uint8_t* zero, int row, int h, int p, int q) {
+  const uint8_t* const base = op + row * SPR * 16;
+  const v4i lo = *reinterpret_cast<const v4i*>(q ? zero : base + 16 * ((2 * p) ^ h));
+  const v4i hi = *reinterpret_cast<const v4i*>(q ? zero : base + 16 * ((2 * p + 1) ^ h));
   v8i r = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return r;
 }
@@ -644,9 +656,10 @@ __device__ __forceinline__ v8i lds_operand_k_sub(const uint8_t* stage, int r0, i
 
 // Per-lane part of one LDS-writing load: byte offset of the lane's piece
 // relative to the step's uniform offset (kOOB when the row is outside the
-// problem or the load only keeps the count uniform) and the row's border
-// coordinates for the pair's K-block.
-struct LaneLd { int off, p0, p1; };
+// problem or the load only keeps the count uniform), the row's border
+// coordinates for the piece's K-block, and that K-block within the step
+// (row-major code loads; 0 for the others).
+struct LaneLd { int off, p0, p1, kb; };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // 16 bytes per lane into LDS at lds + 16*lane, from voff + soff
@@ -822,6 +835,8 @@ __global__ __launch_bounds__(256 * NG) __attribute__((amdgpu_waves_per_eu(2))) v
   // (K-major: KL lines of BR bytes per K-block, whatever the code width)
   constexpr int NPKA = TA ? (KH ? 1 : 2) : (KH ? 1 : OA::NPK), NPKB = TB ? (KH ? 1 : 2) : (KH ? 1 : OB::NPK);
   constexpr int A_BYTES = KPS * BM * NPKA * 16, B_BYTES = KPS * BN * NPKB * 16;
+  // slots per row of a row-major stage (K-major stages: unused)
+  constexpr int SPRA = TA ? 2 : KPS * NPKA, SPRB = TB ? 2 : KPS * NPKB;
   constexpr int SA_BYTES = GS ? 256 : 4 * KPS * BM, SB_BYTES = GS ? 256 : 4 * KPS * BN;
   constexpr int OFF_B = A_BYTES, OFF_SA = OFF_B + B_BYTES, OFF_SB = OFF_SA + SA_BYTES;
   constexpr int STAGE = OFF_SB + SB_BYTES;
@@ -890,18 +905,39 @@ __global__ __launch_bounds__(256 * NG) __attribute__((amdgpu_waves_per_eu(2))) v
   // rows stay inside the borders for every step of the problem.
   LaneLd ca[WCA], cb[WCB], sa[WSA], sb[WSB > 0 ? WSB : 1];
   bool innerA = true, innerB = true;
-  auto make_lane = [&](LaneLd& l, int g, int ngl, int per_kb, int np, int ch, bool is_code, bool is_a,
-                       bool& inner) {
+  // per-row scales: load g fills scale dwords [kb][row], 64 rows at a time
+  auto make_lane_s = [&](LaneLd& l, int g, int ngl, int per_kb, bool is_a, bool& inner) {
     const bool real = g < ngl;
     const int kb = real ? (64 * g) / per_kb : 0;
-    const int t = real ? 64 * g + lane - kb * per_kb : 0;
-    const int row = t / np, piece = np == 2 ? ((t & 1) ^ slot_swz(row)) : 0;
+    const int row = real ? 64 * g + lane - kb * per_kb : 0;
     const PairDelta& d = is_a ? dA : dB;
     const RowInfo r = is_a ? prob.row_a(cx, m0 + row) : prob.row_b(cx, n0 + row);
     const bool ok = r.ok & real;
-    l.off = ok ? (is_code ? r.code + piece * ch + kb * d.code : r.scale + kb * d.scale) : kOOB;
+    l.off = ok ? r.scale + kb * d.scale : kOOB;
     l.p0 = r.p0 + kb * d.g0;
     l.p1 = r.p1 + kb * d.g1;
+    l.kb = 0;
+    const GRange& gr = is_a ? gA : gB;
+    const int L0 = is_a ? la0 : lb0, L1 = is_a ? la1 : lb1;
+    inner = inner & (!ok | ((l.p0 + gr.min0 >= 0) & (l.p0 + gr.max0 < L0) & (l.p1 + gr.min1 >= 0) &
+                            (l.p1 + gr.max1 < L1)));
+  };
+  // row-major codes: load g covers rows g * 64 / SPR .. of the [row][SPR]
+  // stage; lane t writes physical slot u = t % SPR of its row, which holds
+  // logical slot u ^ row_swz(row): K-block L / np, piece L % np
+  auto make_lane_r = [&](LaneLd& l, int g, int ngl, auto SPRc, int np, int ch, bool is_a, bool& inner) {
+    constexpr int SPR = decltype(SPRc)::value;
+    const bool real = g < ngl;
+    const int row = real ? g * (64 / SPR) + lane / SPR : 0;
+    const int L = (lane % SPR) ^ row_swz<SPR>(row);
+    const int kb = L / np, piece = L - kb * np;
+    const PairDelta& d = is_a ? dA : dB;
+    const RowInfo r = is_a ? prob.row_a(cx, m0 + row) : prob.row_b(cx, n0 + row);
+    const bool ok = r.ok & real;
+    l.off = ok ? r.code + piece * ch + kb * d.code : kOOB;
+    l.p0 = r.p0 + kb * d.g0;
+    l.p1 = r.p1 + kb * d.g1;
+    l.kb = kb;
     const GRange& gr = is_a ? gA : gB;
     const int L0 = is_a ? la0 : lb0, L1 = is_a ? la1 : lb1;
     inner = inner & (!ok | ((l.p0 + gr.min0 >= 0) & (l.p0 + gr.max0 < L0) & (l.p1 + gr.min1 >= 0) &
@@ -931,6 +967,7 @@ __global__ __launch_bounds__(256 * NG) __attribute__((amdgpu_waves_per_eu(2))) v
     l.off = ok ? r.code + k * ks + kb * d.code : kOOB;
     l.p0 = r.p0 + kb * d.g0;
     l.p1 = r.p1 + kb * d.g1;
+    l.kb = 0;
     const GRange& gr = is_a ? gA : gB;
     const int L0 = is_a ? la0 : lb0, L1 = is_a ? la1 : lb1;
     inner = inner & (!ok | ((l.p0 + gr.min0 >= 0) & (l.p0 + gr.max0 < L0) & (l.p1 + gr.min1 >= 0) &
@@ -940,13 +977,13 @@ __global__ __launch_bounds__(256 * NG) __attribute__((amdgpu_waves_per_eu(2))) v
   for (int k = 0; k < WCA; k++) {
     if constexpr (TA)
       make_lane_k(ca[k], wave + 4 * k, NCA, std::integral_constant<int, BM>{}, std::true_type{}, innerA, prob);
-    else make_lane(ca[k], wave + 4 * k, NCA, BM * NPKA, NPKA, OA::CH, true, true, innerA);
+    else make_lane_r(ca[k], wave + 4 * k, NCA, std::integral_constant<int, SPRA>{}, NPKA, OA::CH, true, innerA);
   }
 #pragma unroll
   for (int k = 0; k < WCB; k++) {
     if constexpr (TB)
       make_lane_k(cb[k], wave + 4 * k, NCB, std::integral_constant<int, BN>{}, std::false_type{}, innerB, prob);
-    else make_lane(cb[k], wave + 4 * k, NCB, BN * NPKB, NPKB, OB::CH, true, false, innerB);
+    else make_lane_r(cb[k], wave + 4 * k, NCB, std::integral_constant<int, SPRB>{}, NPKB, OB::CH, false, innerB);
   }
   // grouped scales: lane e of wave 0 (A) or wave 1 (B) loads the scale of
   // group e % ngroups of K-block e / ngroups (e < KPS * ngroups <= 64)
@@ -964,6 +1001,7 @@ __global__ __launch_bounds__(256 * NG) __attribute__((amdgpu_waves_per_eu(2))) v
     sa[0].off = ok ? r.scale + kb * d.scale : kOOB;
     sa[0].p0 = r.p0 + kb * d.g0;
     sa[0].p1 = r.p1 + kb * d.g1;
+    sa[0].kb = 0;
     s_kb = kb;
     const GRange& gr = isA ? gA : gB;
     const int L0 = isA ? la0 : lb0, L1 = isA ? la1 : lb1;
@@ -973,9 +1011,9 @@ __global__ __launch_bounds__(256 * NG) __attribute__((amdgpu_waves_per_eu(2))) v
     if (isB) innerB = innerB & inner;
   } else {
 #pragma unroll
-    for (int k = 0; k < WSA; k++) make_lane(sa[k], wave + 4 * k, NSA, BM, 1, 0, false, true, innerA);
+    for (int k = 0; k < WSA; k++) make_lane_s(sa[k], wave + 4 * k, NSA, BM, true, innerA);
 #pragma unroll
-    for (int k = 0; k < WSB; k++) make_lane(sb[k], wave + 4 * k, NSB, BN, 1, 0, false, false, innerB);
+    for (int k = 0; k < WSB; k++) make_lane_s(sb[k], wave + 4 * k, NSB, BN, false, innerB);
   }
   // wave-uniform: no lane of this wave ever needs the border test
   const bool waveA = !P::kGeoA || __builtin_amdgcn_ballot_w64(!innerA) == 0;
@@ -1029,19 +1067,23 @@ __global__ __launch_bounds__(256 * NG) __attribute__((amdgpu_waves_per_eu(2))) v
     const bool inA = waveA || (fl & 8);
     const bool inB = waveB || (fl & 16);
     uint8_t* const stage = ring + st * STAGE;
+    // K-major loads belong to one K-block each (uniform validity); a
+    // row-major load spans the step's K-blocks (validity per lane)
 #pragma unroll
     for (int k = 0; k < WCA; k++) {
       const int g = wave + 4 * k;
-      const int kbi = (g * 64) / (BM * NPKA);
-      dma16(rs[0], g < NCA ? stage + g * 64 * 16 : arena + DUMMY, voff(ca[k], ka, P::kGeoA, inA, la0, la1),
-            soff(ka.code, kbi, live, nv));
+      uint8_t* const dst = g < NCA ? stage + g * 64 * 16 : arena + DUMMY;
+      const int v = voff(ca[k], ka, P::kGeoA, inA, la0, la1);
+      if constexpr (TA) dma16(rs[0], dst, v, soff(ka.code, (g * 64) / (BM * NPKA), live, nv));
+      else dma16(rs[0], dst, ca[k].kb < nv ? v : kOOB, live ? ka.code : kOOB);
     }
 #pragma unroll
     for (int k = 0; k < WCB; k++) {
       const int g = wave + 4 * k;
-      const int kbi = (g * 64) / (BN * NPKB);
-      dma16(rs[2], g < NCB ? stage + OFF_B + g * 64 * 16 : arena + DUMMY, voff(cb[k], kb, P::kGeoB, inB, lb0, lb1),
-            soff(kb.code, kbi, live, nv));
+      uint8_t* const dst = g < NCB ? stage + OFF_B + g * 64 * 16 : arena + DUMMY;
+      const int v = voff(cb[k], kb, P::kGeoB, inB, lb0, lb1);
+      if constexpr (TB) dma16(rs[2], dst, v, soff(kb.code, (g * 64) / (BN * NPKB), live, nv));
+      else dma16(rs[2], dst, cb[k].kb < nv ? v : kOOB, live ? kb.code : kOOB);
     }
     if constexpr (GS) {
       // wave 0: A scales, wave 1: B scales, waves 2-3: zero-reading filler
@@ -1084,7 +1126,9 @@ __global__ __launch_bounds__(256 * NG) __attribute__((amdgpu_waves_per_eu(2))) v
       for (int e = 0; e < 16; e++) acc[i][j][e] = 0.0f;
 
   const int r32 = lane & 31, q = lane >> 5;
-  const int swz = slot_swz(r32);  // tile rows start at multiples of 32
+  // row-major stages: tile rows start at multiples of 32, so row_swz of a
+  // row is that of r32
+  const int hA = row_swz<SPRA>(r32), hB = row_swz<SPRB>(r32);
   // operand images and scales of the step's KPS / 2 pairs of K-blocks; pair
   // p starts 2 K-blocks (KBA / KBB bytes each) into the operand's stage
   constexpr int NP = KPS / 2;
@@ -1095,6 +1139,7 @@ __global__ __launch_bounds__(256 * NG) __attribute__((amdgpu_waves_per_eu(2))) v
     const uint8_t* const stage = ring + st * STAGE;
 #pragma unroll
     for (int p = 0; p < NP; p++) {
+      // K-major stages: pair p starts 2 K-blocks into the operand's stage
       const uint8_t* const sA = stage + p * 2 * KBA;
       const uint8_t* const sB = stage + OFF_B + p * 2 * KBB;
       const int kq = 2 * p + q;  // K-block whose scale this lane supplies
@@ -1102,8 +1147,8 @@ __global__ __launch_bounds__(256 * NG) __attribute__((amdgpu_waves_per_eu(2))) v
       for (int i = 0; i < TM; i++) {
         const int row = (wm * TM + i) * 32 + r32;
         if constexpr (TA) a[p][i] = lds_operand_k<BM, KH, true>(sA, (wm * TM + i) * 32, lane);
-        else if constexpr (KH) a[p][i] = lds_operand_half<BM>(sA, arena + ZERO, row, q);
-        else a[p][i] = lds_operand<FA, BM>(sA, row, swz, q);
+        else if constexpr (KH) a[p][i] = lds_operand_half<SPRA>(stage, arena + ZERO, row, hA, p, q);
+        else a[p][i] = lds_operand<FA, SPRA>(stage, row, hA, p, q);
         xa[p][i] = *reinterpret_cast<const int*>(stage + OFF_SA + (GS ? kq * (BM / gsa) + row / gsa : kq * BM + row) * 4);
       }
 #pragma unroll
@@ -1113,8 +1158,8 @@ __global__ __launch_bounds__(256 * NG) __attribute__((amdgpu_waves_per_eu(2))) v
         // zeroed above, a row-major A reads the zero slot)
         if constexpr (TB && FB >= 2) b[p][j] = lds_operand_k_sub<FB, BN>(sB, (wn * TN + j) * 32, lane);
         else if constexpr (TB) b[p][j] = lds_operand_k<BN, KH, false>(sB, (wn * TN + j) * 32, lane);
-        else if constexpr (KH) b[p][j] = lds_operand_half<BN>(sB, arena + ZERO, row, q);
-        else b[p][j] = lds_operand<FB, BN>(sB, row, swz, q);
+        else if constexpr (KH) b[p][j] = lds_operand_half<SPRB>(stage + OFF_B, arena + ZERO, row, hB, p, q);
+        else b[p][j] = lds_operand<FB, SPRB>(stage + OFF_B, row, hB, p, q);
         xb[p][j] = *reinterpret_cast<const int*>(stage + OFF_SB + (GS ? kq * (BN / gsb) + row / gsb : kq * BN + row) * 4);
       }
     }
