@@ -51,7 +51,9 @@ struct KInfo { int code, scale, g0, g1; };
 struct PairDelta { int code, scale, g0, g1; };
 struct GRange { int min0, max0, min1, max1; };
 // Reciprocals of the grid's x extent and x*y extent (workgroup re-ordering).
-struct GridDivs { FastDiv nx, nxy; };
+// The logical tile grid (tx x ty x tz tiles) and, for a persistent launch,
+// the workgroups per XCD (gx; 0: one workgroup per tile).
+struct GridDivs { FastDiv nx, nxy; int tx, ty, tz, gx; };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, long long bytes) {
   const int n = bytes < (long long)kOOB ? (int)bytes : kOOB;
@@ -185,7 +187,12 @@ struct DgradProb {
     c.nkw = c.kw0 < KW ? (KW - c.kw0 + sw - 1) / sw : 0;
     c.M = c.Hc * c.Wc * N;
     c.hoff = (c.ph_c + ph - c.kh0) / sh; c.woff = (c.pw_c + pw - c.kw0) / sw;
-    c.dwc = dWc[c.pw_c]; c.dnkw = dNkw[c.pw_c];
+    // (selected, not indexed: an indexed kernel-argument array inside the
+    // persistent tile loop became a private-memory copy)
+    c.dwc = dWc[0]; c.dnkw = dNkw[0];
+#pragma unroll
+    for (int k = 1; k < 8; k++)
+      if (c.pw_c == k) { c.dwc = dWc[k]; c.dnkw = dNkw[k]; }
     return c;
   }
   __device__ int rows_a(const Ctx& c) const { return c.M; }
@@ -817,8 +824,26 @@ __device__ __forceinline__ void mx_store_strip(const P& p, const typename P::Ctx
   }
 }
 
+// The backward-data tile with a 2-deep ring (a tile of few K-steps) runs
+// persistent workgroups: as many as fit on the chip, each looping over
+// tiles. Launched one per tile, its short-lived workgroups left the chip
+// at 1.7 of the 3 workgroups per compute unit that fit (SQ_WAVE_CYCLES over
+// the kernel's duration on the stride-2 layer, N 32, 128 -> 256 channels,
+// 160 x 160).
+template <class P, int NS>
+constexpr bool gemm_persistent() {
+  return std::is_base_of<DgradProb, P>::value && NS == 2;
+}
+// Waves per SIMD the register budget must allow: three for the persistent
+// tile (its occupancy is fixed at launch), else two.
+template <class P, int NS>
+constexpr int gemm_waves_per_eu() {
+  return gemm_persistent<P, NS>() ? 3 : 2;
+}
+
 template <int FA, int FB, class P, int WM, int WN, int TM, int TN, int NS, bool GS, bool KH, int KPS, int NG>
-__global__ __launch_bounds__(256 * NG) __attribute__((amdgpu_waves_per_eu(2))) void mx_gemm_kernel(P prob) {
+__global__ __launch_bounds__(256 * NG) __attribute__((amdgpu_waves_per_eu(gemm_waves_per_eu<P, NS>())))
+void mx_gemm_kernel(P prob) {
   static_assert(!KH || (FA <= 1 && FB <= 1), "half K-blocks only for 8-bit codes");
   // K-major operands (8-bit codes; 6/4-bit B codes without half K-blocks):
   // the staging order of the contraction's natural layout, read back with
@@ -858,43 +883,63 @@ __global__ __launch_bounds__(256 * NG) __attribute__((amdgpu_waves_per_eu(2))) v
   constexpr int ARENA = (ZERO + 16) > EPI ? (ZERO + 16) : EPI;
   __shared__ __attribute__((aligned(16))) uint8_t arena[ARENA];
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int grp = __builtin_amdgcn_readfirstlane(tid >> 8);          // wave group
-  const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);   // wave within the group
-  const int wm = wave % WM, wn = wave / WM;
-  uint8_t* const ring = arena + grp * NS * STAGE;  // this group's stages
   // XCD-aware tile order: the hardware hands consecutive workgroups to the 8
   // XCDs in turn, each with its own L2. Remap so that every XCD works on a
   // contiguous range of tiles (column tiles fastest, then row tiles):
   // neighbouring row tiles share the weight tile and the rows of the
   // implicit im2col, and now share an L2.
+  // Persistent launch (prob.grid.gx > 0 workgroups per XCD, as many as fit
+  // on the chip at once): workgroup j of an XCD takes, at its k-th pass,
+  // local tile k*gx + (j + k) % gx, so a pass of the XCD's workgroups covers
+  // gx consecutive tiles (the same L2 locality as one tile per workgroup)
+  // and, with gx a multiple of the class count, each workgroup cycles
+  // through the backward-data parity classes (whose K lengths differ).
+  // (only the backward-data tile with a 2-deep ring is built with the loop;
+  // every other kernel takes one tile and compiles as straight-line code)
+  constexpr bool PERSIST = gemm_persistent<P, NS>();
+  const int tnx = prob.grid.tx, tny = prob.grid.ty, tnz = prob.grid.tz, gx = PERSIST ? prob.grid.gx : 0;
+  const int nb = tnx * tny * tnz;
+  const int hw = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  const int xcd = hw % 8, jx = hw / 8, q8 = nb / 8, r8 = nb % 8;
+  const int n_x = xcd < r8 ? q8 + 1 : q8;  // tiles of this XCD
+  const int lo_x = xcd < r8 ? xcd * (q8 + 1) : r8 * (q8 + 1) + (xcd - r8) * q8;
+  for (int pass = 0; gx > 0 ? pass * gx < n_x : pass == 0; pass++) {
+  const int u = gx > 0 ? pass * gx + (jx + pass) % gx : jx;
+  if (u >= n_x) continue;  // (uniform)
+  // the previous tile's epilogue may still read LDS that this tile's first
+  // loads write
+  if (pass > 0) stage_barrier();
+  // The thread index passes through an empty asm each pass, so nothing
+  // computed from it is hoisted out of the tile loop (values kept live
+  // across the whole loop would exceed the register budget).
+  int tid = threadIdx.x;
+  if constexpr (PERSIST) asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
+  const int grp = __builtin_amdgcn_readfirstlane(tid >> 8);          // wave group
+  const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);   // wave within the group
+  const int wm = wave % WM, wn = wave / WM;
+  uint8_t* const ring = arena + grp * NS * STAGE;  // this group's stages
   int bx, by, z;
   {
-    const int nx = gridDim.x, ny = gridDim.y;
-    const int nb = nx * ny * gridDim.z;
-    const int lin = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
-    const int xcd = lin % 8, idx = lin / 8, q8 = nb / 8, r8 = nb % 8;
-    const int logical = xcd < r8 ? xcd * (q8 + 1) + idx : r8 * (q8 + 1) + (xcd - r8) * q8 + idx;
+    const int logical = lo_x + u;
     int rem;
     if constexpr (std::is_base_of<DgradProb, P>::value) {
       // backward-data: the stride-parity classes of one tile position run
       // side by side (they read the same dY rows through different taps)
-      const int nz = gridDim.z;
-      rem = logical / nz;
-      z = logical - rem * nz;
+      rem = logical / tnz;
+      z = logical - rem * tnz;
     } else {
       z = (int)fdiv((unsigned)logical, prob.grid.nxy);
-      rem = logical - z * nx * ny;
+      rem = logical - z * tnx * tny;
     }
     // column tiles fastest: the column tiles of one row tile read the same
     // A rows, now from the same XCD's L2
-    bx = rem / ny;
-    by = rem - bx * ny;
+    bx = rem / tny;
+    by = rem - bx * tny;
   }
   const typename P::Ctx cx = prob.ctx(z);
   const int m0 = bx * BM, n0 = by * BN;
-  if (m0 >= prob.rows_a(cx)) return;  // whole tile beyond this class's rows (uniform)
+  if (m0 >= prob.rows_a(cx)) continue;  // whole tile beyond this class's rows (uniform)
   __amdgpu_buffer_rsrc_t rs[4];
   rsrcs(prob, rs);
   const PairDelta dA = prob.pd_a(), dB = prob.pd_b();
@@ -1253,7 +1298,7 @@ __global__ __launch_bounds__(256 * NG) __attribute__((amdgpu_waves_per_eu(2))) v
     // the strips below reuse the exchange area: every group-0 wave must have
     // read its part first (all waves of both groups take this barrier)
     stage_barrier();
-    if (grp == 1) return;
+    if (grp == 1) continue;
   }
 
   // Epilogue through LDS (the stages are free now). For each 32-row strip i
@@ -1270,6 +1315,27 @@ __global__ __launch_bounds__(256 * NG) __attribute__((amdgpu_waves_per_eu(2))) v
   typedef float v4f __attribute__((ext_vector_type(4)));
 #pragma unroll
   for (int i = 0; i < TM; i++) {
+    if constexpr (!MxOut<P>::value && PERSIST) {
+      // (persistent backward-data) A strip whose 32 rows all lie at a fixed stride from its first row
+      // and whose columns are all in range goes out straight from the
+      // accumulators: for each accumulator register, lanes 0-31 and 32-63
+      // each write one whole 128-byte row segment (no LDS round trip, which
+      // would compete with the K loops of the other workgroups on the CU).
+      const int ms = m0 + (wm * TM + i) * 32;
+      float* const sb = prob.out_row(cx, z, ms);
+      const bool direct = sb != nullptr && c_wave + EW <= ncols && ms + 32 <= prob.rows_a(cx) &&
+                          prob.row_run(cx, ms) >= 32;
+      if (direct) {
+        float* const col = sb + c_wave + r32;
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+#pragma unroll
+          for (int e = 0; e < 16; e++)
+            __builtin_nontemporal_store(acc[i][j][e],
+                                        col + (long long)(8 * (e >> 2) + 4 * q + (e & 3)) * ncols + j * 32);
+        continue;
+      }
+    }
 #pragma unroll
     for (int j = 0; j < TN; j++)
 #pragma unroll
@@ -1317,6 +1383,31 @@ __global__ __launch_bounds__(256 * NG) __attribute__((amdgpu_waves_per_eu(2))) v
     }
     __builtin_amdgcn_wave_barrier();
   }
+  }  // tiles of a persistent workgroup
+}
+
+// Workgroups of a kernel that fit on one compute unit at once (0 if the
+// runtime cannot say; the query's error is cleared).
+inline int kernel_occupancy(const void* kern, int threads) {
+  int occ = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, threads, 0) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  return occ;
+}
+// Workgroups of a persistent launch: all that fit on the current device at
+// once, a multiple of 8 * nz (eight XCDs, each pass of an XCD's workgroups
+// spanning whole groups of nz parity classes); 0: launch one per tile.
+inline int persistent_groups(int occ, int nz) {
+  int dev = 0, cus = 0;
+  if (occ <= 0 || hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  const int unit = 8 * (nz > 0 ? nz : 1);
+  return occ * cus / unit * unit;
 }
 
 template <class P, int WM, int WN, int TM, int TN, int NS, bool GS, bool KH>
@@ -1325,11 +1416,23 @@ hipError_t launch_gemm(int fa, int fb, const P& prob, dim3 grid, hipStream_t st)
   // and two wave groups per workgroup
   constexpr int KPS = (P::kQuad && KH) ? 4 : 2;
   constexpr int NG = (P::kQuad && KH) ? 2 : 1;
+  // persistent workgroups (see gemm_persistent)
+  constexpr bool PERSIST = gemm_persistent<P, NS>();
 #define MQ_CASE(A, B)                                                                                   \
   if (fa == A && fb == B) {                                                                             \
-    hipLaunchKernelGGL((mx_gemm_kernel<A, B, P, WM, WN, TM, TN, NS, GS, KH, KPS, NG>), grid, dim3(256 * NG), 0, \
-                       st, prob);                                                                       \
-    return launch_check();                                                                           \
+    const auto kern = mx_gemm_kernel<A, B, P, WM, WN, TM, TN, NS, GS, KH, KPS, NG>;                     \
+    P pr = prob;                                                                                        \
+    dim3 g = grid;                                                                                      \
+    if (PERSIST) {                                                                                      \
+      static const int occ = kernel_occupancy(reinterpret_cast<const void*>(kern), 256 * NG);          \
+      const int G = persistent_groups(occ, (int)grid.z);                                                \
+      if (G > 0 && (long long)grid.x * grid.y * grid.z > G) {                                           \
+        pr.grid.gx = G / 8;                                                                             \
+        g = dim3(G);                                                                                    \
+      }                                                                                                 \
+    }                                                                                                   \
+    hipLaunchKernelGGL(kern, g, dim3(256 * NG), 0, st, pr);                                             \
+    return launch_check();                                                                              \
   }
   if constexpr (SubB<P>::value) {  // 8-bit A, 6/4-bit B, full K-blocks only
     if constexpr (!KH) { MQ_CASE(0, 2) MQ_CASE(0, 3) MQ_CASE(0, 4) MQ_CASE(1, 2) MQ_CASE(1, 3) MQ_CASE(1, 4) }
@@ -1452,6 +1555,10 @@ hipError_t launch_tiled(int fa, int fb, const P& prob_in, int M, int Ncols, int 
   P prob = prob_in;
   prob.grid.nx = make_fastdiv(grid.x);
   prob.grid.nxy = make_fastdiv(grid.x * grid.y);
+  prob.grid.tx = (int)grid.x;
+  prob.grid.ty = (int)grid.y;
+  prob.grid.tz = (int)grid.z;
+  prob.grid.gx = 0;
   if constexpr (P::kCanGroup) {
     // one 64-lane load holds both K-blocks' group scales of a 256-row tile
     // when groups have at least 8 rows
