@@ -11,6 +11,9 @@ Modes:
   summarize-call
              read the counter CSVs of a call run and write the HBM bytes of
              one call of that entry point (profiles/traffic_<workload>_<call>.json)
+  kernels    read the kernel statistics of a rocprofv3 --kernel-trace --stats
+             run of bench.py and its JSON line, and write both side by side
+             (profiles/kernels_<workload>.txt)
   mfma       read the counter CSV of a step run with the matrix-core counters
              and write, per GEMM kernel, the fraction of SIMD cycles the MFMA
              unit was busy and the matrix operations it executed
@@ -330,6 +333,59 @@ def summarize_mfma(d: str, stem: str, workload: str, out_dir: str, command: str)
     return text
 
 
+def summarize_kernels(d: str, stem: str, bench_log: str, workload: str, title: str, out_dir: str,
+                      command: str) -> str:
+    """Kernel statistics of a rocprofv3 --kernel-trace --stats run of bench.py
+    (D/<stem>_kernel_stats.csv) next to bench.py's own per-call times of the
+    same run (the JSON line of its log): profiles/kernels_<workload>.txt."""
+    from microscaling_quantized_convolution_mxq_amd.workloads import WORKLOADS
+    paths = glob.glob(os.path.join(d, "**", f"{stem}_kernel_stats.csv"), recursive=True)
+    if not paths:
+        raise FileNotFoundError(f"no {stem}_kernel_stats.csv under {d}")
+    rows = list(csv.DictReader(open(paths[0])))
+
+    def col(r, *keys):
+        for k in r:
+            if any(k.lower() == key.lower() for key in keys):
+                return r[k]
+        raise KeyError(keys)
+    def short(name):  # without the return type and the parameter list
+        name = name[5:] if name.startswith("void ") else name
+        depth = 0
+        for i, ch in enumerate(name):
+            depth += ch == "<"
+            depth -= ch == ">"
+            if ch == "(" and depth == 0:
+                return name[:i]
+        return name
+    stats = []
+    for r in rows:
+        stats.append((short(col(r, "Name", "KernelName", "Kernel_Name")), int(float(col(r, "Calls"))),
+                      float(col(r, "AverageNs")) / 1e3, float(col(r, "MinNs")) / 1e3,
+                      float(col(r, "MaxNs")) / 1e3, float(col(r, "Percentage"))))
+    stats.sort(key=lambda t: -t[5])
+    line = [x for x in open(bench_log) if x.startswith("{")][-1]
+    b = json.loads(line)
+    full = WORKLOADS[workload].name
+    out = [title, "", "Command (run from the repository root on one MI355X):", f"  {command}",
+           f"Library source hash: {_source_sha()}", "",
+           "rocprofv3 kernel statistics (durations in microseconds; per launch):", "",
+           f"{'kernel':88s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'share':>7s}"]
+    for name, calls, avg, mn, mx, pct in stats:
+        out.append(f"{name[:88]:88s} {calls:6d} {avg:9.2f} {mn:9.2f} {mx:9.2f} {pct:6.2f}%")
+    out += ["", "bench.py per-call times of the same run (HIP events over graphs of calls, microseconds):"]
+    for k, v in b["kernels"].items():
+        out.append(f"  {k:24s} {v['ms'] * 1000:9.2f}   launches: {'; '.join(v['launches'])}")
+    out += ["", f"Dominant entry point: {b['roofline']['kernel']}; roofline object of the same run: "
+            f"{json.dumps(b['roofline'])}",
+            f"Step: {b['value']:.3f} TFLOP/s, {b['ms_per_step']:.5f} ms per step (traced run)."]
+    text = "\n".join(out) + "\n"
+    os.makedirs(out_dir, exist_ok=True)
+    with open(os.path.join(out_dir, f"kernels_{full}.txt"), "w") as f:
+        f.write(text)
+    return text
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="mode", required=True)
@@ -352,6 +408,14 @@ def main(argv=None):
     f.add_argument("--workload", default="c2")
     f.add_argument("--out", default=os.path.join(ROOT, "profiles"))
     f.add_argument("--command", default="")
+    k = sub.add_parser("kernels")
+    k.add_argument("--dir", required=True)
+    k.add_argument("--stem", default="kt")
+    k.add_argument("--bench-log", required=True)
+    k.add_argument("--workload", default="c5")
+    k.add_argument("--title", default="")
+    k.add_argument("--out", default=os.path.join(ROOT, "profiles"))
+    k.add_argument("--command", default="")
     c = sub.add_parser("summarize")
     c.add_argument("--dir", required=True)
     c.add_argument("--workload", default="c2")
@@ -365,6 +429,8 @@ def main(argv=None):
         run_copy()
     elif args.mode == "mfma":
         summarize_mfma(args.dir, args.stem, args.workload, args.out, args.command)
+    elif args.mode == "kernels":
+        summarize_kernels(args.dir, args.stem, args.bench_log, args.workload, args.title, args.out, args.command)
     elif args.mode == "summarize-call":
         summarize_call(args.dir, args.workload, args.call, args.out, args.command)
     else:
