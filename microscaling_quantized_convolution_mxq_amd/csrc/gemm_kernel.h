@@ -1410,12 +1410,22 @@ inline int persistent_groups(int occ, int nz) {
   return occ * cus / unit * unit;
 }
 
+// The backward-weight tile that runs two wave groups per workgroup with full
+// K-blocks (tile 2, 256 x 128).
+template <int WM, int WN, int TM, int TN>
+constexpr bool wgrad_two_groups() {
+  return WM == 2 && WN == 2 && TM == 4 && TN == 2;
+}
+
 template <class P, int WM, int WN, int TM, int TN, int NS, bool GS, bool KH>
 hipError_t launch_gemm(int fa, int fb, const P& prob, dim3 grid, hipStream_t st) {
   // the backward-weight problem with half K-blocks: four K-blocks per step
   // and two wave groups per workgroup
   constexpr int KPS = (P::kQuad && KH) ? 4 : 2;
-  constexpr int NG = (P::kQuad && KH) ? 2 : 1;
+  // and the 256 x 128 backward-weight tile too: two groups of four waves
+  // split each slice's K range (one workgroup of eight waves per CU instead
+  // of two of four), so half as many slices write fp32 partial sums
+  constexpr int NG = (P::kQuad && (KH || wgrad_two_groups<WM, WN, TM, TN>())) ? 2 : 1;
   // persistent workgroups (see gemm_persistent)
   constexpr bool PERSIST = gemm_persistent<P, NS>();
 #define MQ_CASE(A, B)                                                                                   \

@@ -135,6 +135,13 @@ static WgradPlan wgrad_plan(const Conv& cv, int fdy, int fx) {
   w.kps = half_k_blocks(ga, gb, khalf, fdy, fx) ? 4 : 2;
   const int S0 = wgrad_splits(cv, fdy, fx);
   w.S = w.kps == 4 ? ceil_div(S0, 2) : S0;
+  // the 256 x 128 tile runs two wave groups per workgroup as well (one
+  // workgroup of eight waves per CU where two of four ran): half as many
+  // slices, when the launch still takes that tile for them
+  if (w.kps == 2 && cv.cin % 32 == 0 && w.S > 1) {
+    const int S2 = ceil_div(w.S, 2);
+    if (choose_tile(cv.cout, (long long)cv.kh * cv.kw * cv.cin, S2).id == 2) w.S = S2;
+  }
   const long long npix_o = (long long)cv.ho() * cv.wo();
   const bool in_place = w.natural || w.natural_sub;
   w.dyt_b = (!in_place && !w.mixed) ? align256(transposed_bytes(fdy, npix_o, cv.n, 1, cv.cout)) : 0;
