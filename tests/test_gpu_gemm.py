@@ -61,6 +61,24 @@ def test_gemm_natural_layout_shapes(label, shape, fmts):
     _compare_full(shape, x, w, dy, *fmts, 32, ("fwd", "dgrad", "wgrad"), "natural " + label)
 
 
+# The backward-data tile of few K-steps runs persistent workgroups (as many
+# as fit on the chip, each looping over tiles) once a problem has more tiles
+# than that: odd H and W give parity classes of different row counts, so
+# some tiles of the smaller classes lie past their rows; N = 32 stores
+# strips straight from the accumulators, N = 16 goes through the LDS strips
+# between passes.
+PERSISTENT = [
+    ("n32_61x61_s2", ConvShape(32, 128, 61, 61, 64, 3, 3, 2, 1)),
+    ("n16_81x81_s2", ConvShape(16, 128, 81, 81, 64, 3, 3, 2, 1)),
+]
+
+
+@pytest.mark.parametrize("label,shape", PERSISTENT, ids=[c[0] for c in PERSISTENT])
+def test_backward_data_persistent_passes(label, shape):
+    x, w, dy = _inputs(shape, 23)
+    _compare_full(shape, x, w, dy, 0, 0, 1, 32, ("dgrad",), "persistent " + label)
+
+
 @pytest.mark.parametrize("fx", range(5))
 @pytest.mark.parametrize("fw", range(5))
 def test_gemm_format_matrix(fx, fw):
