@@ -824,26 +824,22 @@ __device__ __forceinline__ void mx_store_strip(const P& p, const typename P::Ctx
   }
 }
 
-// The backward-data tile with a 2-deep ring (a tile of few K-steps) runs
+// The backward-data GEMM with fp32 output on its 256 x 128 tile runs
 // persistent workgroups: as many as fit on the chip, each looping over
-// tiles. Launched one per tile, its short-lived workgroups left the chip
-// at 1.7 of the 3 workgroups per compute unit that fit (SQ_WAVE_CYCLES over
-// the kernel's duration on the stride-2 layer, N 32, 128 -> 256 channels,
-// 160 x 160).
-template <class P, int NS>
+// tiles. Launched one per tile, the short-lived workgroups of the
+// backward-data left the chip at 1.7 of the 3 workgroups per compute unit
+// that fit its 128 x 128 tile (SQ_WAVE_CYCLES over the kernel's duration on
+// the stride-2 layer, N 32, 128 -> 256 channels, 160 x 160); persistent, the
+// 256 x 128 tile (two per CU, a quarter fewer operand bytes per FLOP through
+// LDS) is the faster of the two.
+template <class P, int WM, int WN, int TM, int TN, int NS>
 constexpr bool gemm_persistent() {
-  return std::is_base_of<DgradProb, P>::value && NS == 2;
-}
-// Waves per SIMD the register budget must allow: three for the persistent
-// tile (its occupancy is fixed at launch), else two.
-template <class P, int NS>
-constexpr int gemm_waves_per_eu() {
-  return gemm_persistent<P, NS>() ? 3 : 2;
+  return std::is_base_of<DgradProb, P>::value && !MxOut<P>::value && WM == 2 && WN == 2 && TM == 4 && TN == 2 &&
+         NS == 3;
 }
 
 template <int FA, int FB, class P, int WM, int WN, int TM, int TN, int NS, bool GS, bool KH, int KPS, int NG>
-__global__ __launch_bounds__(256 * NG) __attribute__((amdgpu_waves_per_eu(gemm_waves_per_eu<P, NS>())))
-void mx_gemm_kernel(P prob) {
+__global__ __launch_bounds__(256 * NG) __attribute__((amdgpu_waves_per_eu(2))) void mx_gemm_kernel(P prob) {
   static_assert(!KH || (FA <= 1 && FB <= 1), "half K-blocks only for 8-bit codes");
   // K-major operands (8-bit codes; 6/4-bit B codes without half K-blocks):
   // the staging order of the contraction's natural layout, read back with
@@ -894,9 +890,9 @@ void mx_gemm_kernel(P prob) {
   // gx consecutive tiles (the same L2 locality as one tile per workgroup)
   // and, with gx a multiple of the class count, each workgroup cycles
   // through the backward-data parity classes (whose K lengths differ).
-  // (only the backward-data tile with a 2-deep ring is built with the loop;
-  // every other kernel takes one tile and compiles as straight-line code)
-  constexpr bool PERSIST = gemm_persistent<P, NS>();
+  // (only the persistent backward-data tile is built with the loop; every
+  // other kernel takes one tile and compiles as straight-line code)
+  constexpr bool PERSIST = gemm_persistent<P, WM, WN, TM, TN, NS>();
   const int tnx = prob.grid.tx, tny = prob.grid.ty, tnz = prob.grid.tz, gx = PERSIST ? prob.grid.gx : 0;
   const int nb = tnx * tny * tnz;
   const int hw = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
@@ -1427,7 +1423,7 @@ hipError_t launch_gemm(int fa, int fb, const P& prob, dim3 grid, hipStream_t st)
   // of two of four), so half as many slices write fp32 partial sums
   constexpr int NG = (P::kQuad && (KH || wgrad_two_groups<WM, WN, TM, TN>())) ? 2 : 1;
   // persistent workgroups (see gemm_persistent)
-  constexpr bool PERSIST = gemm_persistent<P, NS>();
+  constexpr bool PERSIST = gemm_persistent<P, WM, WN, TM, TN, NS>();
 #define MQ_CASE(A, B)                                                                                   \
   if (fa == A && fb == B) {                                                                             \
     const auto kern = mx_gemm_kernel<A, B, P, WM, WN, TM, TN, NS, GS, KH, KPS, NG>;                     \
@@ -1478,7 +1474,8 @@ hipError_t launch_gemm(int fa, int fb, const P& prob, dim3 grid, hipStream_t st)
 //   5: 128 x 128 with a 2-stage ring: a tile of few K-steps spends most of its
 //      life outside the K-loop (set-up, first loads, epilogue), so smaller
 //      workgroups that fit more per CU overlap those phases better (measured
-//      on the stride-2 backward-data of 9 K-steps per tile on average)
+//      on the stride-2 backward-data with the MX epilogue, 9 K-steps per tile
+//      on average; the fp32 backward-data runs persistent 256 x 128 tiles)
 struct TileChoice { int id, bm, bn; };
 inline TileChoice tile_shape(int id) {
   switch (id) {
@@ -1550,11 +1547,11 @@ hipError_t launch_tiled(int fa, int fb, const P& prob_in, int M, int Ncols, int 
   if constexpr (P::kCanGroup) grouped = prob_in.ga >= 8 && prob_in.gb >= 8;
   if (!grouped && t.id == 2) t = tile_shape(1);
   if constexpr (std::is_base_of<DgradProb, P>::value) {
-    if (t.id == 2 && ksteps <= 12) t = tile_shape(5);
     // the backward-data problem with the MX epilogue needs more registers
     // than the 256 x 128 tile leaves at two waves per SIMD (it would spill
-    // to scratch memory): 128 x 128 instead
-    if (MxOut<P>::value && t.id == 2) t = tile_shape(1);
+    // to scratch memory): 128 x 128 instead, with a 2-deep ring for tiles
+    // of few K-steps
+    if (MxOut<P>::value && t.id == 2) t = tile_shape(ksteps <= 12 ? 5 : 1);
   }
   // four K-blocks per step double the operand registers: the 256 x 128 tile
   // would then exceed the budget of two waves per SIMD

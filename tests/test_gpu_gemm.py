@@ -61,15 +61,15 @@ def test_gemm_natural_layout_shapes(label, shape, fmts):
     _compare_full(shape, x, w, dy, *fmts, 32, ("fwd", "dgrad", "wgrad"), "natural " + label)
 
 
-# The backward-data tile of few K-steps runs persistent workgroups (as many
-# as fit on the chip, each looping over tiles) once a problem has more tiles
-# than that: odd H and W give parity classes of different row counts, so
-# some tiles of the smaller classes lie past their rows; N = 32 stores
-# strips straight from the accumulators, N = 16 goes through the LDS strips
-# between passes.
+# The backward-data GEMM on its 256 x 128 tile runs persistent workgroups
+# (as many as fit on the chip, each looping over tiles) once a problem has
+# more tiles than that (512 on MI355X): odd H and W give parity classes of
+# different row counts, so some tiles of the smaller classes lie past their
+# rows; N = 32 stores strips straight from the accumulators, N = 16 goes
+# through the LDS strips between passes.
 PERSISTENT = [
-    ("n32_61x61_s2", ConvShape(32, 128, 61, 61, 64, 3, 3, 2, 1)),
-    ("n16_81x81_s2", ConvShape(16, 128, 81, 81, 64, 3, 3, 2, 1)),
+    ("n32_71x71_s2", ConvShape(32, 128, 71, 71, 64, 3, 3, 2, 1)),
+    ("n16_95x95_s2", ConvShape(16, 128, 95, 95, 64, 3, 3, 2, 1)),
 ]
 
 
